@@ -1,0 +1,43 @@
+"""CPU oracle for paged, prefix-sharing KV attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import or run anything here.  The
+product path (the C ABI library and its Python binding) never does, and this
+package imports nothing from the product.  It shares no code with the HIP
+path; the only common input is the seeded generator package ``synth``.
+
+Contents:
+
+* :mod:`oracle.pool` -- a plain Python model of the refcounted block pool:
+  free list, per-sequence block tables, fork, append with copy-on-write,
+  free.  It also keeps its own copy of every block's K/V bits.
+* :mod:`oracle.attention` -- textbook softmax attention in float64 over each
+  sequence's keys, gathered token by token through its block table; decode
+  (one query per sequence) and draft-tree verify (context plus tree
+  ancestors and the node itself).
+* :mod:`oracle.run` -- runs a ``synth`` op program through the two.
+
+Every function here is pinned by the ``-m "not gpu"`` tests against facts the
+pages or plain mathematics fix (hand-derived pool trace, closed forms,
+invariants, a library attention routine, numbers the pages print); none is
+"parity unpinned".
+"""
+
+from .pool import PoolModel, PoolError, OOMError, SeqError, ArgError, EmptyError
+from .attention import bf16_bits_to_f64, attend, decode, tree_verify, tree_key_positions
+from .run import run_program
+
+__all__ = [
+    "PoolModel",
+    "PoolError",
+    "OOMError",
+    "SeqError",
+    "ArgError",
+    "EmptyError",
+    "bf16_bits_to_f64",
+    "attend",
+    "decode",
+    "tree_verify",
+    "tree_key_positions",
+    "run_program",
+]
