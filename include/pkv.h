@@ -1,0 +1,207 @@
+/*
+ * pkv.h -- C ABI of a paged, prefix-sharing KV attention library for
+ * MI355X (gfx950).
+ *
+ * The problem, as the pages state it:
+ *   - K/V activations live in fixed-size token blocks taken from one shared
+ *     pool; each sequence holds an ordered list of block ids instead of a
+ *     contiguous array, and a sequence that shares a prefix acquires the
+ *     existing blocks (refcount + 1) instead of allocating and recomputing
+ *     them ("Introducing RadixAttention into Trellis", section "RadixAttention
+ *     in Trellis").
+ *   - A fork copies block-table pointers, not K/V data, so it costs O(1) in
+ *     the context length; blocks are shared copy-on-write (Dendrite page,
+ *     section details and glossary entry "Copy-on-Write").
+ *   - Decode is bound by memory bandwidth and PagedAttention splits the cache
+ *     into fixed-size blocks like virtual-memory pages (SGLang RadixAttention
+ *     page, section on the KV-cache lifecycle; Dendrite glossary).
+ *   - Speculative decoding checks a draft tree's tokens in one target pass
+ *     (CAST page, technical summary, "Problem").
+ *
+ * Conventions for every call:
+ *   - Status codes, never exceptions or aborts.  On any error the host state
+ *     (tables, refcounts, free list, sequence ids) is exactly as before the
+ *     call and no device work has been enqueued.  pkv_last_error() gives a
+ *     message for the calling thread's last failure.
+ *   - Ownership: every device pointer (the two K/V pools, new K/V, Q, out,
+ *     lse) is owned by the caller and must stay valid until the work enqueued
+ *     on the stream has finished.  The pool handle owns its host metadata and
+ *     the device scratch it allocates itself (plans and partial softmax
+ *     states); kv_pool_destroy releases both after synchronising the device.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Device work of one pool must be issued on a single stream, or
+ *     the caller must order the streams: calls reuse the pool's scratch.
+ *   - Threading: a pool is not thread-safe.
+ *   - Sequence ids are int64, handed out in increasing order and never reused.
+ *
+ * Device layout of the pool (caller-allocated, bf16, each of K and V):
+ *     [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
+ * so one (block, kv head) tile of one layer is contiguous.  Physical slot s
+ * of a sequence's token t is (table[t / block_size], t % block_size).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pkv_pool pkv_pool;
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_ARG = -1,         /* bad argument, pointer or shape */
+  PKV_ERR_OOM = -2,         /* the free list cannot supply the blocks a call needs */
+  PKV_ERR_SEQ = -3,         /* unknown or freed sequence id */
+  PKV_ERR_HIP = -4,         /* a HIP runtime call failed (message says which) */
+  PKV_ERR_EMPTY = -5,       /* attention over a sequence with no tokens */
+  PKV_ERR_UNSUPPORTED = -6  /* a shape the kernels do not handle */
+} pkv_status;
+
+typedef struct pkv_desc {
+  int32_t num_blocks;    /* physical blocks in the pool, >= 1 */
+  int32_t block_size;    /* tokens per block: a power of two, 1..128 */
+  int32_t num_layers;    /* layers sharing one block table per sequence, >= 1 */
+  int32_t num_q_heads;   /* query heads, a multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* key/value heads; q head h reads kv head h / (Hq / Hkv) */
+  int32_t head_dim;      /* 64 or 128 for device pools; any >= 1 for host-only pools */
+} pkv_desc;
+
+/* Bytes of ONE of the two device pool arrays (K or V) for `desc`. 0 if invalid. */
+size_t kv_pool_bytes(const pkv_desc* desc);
+
+/*
+ * Create a pool over caller-owned device arrays k_pool / v_pool (bf16, layout
+ * above, each kv_pool_bytes(desc) bytes, on the device current at this call).
+ * Passing NULL for both makes a host-only pool: the same allocator and block
+ * tables with no device storage, for planning and tests (kv_append then takes
+ * NULL K/V and attention calls return PKV_ERR_ARG).
+ * free_order: NULL for the initial free list 0..num_blocks-1, else a host
+ * array holding a permutation of 0..num_blocks-1 (head first).
+ * Blocks are taken from the head of the free list; a block whose refcount
+ * drops to zero is appended at the tail (SGLang RadixAttention page,
+ * source-level sketch: free page pool, extend on reclaim).
+ */
+pkv_status kv_pool_create(const pkv_desc* desc, void* k_pool, void* v_pool,
+                          const int32_t* free_order, pkv_pool** out);
+
+/* Synchronise the pool's device, then free its scratch and metadata. NULL is a no-op. */
+void kv_pool_destroy(pkv_pool* pool);
+
+/* New empty sequence (no blocks, length 0).  Host only. (Dendrite page,
+ * first code listing: allocate_sequence.) */
+pkv_status seq_allocate(pkv_pool* pool, int64_t* out_seq);
+
+/*
+ * Fork: the child gets a copy of the parent's block table and length and
+ * every block's refcount goes up by one.  No K/V data moves and no device
+ * work is enqueued (Dendrite page, section details and first code listing:
+ * fork_sequence).  Cost is linear in the table length only.
+ */
+pkv_status seq_fork(pkv_pool* pool, int64_t parent, int64_t* out_child);
+
+/* Drop a sequence: refcount - 1 for each block in table order; blocks that
+ * reach zero go to the tail of the free list.  Host only. */
+pkv_status seq_free(pkv_pool* pool, int64_t seq);
+
+/*
+ * Append n_tok new tokens to each of the n_seqs (distinct) sequences.
+ * k_new / v_new: device bf16 [num_layers][n_seqs][n_tok][num_kv_heads][head_dim].
+ * Host planning happens now and is all-or-nothing (PKV_ERR_OOM changes
+ * nothing).  Per sequence in call order, per token in order:
+ *   len % B == 0                 -> take a fresh block;
+ *   else last block refcount > 1 -> copy-on-write: a fresh block receives the
+ *                                   last block's filled slots (all layers, K
+ *                                   and V), the sequence's table points at it
+ *                                   and the old block loses one reference;
+ *   then the token goes to slot (table[len / B], len % B) and len += 1.
+ * (Dendrite glossary, Copy-on-Write; the cache is append-only: Trellis page,
+ * section "LLM prefill and KV cache".)
+ * Device work, in one launch on `stream`: the copy-on-write copies and the
+ * scatter of the new K/V into their slots (they touch disjoint slots).
+ */
+pkv_status kv_append(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
+                     int32_t n_tok, const void* k_new, const void* v_new,
+                     void* stream);
+
+/*
+ * Decode attention at one layer: one query per sequence, GQA.
+ * q:   device bf16 [n_seqs][num_q_heads][head_dim]
+ * out: device fp32 [n_seqs][num_q_heads][head_dim]
+ * lse: device fp32 [n_seqs][num_q_heads] (natural-log log-sum-exp), or NULL.
+ * Each query attends to all `len` cached tokens of its sequence, its own
+ * newest token included (Trellis page, section "LLM prefill and KV cache":
+ * producing token t+1 reads K/V of tokens 0..t).
+ *   out = sum_t softmax_t(sm_scale * q.k_t) v_t,  lse = ln sum_t exp(sm_scale * q.k_t)
+ * Blocks shared by several of the sequences (a common prefix) are read once
+ * per query group and the partial softmax states are merged by log-sum-exp.
+ * Sequences may repeat.  n_seqs == 0 is a no-op.  An empty sequence gives
+ * PKV_ERR_EMPTY.
+ */
+pkv_status paged_attn_decode(pkv_pool* pool, int32_t layer, const int64_t* seqs,
+                             int32_t n_seqs, const void* q, float sm_scale,
+                             float* out, float* lse, void* stream);
+
+/*
+ * Draft-tree verify at one layer (CAST page, technical summary, "Problem":
+ * the target model checks the draft tree's tokens in one pass; EAGLE-style
+ * dynamic trees keep alternative branches).  For each sequence the last
+ * n_nodes tokens are the tree's nodes in node order (appended by kv_append);
+ * the context is the first len - n_nodes tokens.
+ * parent: host int32 [n_seqs][n_nodes], parent[0] == -1, 0 <= parent[i] < i.
+ * q:   device bf16 [n_seqs][n_nodes][num_q_heads][head_dim]
+ * out: device fp32 [n_seqs][n_nodes][num_q_heads][head_dim]
+ * lse: device fp32 [n_seqs][n_nodes][num_q_heads], or NULL.
+ * Node i attends to the whole context, to its ancestors and to itself.
+ * 1 <= n_nodes <= 64.
+ */
+pkv_status paged_attn_tree_verify(pkv_pool* pool, int32_t layer,
+                                  const int64_t* seqs, int32_t n_seqs,
+                                  int32_t n_nodes, const int32_t* parent,
+                                  const void* q, float sm_scale, float* out,
+                                  float* lse, void* stream);
+
+/* ---- introspection (host only) ---------------------------------------- */
+
+/* Block table (up to cap entries copied to out; out may be NULL when cap is 0),
+ * number of blocks and length of a sequence. */
+pkv_status seq_block_table(const pkv_pool* pool, int64_t seq, int32_t* out,
+                           int32_t cap, int32_t* n_blocks, int32_t* len);
+
+/* Refcount of one physical block. */
+pkv_status block_refcount(const pkv_pool* pool, int32_t block, int32_t* rc);
+
+/* The free list, head first (up to cap entries), and its length. */
+pkv_status free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+
+/* Where the last successful kv_append put each token and which copies it
+ * made: slots[i * n_tok + j] = block * block_size + offset for token j of
+ * sequence i; cow = (src, dst, slots copied) triples in the order taken. */
+pkv_status kv_last_append(const pkv_pool* pool, int32_t* slots, int32_t slot_cap,
+                          int32_t* n_slots, int32_t* cow, int32_t cow_cap,
+                          int32_t* n_cow);
+
+typedef struct pkv_plan_stats {
+  int64_t unique_tokens;   /* filled slots of the distinct blocks the call reads */
+  int64_t logical_tokens;  /* sum over queries of the keys each attends to */
+  int32_t unique_blocks;   /* distinct physical blocks the call reads */
+  int32_t segments;        /* shared-prefix segments (runs of blocks with one query set) */
+  int32_t work_items;      /* workgroups per kv head */
+  int32_t merged_rows;     /* query rows whose partial states are merged */
+} pkv_plan_stats;
+
+/* What paged_attn_decode would read and launch for these sequences (host only). */
+pkv_status paged_attn_decode_plan_stats(pkv_pool* pool, const int64_t* seqs,
+                                        int32_t n_seqs, pkv_plan_stats* out);
+
+/* Message of the calling thread's last error ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

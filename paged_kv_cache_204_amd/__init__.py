@@ -1,0 +1,261 @@
+"""Python binding of libpkv.so: paged, prefix-sharing KV attention for gfx950.
+
+Argument marshalling only -- every step of the path runs in the C++ host core
+and the HIP kernels behind the C ABI declared in ``include/pkv.h``.  The
+functions keep the C names.  Device arguments are raw addresses: an ``int``,
+``None`` for NULL, or any object with ``data_ptr()`` (a torch tensor, which
+must then be contiguous).  ``stream`` is a ``hipStream_t`` address (for torch:
+``torch.cuda.current_stream().cuda_stream``); None means the null stream.
+
+Errors raise :class:`PkvError` carrying the C status and message; the pool
+is unchanged when that happens.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "PkvError", "PkvDesc", "load", "library_path",
+    "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy",
+    "seq_allocate", "seq_fork", "seq_free", "kv_append",
+    "paged_attn_decode", "paged_attn_tree_verify",
+    "seq_block_table", "block_refcount", "free_list", "kv_last_append",
+    "paged_attn_decode_plan_stats", "pkv_last_error",
+    "PKV_OK", "PKV_ERR_ARG", "PKV_ERR_OOM", "PKV_ERR_SEQ", "PKV_ERR_HIP",
+    "PKV_ERR_EMPTY", "PKV_ERR_UNSUPPORTED",
+]
+
+PKV_OK = 0
+PKV_ERR_ARG = -1
+PKV_ERR_OOM = -2
+PKV_ERR_SEQ = -3
+PKV_ERR_HIP = -4
+PKV_ERR_EMPTY = -5
+PKV_ERR_UNSUPPORTED = -6
+
+_NAMES = {0: "PKV_OK", -1: "PKV_ERR_ARG", -2: "PKV_ERR_OOM", -3: "PKV_ERR_SEQ",
+          -4: "PKV_ERR_HIP", -5: "PKV_ERR_EMPTY", -6: "PKV_ERR_UNSUPPORTED"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libpkv.so")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"{_NAMES.get(code, code)}: {message}")
+        self.code = code
+        self.message = message
+
+
+class PkvDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_layers", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class PkvPlanStats(ctypes.Structure):
+    _fields_ = [("unique_tokens", ctypes.c_int64), ("logical_tokens", ctypes.c_int64),
+                ("unique_blocks", ctypes.c_int32), ("segments", ctypes.c_int32),
+                ("work_items", ctypes.c_int32), ("merged_rows", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def load():
+    """Load the built library (never builds; raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is not built; run __graft_entry__.build() or "
+            "python paged_kv_cache_204_amd/build.py")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "kv_pool_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvDesc)]),
+        "kv_pool_create": (_I32, [ctypes.POINTER(PkvDesc), _P, _P, _PI32, ctypes.POINTER(_P)]),
+        "kv_pool_destroy": (None, [_P]),
+        "seq_allocate": (_I32, [_P, _PI64]),
+        "seq_fork": (_I32, [_P, _I64, _PI64]),
+        "seq_free": (_I32, [_P, _I64]),
+        "kv_append": (_I32, [_P, _PI64, _I32, _I32, _P, _P, _P]),
+        "paged_attn_decode": (_I32, [_P, _I32, _PI64, _I32, _P, ctypes.c_float, _P, _P, _P]),
+        "paged_attn_tree_verify": (_I32, [_P, _I32, _PI64, _I32, _I32, _PI32, _P,
+                                          ctypes.c_float, _P, _P, _P]),
+        "seq_block_table": (_I32, [_P, _I64, _PI32, _I32, _PI32, _PI32]),
+        "block_refcount": (_I32, [_P, _I32, _PI32]),
+        "free_list": (_I32, [_P, _PI32, _I32, _PI32]),
+        "kv_last_append": (_I32, [_P, _PI32, _I32, _PI32, _PI32, _I32, _PI32]),
+        "paged_attn_decode_plan_stats": (_I32, [_P, _PI64, _I32, ctypes.POINTER(PkvPlanStats)]),
+        "pkv_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(code):
+    if code != PKV_OK:
+        raise PkvError(code, load().pkv_last_error().decode())
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    if hasattr(x, "data_ptr"):
+        if hasattr(x, "is_contiguous") and not x.is_contiguous():
+            raise ValueError("device arguments must be contiguous")
+        return x.data_ptr()
+    raise TypeError(f"cannot take a device address from {type(x).__name__}")
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s or None
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream or None
+    raise TypeError("stream must be an int address or have .cuda_stream")
+
+
+def _seq_array(seqs):
+    a = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64).reshape(-1))
+    return a, a.ctypes.data_as(_PI64)
+
+
+def _desc(desc):
+    if isinstance(desc, PkvDesc):
+        return desc
+    if isinstance(desc, dict):
+        return PkvDesc(**desc)
+    return PkvDesc(desc.num_blocks, desc.block_size, desc.num_layers,
+                   desc.num_q_heads, desc.num_kv_heads, desc.head_dim)
+
+
+# ------------------------------------------------------------------- calls
+
+def kv_pool_bytes(desc) -> int:
+    d = _desc(desc)
+    return load().kv_pool_bytes(ctypes.byref(d))
+
+
+def kv_pool_create(desc, k_pool=None, v_pool=None, free_order=None):
+    d = _desc(desc)
+    fo = None
+    keep = None
+    if free_order is not None:
+        keep = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+        fo = keep.ctypes.data_as(_PI32)
+    out = _P()
+    _check(load().kv_pool_create(ctypes.byref(d), _addr(k_pool), _addr(v_pool), fo,
+                                 ctypes.byref(out)))
+    return out
+
+
+def kv_pool_destroy(pool):
+    load().kv_pool_destroy(pool)
+
+
+def seq_allocate(pool) -> int:
+    out = _I64()
+    _check(load().seq_allocate(pool, ctypes.byref(out)))
+    return out.value
+
+
+def seq_fork(pool, parent) -> int:
+    out = _I64()
+    _check(load().seq_fork(pool, int(parent), ctypes.byref(out)))
+    return out.value
+
+
+def seq_free(pool, seq):
+    _check(load().seq_free(pool, int(seq)))
+
+
+def kv_append(pool, seqs, n_tok, k_new=None, v_new=None, stream=None):
+    a, p = _seq_array(seqs)
+    _check(load().kv_append(pool, p, len(a), int(n_tok), _addr(k_new), _addr(v_new),
+                            _stream(stream)))
+
+
+def paged_attn_decode(pool, layer, seqs, q, sm_scale, out, lse=None, stream=None):
+    a, p = _seq_array(seqs)
+    _check(load().paged_attn_decode(pool, int(layer), p, len(a), _addr(q), float(sm_scale),
+                                    _addr(out), _addr(lse), _stream(stream)))
+
+
+def paged_attn_tree_verify(pool, layer, seqs, n_nodes, parent, q, sm_scale, out, lse=None,
+                           stream=None):
+    a, p = _seq_array(seqs)
+    par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+    if par.size != len(a) * int(n_nodes):
+        raise ValueError("parent must hold n_seqs * n_nodes entries")
+    _check(load().paged_attn_tree_verify(pool, int(layer), p, len(a), int(n_nodes),
+                                         par.ctypes.data_as(_PI32), _addr(q), float(sm_scale),
+                                         _addr(out), _addr(lse), _stream(stream)))
+
+
+def seq_block_table(pool, seq):
+    n = _I32()
+    ln = _I32()
+    _check(load().seq_block_table(pool, int(seq), None, 0, ctypes.byref(n), ctypes.byref(ln)))
+    buf = (ctypes.c_int32 * max(1, n.value))()
+    _check(load().seq_block_table(pool, int(seq), buf, n.value, ctypes.byref(n), ctypes.byref(ln)))
+    return list(buf[:n.value]), ln.value
+
+
+def block_refcount(pool, block) -> int:
+    rc = _I32()
+    _check(load().block_refcount(pool, int(block), ctypes.byref(rc)))
+    return rc.value
+
+
+def free_list(pool):
+    n = _I32()
+    _check(load().free_list(pool, None, 0, ctypes.byref(n)))
+    buf = (ctypes.c_int32 * max(1, n.value))()
+    _check(load().free_list(pool, buf, n.value, ctypes.byref(n)))
+    return list(buf[:n.value])
+
+
+def kv_last_append(pool):
+    ns = _I32()
+    nc = _I32()
+    _check(load().kv_last_append(pool, None, 0, ctypes.byref(ns), None, 0, ctypes.byref(nc)))
+    sb = (ctypes.c_int32 * max(1, ns.value))()
+    cb = (ctypes.c_int32 * max(1, 3 * nc.value))()
+    _check(load().kv_last_append(pool, sb, ns.value, ctypes.byref(ns), cb, 3 * nc.value,
+                                 ctypes.byref(nc)))
+    cow = [tuple(cb[3 * i:3 * i + 3]) for i in range(nc.value)]
+    return list(sb[:ns.value]), cow
+
+
+def paged_attn_decode_plan_stats(pool, seqs) -> dict:
+    a, p = _seq_array(seqs)
+    st = PkvPlanStats()
+    _check(load().paged_attn_decode_plan_stats(pool, p, len(a), ctypes.byref(st)))
+    return {f: getattr(st, f) for f, _ in PkvPlanStats._fields_}
+
+
+def pkv_last_error() -> str:
+    return load().pkv_last_error().decode()

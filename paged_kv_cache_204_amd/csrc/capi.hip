@@ -1,0 +1,491 @@
+// C ABI: the calls declared in include/pkv.h.
+//
+// Host metadata lives in pkv::BlockPool (tables, refcounts, free list) and
+// the planners; this file adds the device side: the pool's own scratch
+// (plan buffers, partial softmax states), a small ring of pinned staging
+// buffers for plan uploads, and the kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pkv.h"
+#include "host/plan.hpp"
+#include "host/pool.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+pkv_status fail(pkv_status s, std::string msg) {
+  g_err = std::move(msg);
+  return s;
+}
+
+pkv_status to_status(pkv::Err e) { return static_cast<pkv_status>(static_cast<int>(e)); }
+
+#define PKV_HIP(call)                                                                 \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(PKV_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_));    \
+  } while (0)
+
+struct DevBuf {
+  void* ptr = nullptr;
+  size_t cap = 0;
+};
+
+constexpr int kStageSlots = 4;
+
+size_t align16(size_t x) { return (x + 15) & ~size_t{15}; }
+
+// Offsets of the plan arrays inside one contiguous upload.
+struct PlanLayout {
+  size_t valu = 0, mfma = 0, groups = 0, blocks = 0, merges = 0, parts = 0, total = 0;
+};
+
+PlanLayout layout_of(const pkv::Plan& p) {
+  PlanLayout o;
+  size_t at = 0;
+  auto put = [&](size_t& field, size_t bytes) {
+    field = at;
+    at += align16(bytes);
+  };
+  put(o.valu, p.valu.size() * sizeof(pkv::WorkItem));
+  put(o.mfma, p.mfma.size() * sizeof(pkv::WorkItem));
+  put(o.groups, p.groups.size() * sizeof(pkv::RowGroup));
+  put(o.blocks, p.blocks.size() * sizeof(int32_t));
+  put(o.merges, p.merges.size() * sizeof(pkv::MergeRow));
+  put(o.parts, p.parts.size() * sizeof(int32_t));
+  o.total = at;
+  return o;
+}
+
+void serialize(const pkv::Plan& p, const PlanLayout& o, char* dst) {
+  auto cp = [&](size_t off, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(dst + off, src, bytes);
+  };
+  cp(o.valu, p.valu.data(), p.valu.size() * sizeof(pkv::WorkItem));
+  cp(o.mfma, p.mfma.data(), p.mfma.size() * sizeof(pkv::WorkItem));
+  cp(o.groups, p.groups.data(), p.groups.size() * sizeof(pkv::RowGroup));
+  cp(o.blocks, p.blocks.data(), p.blocks.size() * sizeof(int32_t));
+  cp(o.merges, p.merges.data(), p.merges.size() * sizeof(pkv::MergeRow));
+  cp(o.parts, p.parts.data(), p.parts.size() * sizeof(int32_t));
+}
+
+// Makes the pool's device current for the duration of a call.
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) {
+      err = hipSetDevice(dev);
+      changed = err == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct pkv_pool {
+  explicit pkv_pool(const pkv::Shape& s, const int32_t* order) : core(s, order) {}
+  pkv::BlockPool core;
+  pkv::PlanConfig cfg;
+  bool device = false;
+  int dev = -1;
+  uint16_t* k_pool = nullptr;
+  uint16_t* v_pool = nullptr;
+  DevBuf append_plan, decode_plan, verify_plan, partials;
+  void* stage[kStageSlots] = {};
+  size_t stage_cap[kStageSlots] = {};
+  hipEvent_t stage_ev[kStageSlots] = {};
+  bool stage_used[kStageSlots] = {};
+  int stage_next = 0;
+  // decode plan cache: same sequence list on an unchanged pool -> reuse
+  bool dcache_valid = false;
+  uint64_t dcache_version = 0;
+  std::vector<int64_t> dcache_seqs;
+  pkv::Plan dplan;
+  PlanLayout dlayout;
+  pkv::Plan vplan;
+  PlanLayout vlayout;
+};
+
+namespace {
+
+pkv_status ensure(DevBuf& b, size_t bytes) {
+  if (bytes <= b.cap) return PKV_OK;
+  size_t want = bytes + bytes / 2 + 4096;
+  if (b.ptr) {
+    // the old buffer may still be read by enqueued kernels
+    PKV_HIP(hipDeviceSynchronize());
+    PKV_HIP(hipFree(b.ptr));
+    b.ptr = nullptr;
+    b.cap = 0;
+  }
+  PKV_HIP(hipMalloc(&b.ptr, want));
+  b.cap = want;
+  return PKV_OK;
+}
+
+// Copy `bytes` produced by `fill` into device buffer `dst` via a pinned
+// staging slot, ordered on `stream`.  A slot is reused only after the copy
+// that last read it has completed.
+template <class Fill>
+pkv_status upload(pkv_pool* p, DevBuf& dst, size_t bytes, hipStream_t stream, Fill fill) {
+  pkv_status s = ensure(dst, bytes);
+  if (s != PKV_OK) return s;
+  if (bytes == 0) return PKV_OK;
+  const int i = p->stage_next;
+  p->stage_next = (i + 1) % kStageSlots;
+  if (p->stage_used[i]) PKV_HIP(hipEventSynchronize(p->stage_ev[i]));
+  if (p->stage_cap[i] < bytes) {
+    if (p->stage[i]) PKV_HIP(hipHostFree(p->stage[i]));
+    p->stage[i] = nullptr;
+    p->stage_cap[i] = 0;
+    size_t want = bytes + bytes / 2 + 4096;
+    PKV_HIP(hipHostMalloc(&p->stage[i], want, hipHostMallocDefault));
+    p->stage_cap[i] = want;
+  }
+  if (!p->stage_ev[i]) PKV_HIP(hipEventCreateWithFlags(&p->stage_ev[i], hipEventDisableTiming));
+  fill(static_cast<char*>(p->stage[i]));
+  PKV_HIP(hipMemcpyAsync(dst.ptr, p->stage[i], bytes, hipMemcpyHostToDevice, stream));
+  PKV_HIP(hipEventRecord(p->stage_ev[i], stream));
+  p->stage_used[i] = true;
+  return PKV_OK;
+}
+
+pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
+                       const DevBuf& buf, int32_t layer, const void* q, float sm_scale,
+                       float* out, float* lse, hipStream_t stream) {
+  const pkv::Shape& sh = p->core.shape();
+  const char* base = static_cast<const char*>(buf.ptr);
+  pkv_status s = ensure(p->partials, static_cast<size_t>(plan.partial_rows) * (sh.head_dim + 1) * sizeof(float));
+  if (s != PKV_OK) return s;
+  float* part_o = static_cast<float*>(p->partials.ptr);
+  float* part_lse = part_o + static_cast<size_t>(plan.partial_rows) * sh.head_dim;
+
+  pkv::AttnParams ap{};
+  ap.groups = reinterpret_cast<const pkv::RowGroup*>(base + lay.groups);
+  ap.blocks = reinterpret_cast<const int32_t*>(base + lay.blocks);
+  ap.q = static_cast<const uint16_t*>(q);
+  ap.k_pool = p->k_pool;
+  ap.v_pool = p->v_pool;
+  ap.out = out;
+  ap.lse = lse;
+  ap.part_o = part_o;
+  ap.part_lse = part_lse;
+  ap.layer = layer;
+  ap.N = sh.num_blocks;
+  ap.Hq = sh.num_q_heads;
+  ap.Hkv = sh.num_kv_heads;
+  ap.G = sh.num_q_heads / sh.num_kv_heads;
+  ap.B = sh.block_size;
+  ap.log2B = p->core.log2_block();
+  ap.scale_log2 = sm_scale * pkv::kLog2eHost;
+  if (!plan.valu.empty()) {
+    ap.items = reinterpret_cast<const pkv::WorkItem*>(base + lay.valu);
+    PKV_HIP(pkv::launch_attn_valu(ap, static_cast<int32_t>(plan.valu.size()), sh.head_dim, stream));
+  }
+  if (!plan.mfma.empty())
+    return fail(PKV_ERR_UNSUPPORTED, "attention: MFMA work items are not available");
+  if (!plan.merges.empty()) {
+    pkv::MergeParams mp{};
+    mp.merges = reinterpret_cast<const pkv::MergeRow*>(base + lay.merges);
+    mp.parts = reinterpret_cast<const int32_t*>(base + lay.parts);
+    mp.part_o = part_o;
+    mp.part_lse = part_lse;
+    mp.out = out;
+    mp.lse = lse;
+    mp.Hq = sh.num_q_heads;
+    mp.D = sh.head_dim;
+    PKV_HIP(pkv::launch_merge(mp, static_cast<int32_t>(plan.merges.size()), stream));
+  }
+  return PKV_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t kv_pool_bytes(const pkv_desc* d) {
+  if (!d) return 0;
+  pkv::Shape s{d->num_blocks, d->block_size, d->num_layers, d->num_q_heads, d->num_kv_heads, d->head_dim};
+  if (!pkv::valid_shape(s, nullptr)) return 0;
+  return static_cast<size_t>(s.num_layers) * s.num_blocks * s.num_kv_heads * s.block_size *
+         s.head_dim * sizeof(uint16_t);
+}
+
+pkv_status kv_pool_create(const pkv_desc* d, void* k_pool, void* v_pool,
+                          const int32_t* free_order, pkv_pool** out) {
+  if (!d || !out) return fail(PKV_ERR_ARG, "kv_pool_create: desc and out must not be NULL");
+  *out = nullptr;
+  pkv::Shape s{d->num_blocks, d->block_size, d->num_layers, d->num_q_heads, d->num_kv_heads, d->head_dim};
+  std::string why;
+  if (!pkv::valid_shape(s, &why)) return fail(PKV_ERR_ARG, "kv_pool_create: " + why);
+  if ((k_pool == nullptr) != (v_pool == nullptr))
+    return fail(PKV_ERR_ARG, "kv_pool_create: give both device pools or neither");
+  const bool device = k_pool != nullptr;
+  if (device) {
+    if (s.head_dim != 64 && s.head_dim != 128)
+      return fail(PKV_ERR_UNSUPPORTED, "kv_pool_create: device pools need head_dim 64 or 128");
+    if (s.num_q_heads / s.num_kv_heads > 16)
+      return fail(PKV_ERR_UNSUPPORTED, "kv_pool_create: more than 16 query heads per kv head");
+    if (!aligned16(k_pool) || !aligned16(v_pool))
+      return fail(PKV_ERR_ARG, "kv_pool_create: pools must be 16-byte aligned");
+  }
+  if (free_order) {
+    std::vector<char> seen(s.num_blocks, 0);
+    for (int32_t i = 0; i < s.num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= s.num_blocks || seen[b])
+        return fail(PKV_ERR_ARG, "kv_pool_create: free_order is not a permutation of the block ids");
+      seen[b] = 1;
+    }
+  }
+  pkv_pool* p = new (std::nothrow) pkv_pool(s, free_order);
+  if (!p) return fail(PKV_ERR_ARG, "kv_pool_create: out of host memory");
+  p->device = device;
+  if (device) {
+    hipError_t e = hipGetDevice(&p->dev);
+    if (e != hipSuccess) {
+      delete p;
+      return fail(PKV_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    }
+    p->k_pool = static_cast<uint16_t*>(k_pool);
+    p->v_pool = static_cast<uint16_t*>(v_pool);
+  }
+  *out = p;
+  return PKV_OK;
+}
+
+void kv_pool_destroy(pkv_pool* p) {
+  if (!p) return;
+  if (p->device) {
+    DeviceGuard g(p->dev);
+    (void)hipDeviceSynchronize();
+    for (DevBuf* b : {&p->append_plan, &p->decode_plan, &p->verify_plan, &p->partials})
+      if (b->ptr) (void)hipFree(b->ptr);
+    for (int i = 0; i < kStageSlots; ++i) {
+      if (p->stage[i]) (void)hipHostFree(p->stage[i]);
+      if (p->stage_ev[i]) (void)hipEventDestroy(p->stage_ev[i]);
+    }
+  }
+  delete p;
+}
+
+pkv_status seq_allocate(pkv_pool* p, int64_t* out_seq) {
+  if (!p || !out_seq) return fail(PKV_ERR_ARG, "seq_allocate: NULL argument");
+  *out_seq = p->core.allocate();
+  return PKV_OK;
+}
+
+pkv_status seq_fork(pkv_pool* p, int64_t parent, int64_t* out_child) {
+  if (!p || !out_child) return fail(PKV_ERR_ARG, "seq_fork: NULL argument");
+  std::string why;
+  pkv::Err e = p->core.fork(parent, out_child, &why);
+  return e == pkv::Err::ok ? PKV_OK : fail(to_status(e), why);
+}
+
+pkv_status seq_free(pkv_pool* p, int64_t seq) {
+  if (!p) return fail(PKV_ERR_ARG, "seq_free: NULL pool");
+  std::string why;
+  pkv::Err e = p->core.release(seq, &why);
+  return e == pkv::Err::ok ? PKV_OK : fail(to_status(e), why);
+}
+
+pkv_status kv_append(pkv_pool* p, const int64_t* seqs, int32_t n_seqs, int32_t n_tok,
+                     const void* k_new, const void* v_new, void* stream) {
+  if (!p) return fail(PKV_ERR_ARG, "kv_append: NULL pool");
+  const bool has_work = n_seqs > 0 && n_tok > 0;
+  if (p->device) {
+    if (has_work && (!k_new || !v_new))
+      return fail(PKV_ERR_ARG, "kv_append: k_new and v_new are required for a device pool");
+    if (has_work && (!aligned16(k_new) || !aligned16(v_new)))
+      return fail(PKV_ERR_ARG, "kv_append: k_new / v_new must be 16-byte aligned");
+  } else if (k_new || v_new) {
+    return fail(PKV_ERR_ARG, "kv_append: a host-only pool takes no K/V data");
+  }
+  pkv::PendingAppend pa;
+  std::string why;
+  pkv::Err e = p->core.prepare_append(seqs, n_seqs, n_tok, &pa, &why);
+  if (e != pkv::Err::ok) return fail(to_status(e), why);
+  if (p->device && has_work) {
+    DeviceGuard g(p->dev);
+    PKV_HIP(g.err);
+    const pkv::Shape& sh = p->core.shape();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t slot_bytes = pa.result.slots.size() * sizeof(int32_t);
+    const size_t cow_off = align16(slot_bytes);
+    const size_t bytes = cow_off + pa.result.cow.size() * 3 * sizeof(int32_t);
+    pkv_status s = upload(p, p->append_plan, bytes, st, [&](char* dst) {
+      std::memcpy(dst, pa.result.slots.data(), slot_bytes);
+      int32_t* c = reinterpret_cast<int32_t*>(dst + cow_off);
+      for (size_t k = 0; k < pa.result.cow.size(); ++k) {
+        c[3 * k + 0] = pa.result.cow[k].src;
+        c[3 * k + 1] = pa.result.cow[k].dst;
+        c[3 * k + 2] = pa.result.cow[k].n_slots;
+      }
+    });
+    if (s != PKV_OK) return s;
+    pkv::AppendParams ap{};
+    ap.k_new = static_cast<const uint16_t*>(k_new);
+    ap.v_new = static_cast<const uint16_t*>(v_new);
+    ap.k_pool = p->k_pool;
+    ap.v_pool = p->v_pool;
+    ap.slots = static_cast<const int32_t*>(p->append_plan.ptr);
+    ap.cow = reinterpret_cast<const int32_t*>(static_cast<const char*>(p->append_plan.ptr) + cow_off);
+    ap.n_rows = n_seqs * n_tok;
+    ap.n_cow = static_cast<int32_t>(pa.result.cow.size());
+    ap.L = sh.num_layers;
+    ap.N = sh.num_blocks;
+    ap.Hkv = sh.num_kv_heads;
+    ap.B = sh.block_size;
+    ap.log2B = p->core.log2_block();
+    ap.D = sh.head_dim;
+    PKV_HIP(pkv::launch_append(ap, st));
+  }
+  p->core.commit_append(std::move(pa));
+  return PKV_OK;
+}
+
+pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs,
+                             const void* q, float sm_scale, float* out, float* lse, void* stream) {
+  if (!p) return fail(PKV_ERR_ARG, "paged_attn_decode: NULL pool");
+  if (!p->device) return fail(PKV_ERR_ARG, "paged_attn_decode: the pool has no device storage");
+  if (n_seqs < 0) return fail(PKV_ERR_ARG, "paged_attn_decode: negative n_seqs");
+  if (n_seqs == 0) return PKV_OK;
+  if (!seqs || !q || !out) return fail(PKV_ERR_ARG, "paged_attn_decode: NULL seqs, q or out");
+  if (layer < 0 || layer >= p->core.shape().num_layers)
+    return fail(PKV_ERR_ARG, "paged_attn_decode: layer out of range");
+  if (!aligned16(q) || !aligned16(out))
+    return fail(PKV_ERR_ARG, "paged_attn_decode: q and out must be 16-byte aligned");
+  DeviceGuard g(p->dev);
+  PKV_HIP(g.err);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool hit = p->dcache_valid && p->dcache_version == p->core.version() &&
+                   p->dcache_seqs.size() == static_cast<size_t>(n_seqs) &&
+                   std::memcmp(p->dcache_seqs.data(), seqs, n_seqs * sizeof(int64_t)) == 0;
+  if (!hit) {
+    p->dcache_valid = false;
+    std::string why;
+    pkv::Err e = pkv::plan_decode(p->core, seqs, n_seqs, p->cfg, &p->dplan, &why);
+    if (e != pkv::Err::ok) return fail(to_status(e), why);
+    p->dlayout = layout_of(p->dplan);
+    pkv_status s = upload(p, p->decode_plan, p->dlayout.total, st,
+                          [&](char* dst) { serialize(p->dplan, p->dlayout, dst); });
+    if (s != PKV_OK) return s;
+    p->dcache_seqs.assign(seqs, seqs + n_seqs);
+    p->dcache_version = p->core.version();
+    p->dcache_valid = true;
+  }
+  return launch_plan(p, p->dplan, p->dlayout, p->decode_plan, layer, q, sm_scale, out, lse, st);
+}
+
+pkv_status paged_attn_tree_verify(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs,
+                                  int32_t n_nodes, const int32_t* parent, const void* q,
+                                  float sm_scale, float* out, float* lse, void* stream) {
+  if (!p) return fail(PKV_ERR_ARG, "paged_attn_tree_verify: NULL pool");
+  if (!p->device) return fail(PKV_ERR_ARG, "paged_attn_tree_verify: the pool has no device storage");
+  if (n_seqs < 0) return fail(PKV_ERR_ARG, "paged_attn_tree_verify: negative n_seqs");
+  if (n_seqs == 0) return PKV_OK;
+  if (!seqs || !parent || !q || !out)
+    return fail(PKV_ERR_ARG, "paged_attn_tree_verify: NULL seqs, parent, q or out");
+  if (layer < 0 || layer >= p->core.shape().num_layers)
+    return fail(PKV_ERR_ARG, "paged_attn_tree_verify: layer out of range");
+  if (!aligned16(q) || !aligned16(out))
+    return fail(PKV_ERR_ARG, "paged_attn_tree_verify: q and out must be 16-byte aligned");
+  std::string why;
+  pkv::Err e = pkv::plan_verify(p->core, seqs, n_seqs, n_nodes, parent, p->cfg, &p->vplan, &why);
+  if (e != pkv::Err::ok) return fail(to_status(e), why);
+  DeviceGuard g(p->dev);
+  PKV_HIP(g.err);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  p->vlayout = layout_of(p->vplan);
+  pkv_status s = upload(p, p->verify_plan, p->vlayout.total, st,
+                        [&](char* dst) { serialize(p->vplan, p->vlayout, dst); });
+  if (s != PKV_OK) return s;
+  return launch_plan(p, p->vplan, p->vlayout, p->verify_plan, layer, q, sm_scale, out, lse, st);
+}
+
+pkv_status seq_block_table(const pkv_pool* p, int64_t seq, int32_t* out, int32_t cap,
+                           int32_t* n_blocks, int32_t* len) {
+  if (!p) return fail(PKV_ERR_ARG, "seq_block_table: NULL pool");
+  const pkv::SeqState* s = p->core.find(seq);
+  if (!s) return fail(PKV_ERR_SEQ, "seq_block_table: unknown sequence " + std::to_string(seq));
+  const int32_t n = static_cast<int32_t>(s->table.size());
+  if (cap > 0 && !out) return fail(PKV_ERR_ARG, "seq_block_table: NULL out with cap > 0");
+  for (int32_t i = 0; i < n && i < cap; ++i) out[i] = s->table[i];
+  if (n_blocks) *n_blocks = n;
+  if (len) *len = s->len;
+  return PKV_OK;
+}
+
+pkv_status block_refcount(const pkv_pool* p, int32_t block, int32_t* rc) {
+  if (!p || !rc) return fail(PKV_ERR_ARG, "block_refcount: NULL argument");
+  if (block < 0 || block >= p->core.shape().num_blocks)
+    return fail(PKV_ERR_ARG, "block_refcount: block out of range");
+  *rc = p->core.refcount(block);
+  return PKV_OK;
+}
+
+pkv_status free_list(const pkv_pool* p, int32_t* out, int32_t cap, int32_t* n) {
+  if (!p) return fail(PKV_ERR_ARG, "free_list: NULL pool");
+  if (cap > 0 && !out) return fail(PKV_ERR_ARG, "free_list: NULL out with cap > 0");
+  const auto& f = p->core.free_list();
+  int32_t i = 0;
+  for (auto it = f.begin(); it != f.end() && i < cap; ++it) out[i++] = *it;
+  if (n) *n = static_cast<int32_t>(f.size());
+  return PKV_OK;
+}
+
+pkv_status kv_last_append(const pkv_pool* p, int32_t* slots, int32_t slot_cap, int32_t* n_slots,
+                          int32_t* cow, int32_t cow_cap, int32_t* n_cow) {
+  if (!p) return fail(PKV_ERR_ARG, "kv_last_append: NULL pool");
+  if ((slot_cap > 0 && !slots) || (cow_cap > 0 && !cow))
+    return fail(PKV_ERR_ARG, "kv_last_append: NULL buffer with cap > 0");
+  const pkv::AppendResult& r = p->core.last_append();
+  const int32_t ns = static_cast<int32_t>(r.slots.size());
+  for (int32_t i = 0; i < ns && i < slot_cap; ++i) slots[i] = r.slots[i];
+  const int32_t nc = static_cast<int32_t>(r.cow.size());
+  for (int32_t i = 0; i < nc && 3 * i + 2 < cow_cap; ++i) {
+    cow[3 * i + 0] = r.cow[i].src;
+    cow[3 * i + 1] = r.cow[i].dst;
+    cow[3 * i + 2] = r.cow[i].n_slots;
+  }
+  if (n_slots) *n_slots = ns;
+  if (n_cow) *n_cow = nc;
+  return PKV_OK;
+}
+
+pkv_status paged_attn_decode_plan_stats(pkv_pool* p, const int64_t* seqs, int32_t n_seqs,
+                                        pkv_plan_stats* out) {
+  if (!p || !out || (n_seqs > 0 && !seqs) || n_seqs < 0)
+    return fail(PKV_ERR_ARG, "paged_attn_decode_plan_stats: bad argument");
+  pkv::Plan plan;
+  std::string why;
+  pkv::Err e = pkv::plan_decode(p->core, seqs, n_seqs, p->cfg, &plan, &why);
+  if (e != pkv::Err::ok) return fail(to_status(e), why);
+  out->unique_tokens = plan.unique_tokens;
+  out->logical_tokens = plan.logical_tokens;
+  out->unique_blocks = plan.unique_blocks;
+  out->segments = plan.segments;
+  out->work_items = static_cast<int32_t>(plan.valu.size() + plan.mfma.size());
+  out->merged_rows = static_cast<int32_t>(plan.merges.size()) * p->core.shape().num_q_heads;
+  return PKV_OK;
+}
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

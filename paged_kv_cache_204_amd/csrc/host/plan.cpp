@@ -1,0 +1,295 @@
+#include "plan.hpp"
+
+#include <algorithm>
+#include <climits>
+#include <unordered_map>
+
+namespace pkv {
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Segment {
+  std::vector<int32_t> queries;  // indices into the call's query list
+  const int32_t* blocks;         // the segment's first block in a member's table
+  int32_t nblk;
+  int32_t ntok;
+};
+
+// Chunk length in tokens for a total amount of (token x item-row-tile) work.
+int32_t pick_chunk(int64_t work_tokens, int32_t kv_heads, int32_t block_size,
+                   const PlanConfig& cfg) {
+  const int32_t unit = std::max(cfg.tile, block_size);
+  int64_t per_wg = ceil_div(work_tokens * kv_heads, std::max(1, cfg.target_wgs));
+  int64_t chunk = ceil_div(std::max<int64_t>(per_wg, 1), unit) * unit;
+  int64_t cap = std::max<int64_t>(unit, (cfg.max_chunk / unit) * unit);
+  return static_cast<int32_t>(std::min(chunk, cap));
+}
+
+// Partial-row bookkeeping shared by both planners: `owner[g]` is the query
+// vector of row group g; items that do not cover all keys of their queries
+// get partial rows, and every such query gets a merge row.
+void finish_parts(Plan* plan, const std::vector<int32_t>& n_parts, int32_t hq) {
+  std::vector<std::vector<int32_t>> parts_of(n_parts.size());
+  auto assign = [&](std::vector<WorkItem>& items) {
+    for (WorkItem& it : items) {
+      bool direct = true;
+      for (int32_t u = 0; u < it.n_grp; ++u)
+        if (n_parts[plan->groups[it.grp_off + u].q_index] != 1) direct = false;
+      if (direct) {
+        it.part_base = -1;
+        continue;
+      }
+      it.part_base = static_cast<int32_t>(plan->partial_rows);
+      plan->partial_rows += static_cast<int64_t>(it.n_grp) * hq;
+      for (int32_t u = 0; u < it.n_grp; ++u)
+        parts_of[plan->groups[it.grp_off + u].q_index].push_back(it.part_base + u * hq);
+    }
+  };
+  assign(plan->valu);
+  assign(plan->mfma);
+  for (size_t q = 0; q < parts_of.size(); ++q) {
+    if (n_parts[q] <= 1) continue;
+    MergeRow m;
+    m.q_index = static_cast<int32_t>(q);
+    m.parts_off = static_cast<int32_t>(plan->parts.size());
+    m.n_parts = static_cast<int32_t>(parts_of[q].size());
+    m.pad = 0;
+    plan->parts.insert(plan->parts.end(), parts_of[q].begin(), parts_of[q].end());
+    plan->merges.push_back(m);
+  }
+}
+
+}  // namespace
+
+bool ancestor_masks(const int32_t* parent, int32_t n_nodes, uint64_t* anc) {
+  if (n_nodes < 1 || n_nodes > 64 || !parent || parent[0] != -1) return false;
+  anc[0] = 1;
+  for (int32_t i = 1; i < n_nodes; ++i) {
+    if (parent[i] < 0 || parent[i] >= i) return false;
+    anc[i] = anc[parent[i]] | (uint64_t{1} << i);
+  }
+  return true;
+}
+
+Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
+                const PlanConfig& cfg, Plan* plan, std::string* why) {
+  *plan = Plan{};
+  const Shape& sh = pool.shape();
+  const int32_t B = sh.block_size;
+  const int32_t G = sh.num_q_heads / sh.num_kv_heads;
+  std::vector<const SeqState*> st(n_seqs);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    st[i] = pool.find(seqs[i]);
+    if (!st[i]) {
+      *why = "paged_attn_decode: unknown sequence " + std::to_string(seqs[i]);
+      return Err::seq;
+    }
+    if (st[i]->len == 0) {
+      *why = "paged_attn_decode: sequence " + std::to_string(seqs[i]) + " is empty";
+      return Err::empty;
+    }
+    plan->logical_tokens += st[i]->len;
+  }
+  auto nblk = [&](int32_t q) { return static_cast<int32_t>(st[q]->table.size()); };
+  auto fill = [&](int32_t q, int32_t pos) {
+    return std::min(B, st[q]->len - pos * B);
+  };
+
+  // ---- trie over block ids, compressed into segments ----
+  std::vector<Segment> segs;
+  struct Frame {
+    std::vector<int32_t> qs;
+    int32_t pos;
+  };
+  std::vector<Frame> stack;
+  if (n_seqs > 0) {
+    Frame root;
+    root.pos = 0;
+    for (int32_t i = 0; i < n_seqs; ++i) root.qs.push_back(i);
+    stack.push_back(std::move(root));
+  }
+  while (!stack.empty()) {
+    Frame f = std::move(stack.back());
+    stack.pop_back();
+    const std::vector<int32_t>& t0 = st[f.qs[0]]->table;
+    int32_t e = f.pos;
+    for (;;) {
+      bool same = true;
+      for (int32_t q : f.qs)
+        if (nblk(q) <= e || st[q]->table[e] != t0[e]) {
+          same = false;
+          break;
+        }
+      if (!same) break;
+      ++e;
+    }
+    if (e > f.pos) {
+      Segment s;
+      s.queries = f.qs;
+      s.blocks = t0.data() + f.pos;
+      s.nblk = e - f.pos;
+      s.ntok = (s.nblk - 1) * B + fill(f.qs[0], e - 1);
+      for (int32_t q : f.qs)
+        if (fill(q, e - 1) != fill(f.qs[0], e - 1)) {
+          *why = "paged_attn_decode: a shared block has different fills (pool invariant broken)";
+          return Err::arg;
+        }
+      segs.push_back(std::move(s));
+    }
+    // children keyed by the next block id, in first-appearance order
+    std::vector<Frame> kids;
+    std::unordered_map<int32_t, size_t> index;
+    for (int32_t q : f.qs) {
+      if (nblk(q) <= e) continue;
+      int32_t b = st[q]->table[e];
+      auto it = index.find(b);
+      if (it == index.end()) {
+        index.emplace(b, kids.size());
+        kids.push_back(Frame{{q}, e});
+      } else {
+        kids[it->second].qs.push_back(q);
+      }
+    }
+    for (auto it = kids.rbegin(); it != kids.rend(); ++it) stack.push_back(std::move(*it));
+  }
+  plan->segments = static_cast<int32_t>(segs.size());
+
+  // ---- chunking ----
+  auto rows_per_item = [&](const Segment& s) {
+    int64_t rows = static_cast<int64_t>(s.queries.size()) * G;
+    bool mfma = cfg.mfma_min_rows > 0 && rows >= cfg.mfma_min_rows;
+    return mfma ? cfg.mfma_rows : cfg.valu_rows;
+  };
+  int64_t work = 0;
+  for (const Segment& s : segs) {
+    plan->unique_tokens += s.ntok;
+    plan->unique_blocks += s.nblk;
+    int32_t per = std::max(1, rows_per_item(s) / G);
+    work += static_cast<int64_t>(s.ntok) * ceil_div(static_cast<int64_t>(s.queries.size()), per);
+  }
+  const int32_t chunk = pick_chunk(work, sh.num_kv_heads, B, cfg);
+
+  std::vector<int32_t> n_parts(n_seqs, 0);
+  for (const Segment& s : segs) {
+    const bool mfma = cfg.mfma_min_rows > 0 &&
+                      static_cast<int64_t>(s.queries.size()) * G >= cfg.mfma_min_rows;
+    const int32_t per = std::max(1, (mfma ? cfg.mfma_rows : cfg.valu_rows) / G);
+    const int32_t nchunk = static_cast<int32_t>(ceil_div(s.ntok, chunk));
+    for (int32_t q : s.queries) n_parts[q] += nchunk;
+    const int32_t blk_base = static_cast<int32_t>(plan->blocks.size());
+    plan->blocks.insert(plan->blocks.end(), s.blocks, s.blocks + s.nblk);
+    for (size_t u0 = 0; u0 < s.queries.size(); u0 += per) {
+      const int32_t ng = static_cast<int32_t>(std::min<size_t>(per, s.queries.size() - u0));
+      const int32_t grp_off = static_cast<int32_t>(plan->groups.size());
+      for (int32_t u = 0; u < ng; ++u)
+        plan->groups.push_back(RowGroup{s.queries[u0 + u], -1, 0u, 0u});
+      for (int32_t c = 0; c < nchunk; ++c) {
+        WorkItem it;
+        it.blk_off = blk_base + c * (chunk / B);
+        it.n_tok = std::min(chunk, s.ntok - c * chunk);
+        it.tail_start = INT_MAX;
+        it.tail_node0 = 0;
+        it.grp_off = grp_off;
+        it.n_grp = ng;
+        it.part_base = -1;
+        it.xcd_slot = 0;
+        (mfma ? plan->mfma : plan->valu).push_back(it);
+      }
+    }
+  }
+  finish_parts(plan, n_parts, sh.num_q_heads);
+  return Err::ok;
+}
+
+Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
+                int32_t n_nodes, const int32_t* parent, const PlanConfig& cfg,
+                Plan* plan, std::string* why) {
+  *plan = Plan{};
+  const Shape& sh = pool.shape();
+  const int32_t B = sh.block_size;
+  const int32_t G = sh.num_q_heads / sh.num_kv_heads;
+  if (n_nodes < 1 || n_nodes > 64) {
+    *why = "paged_attn_tree_verify: n_nodes must be in 1..64";
+    return Err::arg;
+  }
+  std::vector<const SeqState*> st(n_seqs);
+  std::vector<uint64_t> anc(static_cast<size_t>(n_seqs) * n_nodes);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    st[i] = pool.find(seqs[i]);
+    if (!st[i]) {
+      *why = "paged_attn_tree_verify: unknown sequence " + std::to_string(seqs[i]);
+      return Err::seq;
+    }
+    if (st[i]->len < n_nodes) {
+      *why = "paged_attn_tree_verify: sequence " + std::to_string(seqs[i]) +
+             " is shorter than its tree";
+      return Err::arg;
+    }
+    if (!ancestor_masks(parent + static_cast<size_t>(i) * n_nodes, n_nodes,
+                        anc.data() + static_cast<size_t>(i) * n_nodes)) {
+      *why = "paged_attn_tree_verify: parent[] of sequence " + std::to_string(i) +
+             " is not a tree in node order (parent[0] = -1, 0 <= parent[i] < i)";
+      return Err::arg;
+    }
+  }
+  const bool mfma = cfg.mfma_min_rows > 0 &&
+                    static_cast<int64_t>(n_nodes) * G >= cfg.mfma_min_rows;
+  const int32_t per = std::max(1, (mfma ? cfg.mfma_rows : cfg.valu_rows) / G);
+  const int64_t subsets = ceil_div(n_nodes, per);
+  int64_t work = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    work += static_cast<int64_t>(st[i]->len) * subsets;
+    plan->unique_tokens += st[i]->len;
+    plan->unique_blocks += static_cast<int32_t>(st[i]->table.size());
+  }
+  plan->segments = n_seqs;
+  const int32_t chunk = pick_chunk(work, sh.num_kv_heads, B, cfg);
+  std::vector<int32_t> n_parts(static_cast<size_t>(n_seqs) * n_nodes, 0);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t len = st[i]->len;
+    const int32_t ctx = len - n_nodes;
+    const int32_t nchunk = static_cast<int32_t>(ceil_div(len, chunk));
+    const int32_t blk_base = static_cast<int32_t>(plan->blocks.size());
+    plan->blocks.insert(plan->blocks.end(), st[i]->table.begin(), st[i]->table.end());
+    for (int32_t j = 0; j < n_nodes; ++j) {
+      n_parts[static_cast<size_t>(i) * n_nodes + j] = nchunk;
+      // logical keys of node j: the context plus its ancestors and itself
+      plan->logical_tokens += ctx + __builtin_popcountll(anc[static_cast<size_t>(i) * n_nodes + j]);
+    }
+    for (int32_t j0 = 0; j0 < n_nodes; j0 += per) {
+      const int32_t ng = std::min(per, n_nodes - j0);
+      const int32_t grp_off = static_cast<int32_t>(plan->groups.size());
+      for (int32_t j = j0; j < j0 + ng; ++j) {
+        uint64_t m = anc[static_cast<size_t>(i) * n_nodes + j];
+        plan->groups.push_back(RowGroup{i * n_nodes + j, j, static_cast<uint32_t>(m),
+                                        static_cast<uint32_t>(m >> 32)});
+      }
+      for (int32_t c = 0; c < nchunk; ++c) {
+        const int32_t start = c * chunk;
+        WorkItem it;
+        it.blk_off = blk_base + start / B;
+        it.n_tok = std::min(chunk, len - start);
+        if (ctx - start >= it.n_tok) {
+          it.tail_start = INT_MAX;
+          it.tail_node0 = 0;
+        } else if (start >= ctx) {
+          it.tail_start = 0;
+          it.tail_node0 = start - ctx;
+        } else {
+          it.tail_start = ctx - start;
+          it.tail_node0 = 0;
+        }
+        it.grp_off = grp_off;
+        it.n_grp = ng;
+        it.part_base = -1;
+        it.xcd_slot = 0;
+        (mfma ? plan->mfma : plan->valu).push_back(it);
+      }
+    }
+  }
+  finish_parts(plan, n_parts, sh.num_q_heads);
+  return Err::ok;
+}
+
+}  // namespace pkv

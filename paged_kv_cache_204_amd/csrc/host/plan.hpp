@@ -1,0 +1,62 @@
+// Host planners for the attention calls (no HIP in here).
+//
+// Decode: the batch's block tables are grouped into a trie keyed by physical
+// block id, compressed into segments -- maximal runs of blocks that one set of
+// queries shares.  This mirrors the radix-tree view of shared prefixes
+// (SGLang RadixAttention page, "Mathematical and data-structure foundations"
+// and the match / split operations), but keyed on blocks the pool already
+// shares, so no token comparison is needed.  Each segment is read once per
+// query group (all of the segment's queries x the GQA heads of one kv head)
+// instead of once per query, split into key chunks for parallelism, and the
+// partial softmax states are merged by log-sum-exp.
+//
+// Tree verify: one key range per sequence (context + draft-tree tail),
+// split into chunks; the row groups are the tree nodes with their
+// ancestor-or-self masks.
+#pragma once
+
+#include <string>
+#include <vector>
+
+#include "../plan_format.h"
+#include "pool.hpp"
+
+namespace pkv {
+
+struct PlanConfig {
+  int32_t valu_rows = 16;      // rows (groups x G) per VALU work item, <= 16
+  int32_t mfma_rows = 256;     // rows per MFMA work item
+  int32_t mfma_min_rows = 0;   // segments with at least this many rows use MFMA; 0 = never
+  int32_t target_wgs = 1024;   // workgroups to aim for over all kv heads
+  int32_t tile = 64;           // key tokens per kernel tile; chunks are multiples
+  int32_t max_chunk = 4096;    // key tokens per work item at most
+};
+
+struct Plan {
+  std::vector<WorkItem> valu;   // items for the VALU kernel
+  std::vector<WorkItem> mfma;   // items for the MFMA kernel
+  std::vector<RowGroup> groups;
+  std::vector<int32_t> blocks;
+  std::vector<MergeRow> merges;
+  std::vector<int32_t> parts;
+  int64_t partial_rows = 0;
+  // what the call reads
+  int64_t unique_tokens = 0;
+  int64_t logical_tokens = 0;
+  int32_t unique_blocks = 0;
+  int32_t segments = 0;
+};
+
+Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
+                const PlanConfig& cfg, Plan* plan, std::string* why);
+
+Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
+                int32_t n_nodes, const int32_t* parent, const PlanConfig& cfg,
+                Plan* plan, std::string* why);
+
+// Ancestor-or-self masks of one draft tree: anc[0] = 1,
+// anc[i] = anc[parent[i]] | 1 << i.  False if parent[] is not a tree in node
+// order (parent[0] == -1, 0 <= parent[i] < i) or n_nodes is outside 1..64.
+bool ancestor_masks(const int32_t* parent, int32_t n_nodes, uint64_t* anc);
+
+}  // namespace pkv

@@ -1,0 +1,158 @@
+#include "pool.hpp"
+
+#include <unordered_set>
+
+namespace pkv {
+
+bool valid_shape(const Shape& s, std::string* why) {
+  auto fail = [&](const char* m) {
+    if (why) *why = m;
+    return false;
+  };
+  if (s.num_blocks < 1) return fail("num_blocks must be >= 1");
+  if (s.block_size < 1 || s.block_size > 128 || (s.block_size & (s.block_size - 1)))
+    return fail("block_size must be a power of two in 1..128");
+  if (s.num_layers < 1) return fail("num_layers must be >= 1");
+  if (s.num_kv_heads < 1 || s.num_q_heads < 1 || s.num_q_heads % s.num_kv_heads)
+    return fail("num_q_heads must be a positive multiple of num_kv_heads");
+  if (s.head_dim < 1) return fail("head_dim must be >= 1");
+  if (static_cast<int64_t>(s.num_blocks) * s.block_size > INT32_MAX)
+    return fail("num_blocks * block_size must fit in int32");
+  return true;
+}
+
+BlockPool::BlockPool(const Shape& s, const int32_t* free_order)
+    : shape_(s), rc_(s.num_blocks, 0) {
+  while ((1 << log2b_) < s.block_size) ++log2b_;
+  for (int32_t i = 0; i < s.num_blocks; ++i)
+    fifo_.push_back(free_order ? free_order[i] : i);
+}
+
+int64_t BlockPool::allocate() {
+  int64_t id = next_id_++;
+  seqs_.emplace(id, SeqState{});
+  ++version_;
+  return id;
+}
+
+const SeqState* BlockPool::find(int64_t seq) const {
+  auto it = seqs_.find(seq);
+  return it == seqs_.end() ? nullptr : &it->second;
+}
+
+Err BlockPool::fork(int64_t parent, int64_t* child, std::string* why) {
+  auto it = seqs_.find(parent);
+  if (it == seqs_.end()) {
+    *why = "seq_fork: unknown parent sequence " + std::to_string(parent);
+    return Err::seq;
+  }
+  SeqState copy = it->second;  // table pointers only; no K/V moves
+  for (int32_t b : copy.table) ++rc_[b];
+  int64_t id = next_id_++;
+  seqs_.emplace(id, std::move(copy));
+  *child = id;
+  ++version_;
+  return Err::ok;
+}
+
+Err BlockPool::release(int64_t seq, std::string* why) {
+  auto it = seqs_.find(seq);
+  if (it == seqs_.end()) {
+    *why = "seq_free: unknown sequence " + std::to_string(seq);
+    return Err::seq;
+  }
+  for (int32_t b : it->second.table) {
+    if (--rc_[b] == 0) fifo_.push_back(b);
+  }
+  seqs_.erase(it);
+  ++version_;
+  return Err::ok;
+}
+
+Err BlockPool::prepare_append(const int64_t* seqs, int32_t n_seqs, int32_t n_tok,
+                              PendingAppend* out, std::string* why) const {
+  if (n_seqs < 0 || n_tok < 0) {
+    *why = "kv_append: negative count";
+    return Err::arg;
+  }
+  if (n_seqs > 0 && !seqs) {
+    *why = "kv_append: seqs is NULL";
+    return Err::arg;
+  }
+  const int32_t B = shape_.block_size;
+  std::vector<const SeqState*> st(n_seqs);
+  {
+    std::unordered_set<int64_t> seen;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      auto it = seqs_.find(seqs[i]);
+      if (it == seqs_.end()) {
+        *why = "kv_append: unknown sequence " + std::to_string(seqs[i]);
+        return Err::seq;
+      }
+      if (!seen.insert(seqs[i]).second) {
+        *why = "kv_append: sequence " + std::to_string(seqs[i]) + " appears twice";
+        return Err::arg;
+      }
+      if (static_cast<int64_t>(it->second.len) + n_tok > INT32_MAX / 2) {
+        *why = "kv_append: sequence length would overflow";
+        return Err::arg;
+      }
+      st[i] = &it->second;
+    }
+  }
+  // Simulate on copies.  Touched refcounts live in a side map; blocks come
+  // from the free-list head in order.
+  std::unordered_map<int32_t, int32_t> rcm;
+  auto rc_of = [&](int32_t b) {
+    auto it = rcm.find(b);
+    return it == rcm.end() ? rc_[b] : it->second;
+  };
+  size_t taken = 0;
+  out->result.slots.assign(static_cast<size_t>(n_seqs) * n_tok, 0);
+  out->result.cow.clear();
+  out->states.clear();
+  out->states.reserve(n_seqs);
+  for (int32_t i = 0; i < n_seqs && n_tok > 0; ++i) {
+    SeqState s = *st[i];
+    for (int32_t j = 0; j < n_tok; ++j) {
+      const int32_t off = s.len % B;
+      if (off == 0) {
+        if (taken >= fifo_.size()) {
+          *why = "kv_append: pool exhausted (" + std::to_string(fifo_.size()) + " free blocks)";
+          return Err::oom;
+        }
+        const int32_t b = fifo_[taken++];
+        rcm[b] = 1;
+        s.table.push_back(b);
+      } else if (rc_of(s.table.back()) > 1) {
+        if (taken >= fifo_.size()) {
+          *why = "kv_append: pool exhausted (" + std::to_string(fifo_.size()) + " free blocks)";
+          return Err::oom;
+        }
+        const int32_t src = s.table.back();
+        const int32_t dst = fifo_[taken++];
+        rcm[dst] = 1;
+        rcm[src] = rc_of(src) - 1;
+        s.table.back() = dst;
+        out->result.cow.push_back(CowCopy{src, dst, off});
+      }
+      out->result.slots[static_cast<size_t>(i) * n_tok + j] = s.table[s.len / B] * B + off;
+      ++s.len;
+    }
+    out->states.emplace_back(seqs[i], std::move(s));
+  }
+  out->refcounts.assign(rcm.begin(), rcm.end());
+  out->taken = taken;
+  out->version = version_;
+  return Err::ok;
+}
+
+void BlockPool::commit_append(PendingAppend&& pa) {
+  for (size_t k = 0; k < pa.taken; ++k) fifo_.pop_front();
+  for (const auto& br : pa.refcounts) rc_[br.first] = br.second;
+  for (auto& ss : pa.states) seqs_[ss.first] = std::move(ss.second);
+  if (!pa.states.empty()) ++version_;
+  last_append_ = std::move(pa.result);
+}
+
+}  // namespace pkv

@@ -1,0 +1,56 @@
+// Launch parameters and launchers of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan_format.h"
+
+namespace pkv {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Copy-on-write copies plus the scatter of new K/V into their slots.
+struct AppendParams {
+  const uint16_t* k_new;  // [L][n_rows][Hkv][D], n_rows = n_seqs * n_tok
+  const uint16_t* v_new;
+  uint16_t* k_pool;       // [L][N][Hkv][B][D]
+  uint16_t* v_pool;
+  const int32_t* slots;   // [n_rows] block * B + offset
+  const int32_t* cow;     // [n_cow][3] (src, dst, filled slots)
+  int32_t n_rows;
+  int32_t n_cow;
+  int32_t L, N, Hkv, B, log2B, D;
+};
+
+// One attention launch over a list of work items (kv head = blockIdx.y).
+struct AttnParams {
+  const WorkItem* items;
+  const RowGroup* groups;
+  const int32_t* blocks;
+  const uint16_t* q;       // [n_q][Hq][D]
+  const uint16_t* k_pool;  // [L][N][Hkv][B][D]
+  const uint16_t* v_pool;
+  float* out;              // [n_q][Hq][D]
+  float* lse;              // [n_q][Hq] natural log, or null
+  float* part_o;           // [partial rows][D]
+  float* part_lse;         // [partial rows], base-2 log
+  int32_t layer, N, Hq, Hkv, G, B, log2B;
+  float scale_log2;        // sm_scale * log2(e)
+};
+
+struct MergeParams {
+  const MergeRow* merges;
+  const int32_t* parts;
+  const float* part_o;
+  const float* part_lse;   // base-2
+  float* out;
+  float* lse;              // natural log, or null
+  int32_t Hq, D;
+};
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_attn_valu(const AttnParams& p, int32_t n_items, int32_t head_dim, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, int32_t n_rows, hipStream_t s);
+
+}  // namespace pkv
