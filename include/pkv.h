@@ -197,6 +197,19 @@ typedef struct pkv_plan_stats {
 pkv_status paged_attn_decode_plan_stats(pkv_pool* pool, const int64_t* seqs,
                                         int32_t n_seqs, pkv_plan_stats* out);
 
+/* ---- kernel timing (benchmarks) --------------------------------------- */
+
+/* When enabled, every paged_attn_decode / paged_attn_tree_verify call records
+ * a pair of HIP events on its stream around its attention kernels (the plan
+ * upload, when there is one, stays outside).  Disabling drops pending pairs. */
+pkv_status pkv_timing_enable(pkv_pool* pool, int32_t enable);
+
+/* Synchronise the recorded events and return the summed kernel time in ms
+ * and the number of bracketed calls since the last reset; reset != 0 starts
+ * a new count. */
+pkv_status pkv_timing_read(pkv_pool* pool, double* total_ms, int64_t* calls,
+                           int32_t reset);
+
 /* Message of the calling thread's last error ("" if none). */
 const char* pkv_last_error(void);
 

@@ -24,7 +24,7 @@ __all__ = [
     "seq_allocate", "seq_fork", "seq_free", "kv_append",
     "paged_attn_decode", "paged_attn_tree_verify",
     "seq_block_table", "block_refcount", "free_list", "kv_last_append",
-    "paged_attn_decode_plan_stats", "pkv_last_error",
+    "paged_attn_decode_plan_stats", "pkv_timing_enable", "pkv_timing_read", "pkv_last_error",
     "PKV_OK", "PKV_ERR_ARG", "PKV_ERR_OOM", "PKV_ERR_SEQ", "PKV_ERR_HIP",
     "PKV_ERR_EMPTY", "PKV_ERR_UNSUPPORTED",
 ]
@@ -101,6 +101,8 @@ def load():
         "free_list": (_I32, [_P, _PI32, _I32, _PI32]),
         "kv_last_append": (_I32, [_P, _PI32, _I32, _PI32, _PI32, _I32, _PI32]),
         "paged_attn_decode_plan_stats": (_I32, [_P, _PI64, _I32, ctypes.POINTER(PkvPlanStats)]),
+        "pkv_timing_enable": (_I32, [_P, _I32]),
+        "pkv_timing_read": (_I32, [_P, ctypes.POINTER(ctypes.c_double), _PI64, _I32]),
         "pkv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -255,6 +257,18 @@ def paged_attn_decode_plan_stats(pool, seqs) -> dict:
     st = PkvPlanStats()
     _check(load().paged_attn_decode_plan_stats(pool, p, len(a), ctypes.byref(st)))
     return {f: getattr(st, f) for f, _ in PkvPlanStats._fields_}
+
+
+def pkv_timing_enable(pool, enable=True):
+    _check(load().pkv_timing_enable(pool, 1 if enable else 0))
+
+
+def pkv_timing_read(pool, reset=True):
+    """(summed attention-kernel milliseconds, bracketed calls)."""
+    ms = ctypes.c_double()
+    n = _I64()
+    _check(load().pkv_timing_read(pool, ctypes.byref(ms), ctypes.byref(n), 1 if reset else 0))
+    return ms.value, n.value
 
 
 def pkv_last_error() -> str:

@@ -23,6 +23,7 @@ SOURCES = [
     "capi.hip",
     "kernels/append.hip",
     "kernels/attn_valu.hip",
+    "kernels/attn_mfma.hip",
     "kernels/merge.hip",
 ]
 

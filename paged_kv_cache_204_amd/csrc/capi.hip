@@ -6,6 +6,7 @@
 // buffers for plan uploads, and the kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -118,6 +119,12 @@ struct pkv_pool {
   PlanLayout dlayout;
   pkv::Plan vplan;
   PlanLayout vlayout;
+  // kernel timing: event pairs recorded around attention kernels
+  bool timing = false;
+  std::vector<hipEvent_t> ev_free;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pending;
+  double timed_ms = 0.0;
+  int64_t timed_calls = 0;
 };
 
 namespace {
@@ -164,9 +171,40 @@ pkv_status upload(pkv_pool* p, DevBuf& dst, size_t bytes, hipStream_t stream, Fi
   return PKV_OK;
 }
 
+pkv_status take_event(pkv_pool* p, hipEvent_t* ev) {
+  if (!p->ev_free.empty()) {
+    *ev = p->ev_free.back();
+    p->ev_free.pop_back();
+    return PKV_OK;
+  }
+  PKV_HIP(hipEventCreate(ev));
+  return PKV_OK;
+}
+
+pkv_status launch_kernels(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
+                          const DevBuf& buf, int32_t layer, const void* q, float sm_scale,
+                          float* out, float* lse, hipStream_t stream);
+
+// Attention kernels of one call, bracketed by timing events when enabled.
 pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
                        const DevBuf& buf, int32_t layer, const void* q, float sm_scale,
                        float* out, float* lse, hipStream_t stream) {
+  if (!p->timing) return launch_kernels(p, plan, lay, buf, layer, q, sm_scale, out, lse, stream);
+  hipEvent_t a, b;
+  pkv_status s = take_event(p, &a);
+  if (s != PKV_OK) return s;
+  s = take_event(p, &b);
+  if (s != PKV_OK) return s;
+  PKV_HIP(hipEventRecord(a, stream));
+  s = launch_kernels(p, plan, lay, buf, layer, q, sm_scale, out, lse, stream);
+  PKV_HIP(hipEventRecord(b, stream));
+  p->ev_pending.emplace_back(a, b);
+  return s;
+}
+
+pkv_status launch_kernels(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
+                          const DevBuf& buf, int32_t layer, const void* q, float sm_scale,
+                          float* out, float* lse, hipStream_t stream) {
   const pkv::Shape& sh = p->core.shape();
   const char* base = static_cast<const char*>(buf.ptr);
   pkv_status s = ensure(p->partials, static_cast<size_t>(plan.partial_rows) * (sh.head_dim + 1) * sizeof(float));
@@ -196,8 +234,11 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
     ap.items = reinterpret_cast<const pkv::WorkItem*>(base + lay.valu);
     PKV_HIP(pkv::launch_attn_valu(ap, static_cast<int32_t>(plan.valu.size()), sh.head_dim, stream));
   }
-  if (!plan.mfma.empty())
-    return fail(PKV_ERR_UNSUPPORTED, "attention: MFMA work items are not available");
+  if (!plan.mfma.empty()) {
+    ap.items = reinterpret_cast<const pkv::WorkItem*>(base + lay.mfma);
+    PKV_HIP(pkv::launch_attn_mfma(ap, static_cast<int32_t>(plan.mfma.size()), sh.head_dim,
+                                  plan.mfma_row_tiles, stream));
+  }
   if (!plan.merges.empty()) {
     pkv::MergeParams mp{};
     mp.merges = reinterpret_cast<const pkv::MergeRow*>(base + lay.merges);
@@ -214,6 +255,23 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+// Planner knobs may be overridden from the environment for tuning sweeps:
+// PKV_MFMA_MIN_ROWS (0 turns the MFMA kernel off), PKV_MFMA_ROW_TILES (1|2),
+// PKV_TARGET_WGS, PKV_TARGET_MFMA_WGS, PKV_MAX_CHUNK.
+void apply_env(pkv::PlanConfig* c) {
+  auto get = [](const char* name, int32_t* v, int32_t lo, int32_t hi) {
+    const char* e = std::getenv(name);
+    if (!e || !*e) return;
+    long x = std::strtol(e, nullptr, 10);
+    if (x >= lo && x <= hi) *v = static_cast<int32_t>(x);
+  };
+  get("PKV_MFMA_MIN_ROWS", &c->mfma_min_rows, 0, 1 << 20);
+  get("PKV_MFMA_ROW_TILES", &c->mfma_row_tiles, 1, 2);
+  get("PKV_TARGET_WGS", &c->target_wgs, 1, 1 << 20);
+  get("PKV_TARGET_MFMA_WGS", &c->target_mfma_wgs, 1, 1 << 20);
+  get("PKV_MAX_CHUNK", &c->max_chunk, 64, 1 << 20);
+}
 
 }  // namespace
 
@@ -257,6 +315,7 @@ pkv_status kv_pool_create(const pkv_desc* d, void* k_pool, void* v_pool,
   pkv_pool* p = new (std::nothrow) pkv_pool(s, free_order);
   if (!p) return fail(PKV_ERR_ARG, "kv_pool_create: out of host memory");
   p->device = device;
+  apply_env(&p->cfg);
   if (device) {
     hipError_t e = hipGetDevice(&p->dev);
     if (e != hipSuccess) {
@@ -280,6 +339,11 @@ void kv_pool_destroy(pkv_pool* p) {
     for (int i = 0; i < kStageSlots; ++i) {
       if (p->stage[i]) (void)hipHostFree(p->stage[i]);
       if (p->stage_ev[i]) (void)hipEventDestroy(p->stage_ev[i]);
+    }
+    for (hipEvent_t e : p->ev_free) (void)hipEventDestroy(e);
+    for (auto& pr : p->ev_pending) {
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
     }
   }
   delete p;
@@ -483,6 +547,44 @@ pkv_status paged_attn_decode_plan_stats(pkv_pool* p, const int64_t* seqs, int32_
   out->segments = plan.segments;
   out->work_items = static_cast<int32_t>(plan.valu.size() + plan.mfma.size());
   out->merged_rows = static_cast<int32_t>(plan.merges.size()) * p->core.shape().num_q_heads;
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_enable(pkv_pool* p, int32_t enable) {
+  if (!p) return fail(PKV_ERR_ARG, "pkv_timing_enable: NULL pool");
+  if (!p->device) return fail(PKV_ERR_ARG, "pkv_timing_enable: the pool has no device storage");
+  p->timing = enable != 0;
+  if (!p->timing) {
+    for (auto& pr : p->ev_pending) {
+      p->ev_free.push_back(pr.first);
+      p->ev_free.push_back(pr.second);
+    }
+    p->ev_pending.clear();
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_read(pkv_pool* p, double* total_ms, int64_t* calls, int32_t reset) {
+  if (!p || !total_ms || !calls) return fail(PKV_ERR_ARG, "pkv_timing_read: NULL argument");
+  if (!p->device) return fail(PKV_ERR_ARG, "pkv_timing_read: the pool has no device storage");
+  DeviceGuard g(p->dev);
+  PKV_HIP(g.err);
+  for (auto& pr : p->ev_pending) {
+    PKV_HIP(hipEventSynchronize(pr.second));
+    float ms = 0.f;
+    PKV_HIP(hipEventElapsedTime(&ms, pr.first, pr.second));
+    p->timed_ms += ms;
+    ++p->timed_calls;
+    p->ev_free.push_back(pr.first);
+    p->ev_free.push_back(pr.second);
+  }
+  p->ev_pending.clear();
+  *total_ms = p->timed_ms;
+  *calls = p->timed_calls;
+  if (reset) {
+    p->timed_ms = 0.0;
+    p->timed_calls = 0;
+  }
   return PKV_OK;
 }
 

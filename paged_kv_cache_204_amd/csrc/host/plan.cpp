@@ -16,14 +16,19 @@ struct Segment {
   int32_t ntok;
 };
 
-// Chunk length in tokens for a total amount of (token x item-row-tile) work.
-int32_t pick_chunk(int64_t work_tokens, int32_t kv_heads, int32_t block_size,
-                   const PlanConfig& cfg) {
-  const int32_t unit = std::max(cfg.tile, block_size);
-  int64_t per_wg = ceil_div(work_tokens * kv_heads, std::max(1, cfg.target_wgs));
+// Chunk length in tokens: spread `work_tokens` (token x row-subset units,
+// per kv head) over about `target` workgroups, in multiples of `unit`, within
+// [unit, cap].
+int32_t pick_chunk(int64_t work_tokens, int32_t kv_heads, int32_t unit, int32_t target,
+                   int64_t cap) {
+  int64_t per_wg = ceil_div(work_tokens * kv_heads, std::max(1, target));
   int64_t chunk = ceil_div(std::max<int64_t>(per_wg, 1), unit) * unit;
-  int64_t cap = std::max<int64_t>(unit, (cfg.max_chunk / unit) * unit);
+  cap = std::max<int64_t>(unit, (cap / unit) * unit);
   return static_cast<int32_t>(std::min(chunk, cap));
+}
+
+int64_t chunk_cap(const PlanConfig& cfg, int32_t block_size) {
+  return std::min<int64_t>(cfg.max_chunk, static_cast<int64_t>(cfg.max_chunk_blocks) * block_size);
 }
 
 // Partial-row bookkeeping shared by both planners: `owner[g]` is the query
@@ -155,26 +160,35 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   }
   plan->segments = static_cast<int32_t>(segs.size());
 
-  // ---- chunking ----
-  auto rows_per_item = [&](const Segment& s) {
-    int64_t rows = static_cast<int64_t>(s.queries.size()) * G;
-    bool mfma = cfg.mfma_min_rows > 0 && rows >= cfg.mfma_min_rows;
-    return mfma ? cfg.mfma_rows : cfg.valu_rows;
+  // ---- work items ----
+  // Segments read by many rows (a shared prefix under many queries) are a
+  // dense contraction and go to the MFMA kernel in row subsets of
+  // mfma_item_rows; the rest go to the VALU kernel in subsets of valu_rows.
+  // Each kind gets its own key-chunk length.
+  const int32_t mrows = mfma_item_rows(cfg.mfma_row_tiles);
+  plan->mfma_row_tiles = cfg.mfma_row_tiles;
+  auto is_mfma = [&](const Segment& s) {
+    return cfg.mfma_min_rows > 0 &&
+           static_cast<int64_t>(s.queries.size()) * G >= cfg.mfma_min_rows;
   };
-  int64_t work = 0;
+  const int32_t unit = std::max(cfg.tile, B);
+  const int64_t cap = chunk_cap(cfg, B);
+  int64_t work_v = 0, work_m = 0;
   for (const Segment& s : segs) {
     plan->unique_tokens += s.ntok;
     plan->unique_blocks += s.nblk;
-    int32_t per = std::max(1, rows_per_item(s) / G);
-    work += static_cast<int64_t>(s.ntok) * ceil_div(static_cast<int64_t>(s.queries.size()), per);
+    const bool m = is_mfma(s);
+    const int64_t per = std::max(1, (m ? mrows : cfg.valu_rows) / G);
+    (m ? work_m : work_v) += static_cast<int64_t>(s.ntok) * ceil_div(static_cast<int64_t>(s.queries.size()), per);
   }
-  const int32_t chunk = pick_chunk(work, sh.num_kv_heads, B, cfg);
+  const int32_t chunk_v = pick_chunk(work_v, sh.num_kv_heads, unit, cfg.target_wgs, cap);
+  const int32_t chunk_m = pick_chunk(work_m, sh.num_kv_heads, unit, cfg.target_mfma_wgs, cap);
 
   std::vector<int32_t> n_parts(n_seqs, 0);
   for (const Segment& s : segs) {
-    const bool mfma = cfg.mfma_min_rows > 0 &&
-                      static_cast<int64_t>(s.queries.size()) * G >= cfg.mfma_min_rows;
-    const int32_t per = std::max(1, (mfma ? cfg.mfma_rows : cfg.valu_rows) / G);
+    const bool mfma = is_mfma(s);
+    const int32_t chunk = mfma ? chunk_m : chunk_v;
+    const int32_t per = std::max(1, (mfma ? mrows : cfg.valu_rows) / G);
     const int32_t nchunk = static_cast<int32_t>(ceil_div(s.ntok, chunk));
     for (int32_t q : s.queries) n_parts[q] += nchunk;
     const int32_t blk_base = static_cast<int32_t>(plan->blocks.size());
@@ -235,7 +249,8 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   }
   const bool mfma = cfg.mfma_min_rows > 0 &&
                     static_cast<int64_t>(n_nodes) * G >= cfg.mfma_min_rows;
-  const int32_t per = std::max(1, (mfma ? cfg.mfma_rows : cfg.valu_rows) / G);
+  plan->mfma_row_tiles = cfg.mfma_row_tiles;
+  const int32_t per = std::max(1, (mfma ? mfma_item_rows(cfg.mfma_row_tiles) : cfg.valu_rows) / G);
   const int64_t subsets = ceil_div(n_nodes, per);
   int64_t work = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
@@ -244,7 +259,8 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     plan->unique_blocks += static_cast<int32_t>(st[i]->table.size());
   }
   plan->segments = n_seqs;
-  const int32_t chunk = pick_chunk(work, sh.num_kv_heads, B, cfg);
+  const int32_t chunk = pick_chunk(work, sh.num_kv_heads, std::max(cfg.tile, B),
+                                   mfma ? cfg.target_mfma_wgs : cfg.target_wgs, chunk_cap(cfg, B));
   std::vector<int32_t> n_parts(static_cast<size_t>(n_seqs) * n_nodes, 0);
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t len = st[i]->len;

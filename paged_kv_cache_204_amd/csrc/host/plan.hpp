@@ -24,13 +24,18 @@
 namespace pkv {
 
 struct PlanConfig {
-  int32_t valu_rows = 16;      // rows (groups x G) per VALU work item, <= 16
-  int32_t mfma_rows = 256;     // rows per MFMA work item
-  int32_t mfma_min_rows = 0;   // segments with at least this many rows use MFMA; 0 = never
-  int32_t target_wgs = 1024;   // workgroups to aim for over all kv heads
-  int32_t tile = 64;           // key tokens per kernel tile; chunks are multiples
-  int32_t max_chunk = 4096;    // key tokens per work item at most
+  int32_t valu_rows = 16;        // rows (groups x G) per VALU work item, <= 16
+  int32_t mfma_row_tiles = 1;    // 16-row tiles per wave of the MFMA kernel (1 or 2)
+  int32_t mfma_min_rows = 32;    // segments with at least this many rows use MFMA; 0 = never
+  int32_t target_wgs = 1024;     // VALU workgroups to aim for over all kv heads
+  int32_t target_mfma_wgs = 256; // MFMA workgroups to aim for over all kv heads
+  int32_t tile = 64;             // key tokens per kernel tile; chunks are multiples
+  int32_t max_chunk = 4096;      // key tokens per work item at most
+  int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)
 };
+
+// Rows of one MFMA work item for a row-tile setting (8 waves x 16 x tiles).
+inline int32_t mfma_item_rows(int32_t row_tiles) { return 8 * 16 * row_tiles; }
 
 struct Plan {
   std::vector<WorkItem> valu;   // items for the VALU kernel
@@ -40,6 +45,7 @@ struct Plan {
   std::vector<MergeRow> merges;
   std::vector<int32_t> parts;
   int64_t partial_rows = 0;
+  int32_t mfma_row_tiles = 1;   // row tiles per wave the MFMA items were cut for
   // what the call reads
   int64_t unique_tokens = 0;
   int64_t logical_tokens = 0;

@@ -51,6 +51,8 @@ struct MergeParams {
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_attn_valu(const AttnParams& p, int32_t n_items, int32_t head_dim, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnParams& p, int32_t n_items, int32_t head_dim,
+                            int32_t row_tiles, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int32_t n_rows, hipStream_t s);
 
 }  // namespace pkv

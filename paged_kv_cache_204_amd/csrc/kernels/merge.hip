@@ -3,8 +3,8 @@
 //   M = max_i lse_i,  w_i = 2^(lse_i - M),  out = sum_i w_i o_i / sum_i w_i,
 //   lse = (M + log2 sum_i w_i) * ln 2.
 // Partial states hold normalised o_i and a base-2 lse_i (-inf for a key set
-// the row could not see).  One workgroup per merged query vector; threads
-// walk (q head, dim) so the o_i reads are coalesced along head_dim.
+// the row could not see).  Grid: merged query vectors x chunks of 256
+// (q head, 4 dims) units; each thread reads its float4 of every partial.
 #include <math.h>
 
 #include "../kernels.hpp"
@@ -15,31 +15,43 @@ namespace {
 
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const MergeRow mr = p.merges[blockIdx.x];
-  const int total = p.Hq * p.D;
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    const int hq = e / p.D, d = e % p.D;
-    float mx = -INFINITY;
-    for (int k = 0; k < mr.n_parts; ++k)
-      mx = fmaxf(mx, p.part_lse[p.parts[mr.parts_off + k] + hq]);
-    float wsum = 0.f, acc = 0.f;
-    for (int k = 0; k < mr.n_parts; ++k) {
-      const size_t row = static_cast<size_t>(p.parts[mr.parts_off + k]) + hq;
-      const float l = p.part_lse[row];
-      const float w = (l == -INFINITY) ? 0.f : exp2f(l - mx);
-      wsum += w;
-      acc = fmaf(w, p.part_o[row * p.D + d], acc);
-    }
-    p.out[(static_cast<size_t>(mr.q_index) * p.Hq + hq) * p.D + d] = acc / wsum;
-    if (p.lse && d == 0)
-      p.lse[static_cast<size_t>(mr.q_index) * p.Hq + hq] = (mx + log2f(wsum)) * kLn2;
+  const int per_head = p.D / 4;
+  const int u = blockIdx.y * blockDim.x + threadIdx.x;
+  if (u >= p.Hq * per_head) return;
+  const int hq = u / per_head;
+  const int d = (u % per_head) * 4;
+  const int32_t* parts = p.parts + mr.parts_off;
+  float mx = -INFINITY;
+#pragma unroll 4
+  for (int k = 0; k < mr.n_parts; ++k) mx = fmaxf(mx, p.part_lse[parts[k] + hq]);
+  float wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int k = 0; k < mr.n_parts; ++k) {
+    const size_t row = static_cast<size_t>(parts[k]) + hq;
+    const float l = p.part_lse[row];
+    const float w = (l == -INFINITY) ? 0.f : exp2f(l - mx);
+    const float4 v = *reinterpret_cast<const float4*>(p.part_o + row * p.D + d);
+    wsum += w;
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
   }
+  const float inv = 1.f / wsum;
+  const size_t orow = static_cast<size_t>(mr.q_index) * p.Hq + hq;
+  *reinterpret_cast<float4*>(p.out + orow * p.D + d) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (p.lse && d == 0) p.lse[orow] = (mx + log2f(wsum)) * kLn2;
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, int32_t n_rows, hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<uint32_t>(n_rows)), dim3(256), 0, s, p);
+  const int units = p.Hq * (p.D / 4);
+  const dim3 grid(static_cast<uint32_t>(n_rows), static_cast<uint32_t>((units + 255) / 256));
+  hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
