@@ -200,8 +200,9 @@ pkv_status paged_attn_decode_plan_stats(pkv_pool* pool, const int64_t* seqs,
 /* ---- kernel timing (benchmarks) --------------------------------------- */
 
 /* When enabled, every paged_attn_decode / paged_attn_tree_verify call records
- * a pair of HIP events on its stream around its attention kernels (the plan
- * upload, when there is one, stays outside).  Disabling drops pending pairs. */
+ * a pair of HIP events on its stream around its attention kernel (the plan
+ * upload and the partial-state merge kernel stay outside).  Disabling drops
+ * pending pairs. */
 pkv_status pkv_timing_enable(pkv_pool* pool, int32_t enable);
 
 /* Synchronise the recorded events and return the summed kernel time in ms

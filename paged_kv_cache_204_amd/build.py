@@ -22,8 +22,7 @@ SOURCES = [
     "host/plan.cpp",
     "capi.hip",
     "kernels/append.hip",
-    "kernels/attn_valu.hip",
-    "kernels/attn_mfma.hip",
+    "kernels/attn.hip",
     "kernels/merge.hip",
 ]
 

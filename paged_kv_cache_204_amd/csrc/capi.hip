@@ -46,7 +46,7 @@ size_t align16(size_t x) { return (x + 15) & ~size_t{15}; }
 
 // Offsets of the plan arrays inside one contiguous upload.
 struct PlanLayout {
-  size_t valu = 0, mfma = 0, groups = 0, blocks = 0, merges = 0, parts = 0, total = 0;
+  size_t items = 0, groups = 0, blocks = 0, merges = 0, parts = 0, total = 0;
 };
 
 PlanLayout layout_of(const pkv::Plan& p) {
@@ -56,8 +56,7 @@ PlanLayout layout_of(const pkv::Plan& p) {
     field = at;
     at += align16(bytes);
   };
-  put(o.valu, p.valu.size() * sizeof(pkv::WorkItem));
-  put(o.mfma, p.mfma.size() * sizeof(pkv::WorkItem));
+  put(o.items, (p.mfma.size() + p.valu.size()) * sizeof(pkv::WorkItem));
   put(o.groups, p.groups.size() * sizeof(pkv::RowGroup));
   put(o.blocks, p.blocks.size() * sizeof(int32_t));
   put(o.merges, p.merges.size() * sizeof(pkv::MergeRow));
@@ -70,8 +69,9 @@ void serialize(const pkv::Plan& p, const PlanLayout& o, char* dst) {
   auto cp = [&](size_t off, const void* src, size_t bytes) {
     if (bytes) std::memcpy(dst + off, src, bytes);
   };
-  cp(o.valu, p.valu.data(), p.valu.size() * sizeof(pkv::WorkItem));
-  cp(o.mfma, p.mfma.data(), p.mfma.size() * sizeof(pkv::WorkItem));
+  // MFMA items first: the kernel picks its path by block index
+  cp(o.items, p.mfma.data(), p.mfma.size() * sizeof(pkv::WorkItem));
+  cp(o.items + p.mfma.size() * sizeof(pkv::WorkItem), p.valu.data(), p.valu.size() * sizeof(pkv::WorkItem));
   cp(o.groups, p.groups.data(), p.groups.size() * sizeof(pkv::RowGroup));
   cp(o.blocks, p.blocks.data(), p.blocks.size() * sizeof(int32_t));
   cp(o.merges, p.merges.data(), p.merges.size() * sizeof(pkv::MergeRow));
@@ -181,28 +181,10 @@ pkv_status take_event(pkv_pool* p, hipEvent_t* ev) {
   return PKV_OK;
 }
 
-pkv_status launch_kernels(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
-                          const DevBuf& buf, int32_t layer, const void* q, float sm_scale,
-                          float* out, float* lse, hipStream_t stream);
-
-// Attention kernels of one call, bracketed by timing events when enabled.
+// The attention kernel of one call and, when some queries have several
+// partial states, the merge kernel.  With timing enabled, a pair of events
+// brackets the attention kernel alone.
 pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
-                       const DevBuf& buf, int32_t layer, const void* q, float sm_scale,
-                       float* out, float* lse, hipStream_t stream) {
-  if (!p->timing) return launch_kernels(p, plan, lay, buf, layer, q, sm_scale, out, lse, stream);
-  hipEvent_t a, b;
-  pkv_status s = take_event(p, &a);
-  if (s != PKV_OK) return s;
-  s = take_event(p, &b);
-  if (s != PKV_OK) return s;
-  PKV_HIP(hipEventRecord(a, stream));
-  s = launch_kernels(p, plan, lay, buf, layer, q, sm_scale, out, lse, stream);
-  PKV_HIP(hipEventRecord(b, stream));
-  p->ev_pending.emplace_back(a, b);
-  return s;
-}
-
-pkv_status launch_kernels(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
                           const DevBuf& buf, int32_t layer, const void* q, float sm_scale,
                           float* out, float* lse, hipStream_t stream) {
   const pkv::Shape& sh = p->core.shape();
@@ -213,6 +195,7 @@ pkv_status launch_kernels(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& 
   float* part_lse = part_o + static_cast<size_t>(plan.partial_rows) * sh.head_dim;
 
   pkv::AttnParams ap{};
+  ap.items = reinterpret_cast<const pkv::WorkItem*>(base + lay.items);
   ap.groups = reinterpret_cast<const pkv::RowGroup*>(base + lay.groups);
   ap.blocks = reinterpret_cast<const int32_t*>(base + lay.blocks);
   ap.q = static_cast<const uint16_t*>(q);
@@ -222,6 +205,7 @@ pkv_status launch_kernels(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& 
   ap.lse = lse;
   ap.part_o = part_o;
   ap.part_lse = part_lse;
+  ap.n_mfma = static_cast<int32_t>(plan.mfma.size());
   ap.layer = layer;
   ap.N = sh.num_blocks;
   ap.Hq = sh.num_q_heads;
@@ -230,14 +214,18 @@ pkv_status launch_kernels(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& 
   ap.B = sh.block_size;
   ap.log2B = p->core.log2_block();
   ap.scale_log2 = sm_scale * pkv::kLog2eHost;
-  if (!plan.valu.empty()) {
-    ap.items = reinterpret_cast<const pkv::WorkItem*>(base + lay.valu);
-    PKV_HIP(pkv::launch_attn_valu(ap, static_cast<int32_t>(plan.valu.size()), sh.head_dim, stream));
+  const int32_t n_items = static_cast<int32_t>(plan.mfma.size() + plan.valu.size());
+  hipEvent_t ev_a = nullptr, ev_b = nullptr;
+  if (p->timing) {
+    s = take_event(p, &ev_a);
+    if (s == PKV_OK) s = take_event(p, &ev_b);
+    if (s != PKV_OK) return s;
+    PKV_HIP(hipEventRecord(ev_a, stream));
   }
-  if (!plan.mfma.empty()) {
-    ap.items = reinterpret_cast<const pkv::WorkItem*>(base + lay.mfma);
-    PKV_HIP(pkv::launch_attn_mfma(ap, static_cast<int32_t>(plan.mfma.size()), sh.head_dim,
-                                  plan.mfma_row_tiles, stream));
+  PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles, stream));
+  if (p->timing) {
+    PKV_HIP(hipEventRecord(ev_b, stream));
+    p->ev_pending.emplace_back(ev_a, ev_b);
   }
   if (!plan.merges.empty()) {
     pkv::MergeParams mp{};

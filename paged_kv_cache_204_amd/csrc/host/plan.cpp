@@ -53,8 +53,10 @@ void finish_parts(Plan* plan, const std::vector<int32_t>& n_parts, int32_t hq) {
   };
   assign(plan->valu);
   assign(plan->mfma);
+  std::vector<int32_t> merge_of(n_parts.size(), -1);
   for (size_t q = 0; q < parts_of.size(); ++q) {
     if (n_parts[q] <= 1) continue;
+    merge_of[q] = static_cast<int32_t>(plan->merges.size());
     MergeRow m;
     m.q_index = static_cast<int32_t>(q);
     m.parts_off = static_cast<int32_t>(plan->parts.size());
@@ -63,6 +65,7 @@ void finish_parts(Plan* plan, const std::vector<int32_t>& n_parts, int32_t hq) {
     plan->parts.insert(plan->parts.end(), parts_of[q].begin(), parts_of[q].end());
     plan->merges.push_back(m);
   }
+  for (RowGroup& g : plan->groups) g.merge = merge_of[g.q_index];
 }
 
 }  // namespace
@@ -168,11 +171,12 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   const int32_t mrows = mfma_item_rows(cfg.mfma_row_tiles);
   plan->mfma_row_tiles = cfg.mfma_row_tiles;
   auto is_mfma = [&](const Segment& s) {
-    return cfg.mfma_min_rows > 0 &&
-           static_cast<int64_t>(s.queries.size()) * G >= cfg.mfma_min_rows;
+    return G > cfg.valu_rows ||
+           (cfg.mfma_min_rows > 0 && static_cast<int64_t>(s.queries.size()) * G >= cfg.mfma_min_rows);
   };
   const int32_t unit = std::max(cfg.tile, B);
   const int64_t cap = chunk_cap(cfg, B);
+  const int64_t cap_v = std::min<int64_t>(cap, cfg.valu_max_tokens);
   int64_t work_v = 0, work_m = 0;
   for (const Segment& s : segs) {
     plan->unique_tokens += s.ntok;
@@ -181,7 +185,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     const int64_t per = std::max(1, (m ? mrows : cfg.valu_rows) / G);
     (m ? work_m : work_v) += static_cast<int64_t>(s.ntok) * ceil_div(static_cast<int64_t>(s.queries.size()), per);
   }
-  const int32_t chunk_v = pick_chunk(work_v, sh.num_kv_heads, unit, cfg.target_wgs, cap);
+  const int32_t chunk_v = pick_chunk(work_v, sh.num_kv_heads, unit, cfg.target_wgs, cap_v);
   const int32_t chunk_m = pick_chunk(work_m, sh.num_kv_heads, unit, cfg.target_mfma_wgs, cap);
 
   std::vector<int32_t> n_parts(n_seqs, 0);
@@ -197,7 +201,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
       const int32_t ng = static_cast<int32_t>(std::min<size_t>(per, s.queries.size() - u0));
       const int32_t grp_off = static_cast<int32_t>(plan->groups.size());
       for (int32_t u = 0; u < ng; ++u)
-        plan->groups.push_back(RowGroup{s.queries[u0 + u], -1, 0u, 0u});
+        plan->groups.push_back(RowGroup{s.queries[u0 + u], -1, 0u, 0u, -1, {0, 0, 0}});
       for (int32_t c = 0; c < nchunk; ++c) {
         WorkItem it;
         it.blk_off = blk_base + c * (chunk / B);
@@ -247,8 +251,8 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
       return Err::arg;
     }
   }
-  const bool mfma = cfg.mfma_min_rows > 0 &&
-                    static_cast<int64_t>(n_nodes) * G >= cfg.mfma_min_rows;
+  const bool mfma = G > cfg.valu_rows ||
+                    (cfg.mfma_min_rows > 0 && static_cast<int64_t>(n_nodes) * G >= cfg.mfma_min_rows);
   plan->mfma_row_tiles = cfg.mfma_row_tiles;
   const int32_t per = std::max(1, (mfma ? mfma_item_rows(cfg.mfma_row_tiles) : cfg.valu_rows) / G);
   const int64_t subsets = ceil_div(n_nodes, per);
@@ -259,8 +263,10 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     plan->unique_blocks += static_cast<int32_t>(st[i]->table.size());
   }
   plan->segments = n_seqs;
+  const int64_t cap = mfma ? chunk_cap(cfg, B)
+                           : std::min<int64_t>(chunk_cap(cfg, B), cfg.valu_max_tokens);
   const int32_t chunk = pick_chunk(work, sh.num_kv_heads, std::max(cfg.tile, B),
-                                   mfma ? cfg.target_mfma_wgs : cfg.target_wgs, chunk_cap(cfg, B));
+                                   mfma ? cfg.target_mfma_wgs : cfg.target_wgs, cap);
   std::vector<int32_t> n_parts(static_cast<size_t>(n_seqs) * n_nodes, 0);
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t len = st[i]->len;
@@ -279,7 +285,7 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
       for (int32_t j = j0; j < j0 + ng; ++j) {
         uint64_t m = anc[static_cast<size_t>(i) * n_nodes + j];
         plan->groups.push_back(RowGroup{i * n_nodes + j, j, static_cast<uint32_t>(m),
-                                        static_cast<uint32_t>(m >> 32)});
+                                        static_cast<uint32_t>(m >> 32), -1, {0, 0, 0}});
       }
       for (int32_t c = 0; c < nchunk; ++c) {
         const int32_t start = c * chunk;

@@ -24,9 +24,11 @@
 namespace pkv {
 
 struct PlanConfig {
-  int32_t valu_rows = 16;        // rows (groups x G) per VALU work item, <= 16
-  int32_t mfma_row_tiles = 1;    // 16-row tiles per wave of the MFMA kernel (1 or 2)
-  int32_t mfma_min_rows = 32;    // segments with at least this many rows use MFMA; 0 = never
+  int32_t valu_rows = 8;         // rows (groups x G) per VALU work item, <= 8
+  int32_t valu_max_tokens = 512; // key tokens per VALU work item at most
+  int32_t mfma_row_tiles = 2;    // 16-row tiles per wave of the MFMA path (1 or 2)
+  int32_t mfma_min_rows = 32;    // segments with at least this many rows use MFMA; 0 = only
+                                 // when a single query's GQA group exceeds valu_rows
   int32_t target_wgs = 1024;     // VALU workgroups to aim for over all kv heads
   int32_t target_mfma_wgs = 256; // MFMA workgroups to aim for over all kv heads
   int32_t tile = 64;             // key tokens per kernel tile; chunks are multiples
@@ -34,8 +36,8 @@ struct PlanConfig {
   int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)
 };
 
-// Rows of one MFMA work item for a row-tile setting (8 waves x 16 x tiles).
-inline int32_t mfma_item_rows(int32_t row_tiles) { return 8 * 16 * row_tiles; }
+// Rows of one MFMA work item for a row-tile setting (4 waves x 16 x tiles).
+inline int32_t mfma_item_rows(int32_t row_tiles) { return 4 * 16 * row_tiles; }
 
 struct Plan {
   std::vector<WorkItem> valu;   // items for the VALU kernel

@@ -23,7 +23,8 @@ struct AppendParams {
   int32_t L, N, Hkv, B, log2B, D;
 };
 
-// One attention launch over a list of work items (kv head = blockIdx.y).
+// One attention launch over a list of work items (kv head = blockIdx.y):
+// items [0, n_mfma) take the MFMA path, the rest the VALU path.
 struct AttnParams {
   const WorkItem* items;
   const RowGroup* groups;
@@ -35,10 +36,16 @@ struct AttnParams {
   float* lse;              // [n_q][Hq] natural log, or null
   float* part_o;           // [partial rows][D]
   float* part_lse;         // [partial rows], base-2 log
+  int32_t n_mfma;
   int32_t layer, N, Hq, Hkv, G, B, log2B;
   float scale_log2;        // sm_scale * log2(e)
 };
 
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t row_tiles,
+                       hipStream_t s);
+
+// Log-sum-exp merge of the partial states of several work items.
 struct MergeParams {
   const MergeRow* merges;
   const int32_t* parts;
@@ -48,11 +55,6 @@ struct MergeParams {
   float* lse;              // natural log, or null
   int32_t Hq, D;
 };
-
-hipError_t launch_append(const AppendParams& p, hipStream_t s);
-hipError_t launch_attn_valu(const AttnParams& p, int32_t n_items, int32_t head_dim, hipStream_t s);
-hipError_t launch_attn_mfma(const AttnParams& p, int32_t n_items, int32_t head_dim,
-                            int32_t row_tiles, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int32_t n_rows, hipStream_t s);
 
 }  // namespace pkv

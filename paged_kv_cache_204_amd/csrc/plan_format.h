@@ -14,7 +14,7 @@
 //   - output: part_base < 0 -> the item covers every key of its queries and
 //     writes final out / lse; otherwise it writes normalised partial states
 //     (o, lse) at partial rows part_base + u * Hq + hq (u = group index
-//     within the item) for the merge step.
+//     within the item) for the merge launch.
 #pragma once
 
 #include <stdint.h>
@@ -37,6 +37,8 @@ struct RowGroup {
   int32_t node;      // draft-tree node of this query, -1 for decode
   uint32_t anc_lo;   // ancestor-or-self mask of the node, bits 0..31
   uint32_t anc_hi;   // bits 32..63
+  int32_t merge;     // MergeRow of this query, -1 when it has a single partial state
+  int32_t pad[3];
 };
 
 // One query vector whose partial states are merged: partial rows
@@ -49,7 +51,7 @@ struct MergeRow {
 };
 
 static_assert(sizeof(WorkItem) == 32, "WorkItem layout");
-static_assert(sizeof(RowGroup) == 16, "RowGroup layout");
+static_assert(sizeof(RowGroup) == 32, "RowGroup layout");
 static_assert(sizeof(MergeRow) == 16, "MergeRow layout");
 
 }  // namespace pkv
