@@ -222,7 +222,8 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
     if (s != PKV_OK) return s;
     PKV_HIP(hipEventRecord(ev_a, stream));
   }
-  PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles, stream));
+  PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles,
+                            plan.valu_max_rows * ap.G, stream));
   if (p->timing) {
     PKV_HIP(hipEventRecord(ev_b, stream));
     p->ev_pending.emplace_back(ev_a, ev_b);

@@ -53,6 +53,7 @@ void finish_parts(Plan* plan, const std::vector<int32_t>& n_parts, int32_t hq) {
   };
   assign(plan->valu);
   assign(plan->mfma);
+  for (const WorkItem& it : plan->valu) plan->valu_max_rows = std::max(plan->valu_max_rows, it.n_grp);
   std::vector<int32_t> merge_of(n_parts.size(), -1);
   for (size_t q = 0; q < parts_of.size(); ++q) {
     if (n_parts[q] <= 1) continue;

@@ -48,6 +48,7 @@ struct Plan {
   std::vector<int32_t> parts;
   int64_t partial_rows = 0;
   int32_t mfma_row_tiles = 1;   // row tiles per wave the MFMA items were cut for
+  int32_t valu_max_rows = 0;    // most rows in any VALU item
   // what the call reads
   int64_t unique_tokens = 0;
   int64_t logical_tokens = 0;

@@ -42,8 +42,9 @@ struct AttnParams {
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+// valu_rows: the most rows any VALU item of the launch holds (<= 8).
 hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t row_tiles,
-                       hipStream_t s);
+                       int32_t valu_rows, hipStream_t s);
 
 // Log-sum-exp merge of the partial states of several work items.
 struct MergeParams {

@@ -262,13 +262,13 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
 }
 
 // ---------------------------------------------------------------- VALU path
-constexpr int kValuRows = 8;     // query rows per item
+constexpr int kValuRows = 8;     // query rows per item at most
 constexpr int kValuTok = 512;    // key tokens per item
 constexpr int kUnroll = 4;       // token passes with loads in flight per thread
 
 template <int D>
-struct ValuSmem {
-  float s[kValuRows][kValuTok + 1];   // scores, then probabilities; odd pitch
+struct alignas(16) ValuSmem {
+  float s[kValuTok][kValuRows];   // scores, then probabilities, token-major
   float red[kThreads / 64][kValuRows][D];
   float m[kValuRows], l[kValuRows];
 };
@@ -284,16 +284,20 @@ __device__ __forceinline__ float dot8(const uint4& q, const uint4& k, float acc)
 }
 
 // A token's head_dim row is read by D/8 lanes (128-bit loads, whole row
-// coalesced); phase 1 forms the scores of every row for the item's keys
-// (v_dot2_f32_bf16, a DPP butterfly over the row's lanes) into LDS, phase 2
-// takes an exact two-pass softmax per row (one wave per row), phase 3
-// accumulates p * v over each lane's tokens for its 8 dims and sums lanes and
-// waves holding the same dims.
-template <int D>
+// coalesced); K and V of the first passes are requested together.  Phase 1
+// forms the scores of every row for the item's keys (v_dot2_f32_bf16, a DPP
+// butterfly over the row's lanes) into LDS, token-major; phase 2 takes an
+// exact two-pass softmax per row (one wave per row); phase 3 accumulates
+// p * v over each lane's tokens for its 8 dims (the 8 rows' p of a token are
+// two 128-bit LDS reads) and sums lanes and waves holding the same dims.
+// RM (4 or 8) bounds the rows at compile time; rows >= R compute on zero
+// queries and are never written.
+template <int D, int RM>
 __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& it, int h,
                                           ValuSmem<D>& sm, const int32_t* blk_s) {
   constexpr int CPR = D / 8;
   constexpr int TPP = kThreads / CPR;
+  static_assert(RM <= CPR, "one score row per lane of a token group");
   const int G = p.G;
   const int R = it.n_grp * G;
   const int tid = threadIdx.x;
@@ -302,9 +306,27 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
   const int c = tid % CPR;
   const int tp = tid / CPR;
 
-  uint4 qv[kValuRows];
+  const size_t blk_stride = static_cast<size_t>(p.Hkv) * p.B * D;
+  const size_t base = static_cast<size_t>(p.layer) * p.N * blk_stride + static_cast<size_t>(h) * p.B * D;
+  const uint16_t* kb = p.k_pool + base;
+  const uint16_t* vb = p.v_pool + base;
+  const int t_last = it.n_tok - 1;
+  auto addr = [&](int t) {
+    t = min(t, t_last);
+    return static_cast<size_t>(blk_s[t >> p.log2B]) * blk_stride +
+           static_cast<size_t>(t & (p.B - 1)) * D + c * 8;
+  };
+  const int npass = (it.n_tok + TPP - 1) / TPP;
+
+  // first passes of K and V, then the queries
+  uint4 kv[kUnroll], vv[kUnroll];
 #pragma unroll
-  for (int r = 0; r < kValuRows; ++r) {
+  for (int u = 0; u < kUnroll; ++u) kv[u] = *reinterpret_cast<const uint4*>(kb + addr(u * TPP + tp));
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) vv[u] = *reinterpret_cast<const uint4*>(vb + addr(u * TPP + tp));
+  uint4 qv[RM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
     qv[r] = make_uint4(0, 0, 0, 0);
     if (r < R) {
       const RowGroup g = p.groups[it.grp_off + r / G];
@@ -318,53 +340,39 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
     anc_mine = (static_cast<uint64_t>(g.anc_hi) << 32) | g.anc_lo;
   }
 
-  const size_t blk_stride = static_cast<size_t>(p.Hkv) * p.B * D;
-  const size_t base = static_cast<size_t>(p.layer) * p.N * blk_stride + static_cast<size_t>(h) * p.B * D;
-  const uint16_t* kb = p.k_pool + base;
-  const uint16_t* vb = p.v_pool + base;
-  const int t_last = it.n_tok - 1;
-  auto addr = [&](int t) {
-    t = min(t, t_last);
-    return static_cast<size_t>(blk_s[t >> p.log2B]) * blk_stride +
-           static_cast<size_t>(t & (p.B - 1)) * D + c * 8;
-  };
-
-  const int npass = (it.n_tok + TPP - 1) / TPP;
+  // ---- phase 1: scores ---------------------------------------------------
   for (int p0 = 0; p0 < npass; p0 += kUnroll) {
-    uint4 kv[kUnroll];
+    if (p0 > 0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) kv[u] = *reinterpret_cast<const uint4*>(kb + addr((p0 + u) * TPP + tp));
+      for (int u = 0; u < kUnroll; ++u) kv[u] = *reinterpret_cast<const uint4*>(kb + addr((p0 + u) * TPP + tp));
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = (p0 + u) * TPP + tp;
       float mine = 0.f;
 #pragma unroll
-      for (int r = 0; r < kValuRows; ++r) {
-        if (r < R) {
-          const float sr = group_sum<CPR>(dot8(qv[r], kv[u], 0.f));
-          if (r == c) mine = sr;
-        }
+      for (int r = 0; r < RM; ++r) {
+        const float sr = group_sum<CPR>(dot8(qv[r], kv[u], 0.f));
+        mine = (r == c) ? sr : mine;
       }
       if (c < R && t < it.n_tok) {
         bool vis = true;
         if (t >= it.tail_start) vis = (anc_mine >> (it.tail_node0 + t - it.tail_start)) & 1ull;
-        sm.s[c][t] = vis ? mine * p.scale_log2 : -INFINITY;
+        sm.s[t][c] = vis ? mine * p.scale_log2 : -INFINITY;
       }
     }
   }
-  uint4 vv[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) vv[u] = *reinterpret_cast<const uint4*>(vb + addr(u * TPP + tp));
   lds_barrier();
+  // ---- phase 2: exact softmax per row -----------------------------------------
   for (int r = wave; r < R; r += kThreads / 64) {
     float mx = -INFINITY;
-    for (int t = lane; t < it.n_tok; t += 64) mx = fmaxf(mx, sm.s[r][t]);
+    for (int t = lane; t < it.n_tok; t += 64) mx = fmaxf(mx, sm.s[t][r]);
     mx = wave_max(mx);
     const float m_use = (mx == -INFINITY) ? 0.f : mx;
     float sum = 0.f;
     for (int t = lane; t < it.n_tok; t += 64) {
-      const float e = fast_exp2(sm.s[r][t] - m_use);
-      sm.s[r][t] = e;
+      const float e = fast_exp2(sm.s[t][r] - m_use);
+      sm.s[t][r] = e;
       sum += e;
     }
     sum = wave_sum(sum);
@@ -374,9 +382,10 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
     }
   }
   lds_barrier();
-  float o[kValuRows][8];
+  // ---- phase 3: O = P V --------------------------------------------------------
+  float o[RM][8];
 #pragma unroll
-  for (int r = 0; r < kValuRows; ++r)
+  for (int r = 0; r < RM; ++r)
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[r][j] = 0.f;
   for (int p0 = 0; p0 < npass; p0 += kUnroll) {
@@ -384,41 +393,48 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) vv[u] = *reinterpret_cast<const uint4*>(vb + addr((p0 + u) * TPP + tp));
     }
+    float pr[kUnroll][RM];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = (p0 + u) * TPP + tp;
-      const bool live = t < it.n_tok;
       const int tc = min(t, t_last);
+      const float4 a = *reinterpret_cast<const float4*>(&sm.s[tc][0]);
+      pr[u][0] = a.x; pr[u][1] = a.y; pr[u][2] = a.z; pr[u][3] = a.w;
+      if constexpr (RM == 8) {
+        const float4 b = *reinterpret_cast<const float4*>(&sm.s[tc][4]);
+        pr[u][4] = b.x; pr[u][5] = b.y; pr[u][6] = b.z; pr[u][7] = b.w;
+      }
+      if (t > t_last) {
+#pragma unroll
+        for (int r = 0; r < RM; ++r) pr[u][r] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
       const float v[8] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y), bf16_hi(vv[u].y),
                           bf16_lo(vv[u].z), bf16_hi(vv[u].z), bf16_lo(vv[u].w), bf16_hi(vv[u].w)};
 #pragma unroll
-      for (int r = 0; r < kValuRows; ++r) {
-        if (r < R) {
-          const float pr = live ? sm.s[r][tc] : 0.f;
+      for (int r = 0; r < RM; ++r)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) o[r][j] = fmaf(pr, v[j], o[r][j]);
-        }
-      }
+        for (int j = 0; j < 8; ++j) o[r][j] = fmaf(pr[u][r], v[j], o[r][j]);
     }
   }
+  // lanes of a wave that hold the same dims (token slots tp) sum up ...
 #pragma unroll
-  for (int r = 0; r < kValuRows; ++r) {
-    if (r < R) {
+  for (int r = 0; r < RM; ++r) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float x = o[r][j];
-        if constexpr (CPR == 8) x += dpp_f32<kDppXor8>(x);
-        o[r][j] = xor32_sum(xor16_sum(x));
-      }
+    for (int j = 0; j < 8; ++j) {
+      float x = o[r][j];
+      if constexpr (CPR == 8) x += dpp_f32<kDppXor8>(x);
+      o[r][j] = xor32_sum(xor16_sum(x));
     }
   }
+  // ... then the waves
   if (lane < CPR) {
 #pragma unroll
-    for (int r = 0; r < kValuRows; ++r) {
-      if (r < R) {
-        *reinterpret_cast<float4*>(&sm.red[wave][r][c * 8]) = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
-        *reinterpret_cast<float4*>(&sm.red[wave][r][c * 8 + 4]) = make_float4(o[r][4], o[r][5], o[r][6], o[r][7]);
-      }
+    for (int r = 0; r < RM; ++r) {
+      *reinterpret_cast<float4*>(&sm.red[wave][r][c * 8]) = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
+      *reinterpret_cast<float4*>(&sm.red[wave][r][c * 8 + 4]) = make_float4(o[r][4], o[r][5], o[r][6], o[r][7]);
     }
   }
   lds_barrier();
@@ -453,9 +469,9 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
   }
 }
 
-template <int D, int RT>
+template <int D, int RT, int RM>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
-  __shared__ union {
+  __shared__ union alignas(16) {
     MfmaSmem<D> m;
     ValuSmem<D> v;
   } sm;
@@ -469,27 +485,29 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   if (static_cast<int>(blockIdx.x) < p.n_mfma)
     mfma_item<D, RT>(p, it, h, sm.m, blk_s);
   else
-    valu_item<D>(p, it, h, sm.v, blk_s);
+    valu_item<D, RM>(p, it, h, sm.v, blk_s);
 }
 
 }  // namespace
 
+template <int D, int RT>
+hipError_t launch_rows(const AttnParams& p, dim3 grid, int32_t valu_rows, hipStream_t s) {
+  if (valu_rows <= 4)
+    hipLaunchKernelGGL((attn_kernel<D, RT, 4>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, RT, 8>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t row_tiles,
-                       hipStream_t s) {
+                       int32_t valu_rows, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(n_items), static_cast<uint32_t>(p.Hkv));
-  const dim3 block(kThreads);
-  if (head_dim == 64 && row_tiles == 1)
-    hipLaunchKernelGGL((attn_kernel<64, 1>), grid, block, 0, s, p);
-  else if (head_dim == 64 && row_tiles == 2)
-    hipLaunchKernelGGL((attn_kernel<64, 2>), grid, block, 0, s, p);
-  else if (head_dim == 128 && row_tiles == 1)
-    hipLaunchKernelGGL((attn_kernel<128, 1>), grid, block, 0, s, p);
-  else if (head_dim == 128 && row_tiles == 2)
-    hipLaunchKernelGGL((attn_kernel<128, 2>), grid, block, 0, s, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (head_dim == 64 && row_tiles == 1) return launch_rows<64, 1>(p, grid, valu_rows, s);
+  if (head_dim == 64 && row_tiles == 2) return launch_rows<64, 2>(p, grid, valu_rows, s);
+  if (head_dim == 128 && row_tiles == 1) return launch_rows<128, 1>(p, grid, valu_rows, s);
+  if (head_dim == 128 && row_tiles == 2) return launch_rows<128, 2>(p, grid, valu_rows, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv
