@@ -42,6 +42,9 @@ def _flags():
         "-Wall", "-Wno-unused-result",
         # packed fp32 VALU ops stay off in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: the online-softmax rescale works on them
+        # with VALU ops, so AGPR copies would cost a move per element per step
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
     ]
 
