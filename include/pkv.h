@@ -79,6 +79,8 @@ size_t kv_pool_bytes(const pkv_desc* desc);
  * Passing NULL for both makes a host-only pool: the same allocator and block
  * tables with no device storage, for planning and tests (kv_append then takes
  * NULL K/V and attention calls return PKV_ERR_ARG).
+ * Device pools also need one layer of one array (num_blocks * num_kv_heads *
+ * block_size * head_dim * 2 bytes) under 64 GiB; else PKV_ERR_UNSUPPORTED.
  * free_order: NULL for the initial free list 0..num_blocks-1, else a host
  * array holding a permutation of 0..num_blocks-1 (head first).
  * Blocks are taken from the head of the free list; a block whose refcount

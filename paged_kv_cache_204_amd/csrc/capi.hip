@@ -291,6 +291,10 @@ pkv_status kv_pool_create(const pkv_desc* d, void* k_pool, void* v_pool,
       return fail(PKV_ERR_UNSUPPORTED, "kv_pool_create: more than 16 query heads per kv head");
     if (!aligned16(k_pool) || !aligned16(v_pool))
       return fail(PKV_ERR_ARG, "kv_pool_create: pools must be 16-byte aligned");
+    // the kernels address one layer of a pool in 32-bit units of 16 bytes
+    const int64_t layer_chunks = static_cast<int64_t>(s.num_blocks) * s.num_kv_heads * s.block_size * s.head_dim / 8;
+    if (layer_chunks >= (int64_t{1} << 32) || static_cast<int64_t>(s.num_kv_heads) * s.block_size * s.head_dim / 8 >= (1 << 24))
+      return fail(PKV_ERR_UNSUPPORTED, "kv_pool_create: one layer of a device pool must stay under 64 GiB");
   }
   if (free_order) {
     std::vector<char> seen(s.num_blocks, 0);

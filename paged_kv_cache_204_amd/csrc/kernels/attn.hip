@@ -35,9 +35,25 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kThreads = 256;
 constexpr int kMaxBlk = 512;       // block ids of one item staged in LDS
 
+// K or V of layer p.layer, kv head h, as 16-byte chunks: token slot `off` of
+// block `blk` starts at chunk blk * (Hkv * B * D / 8) + off * D / 8.  The pool
+// creation keeps a layer under 2^32 chunks and a block under 2^24 chunks, so
+// the index is one 24-bit multiply-add in 32 bits.
+__device__ __forceinline__ const uint4* layer_head_base(const AttnParams& p, const uint16_t* pool,
+                                                        int h, int D) {
+  const size_t blk_stride = static_cast<size_t>(p.Hkv) * p.B * D;
+  return reinterpret_cast<const uint4*>(pool + static_cast<size_t>(p.layer) * p.N * blk_stride +
+                                        static_cast<size_t>(h) * p.B * D);
+}
+
+__device__ __forceinline__ uint32_t chunk_index(int32_t blk, uint32_t blk_chunks, int32_t within) {
+  return __umul24(static_cast<uint32_t>(blk), blk_chunks) + static_cast<uint32_t>(within);
+}
+
 // ---------------------------------------------------------------- MFMA path
 constexpr int kStep = 32;          // key tokens per step (two 16-token tiles)
 constexpr int kDepth = 2;          // steps of K/V requested ahead
+constexpr float kSlack = 8.f;      // log2 headroom of P above the reference max
 
 template <int D>
 struct MfmaSmem {
@@ -50,9 +66,8 @@ struct MfmaSmem {
 // so the softmax max / sum need two cross-row swaps only, and the rounded P
 // (bf16) of the lane's 8 tokens is exactly the B operand of O^T += V^T P^T.
 // O^T keeps each lane on the same row, so the online rescale is lane local.
-// The running max stays exact: a row's largest P is exactly 1.0 and only the
-// smaller terms see bf16 rounding; the O rescale is skipped whenever no row
-// of the wave found a new max.
+// The O rescale runs only when some row of the wave outgrows its reference
+// max by more than kSlack (see the softmax step below).
 template <int D, int RT>
 __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& it, int h,
                                           MfmaSmem<D>& sm, const int32_t* blk_s) {
@@ -113,15 +128,13 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
   const bool v_on = tid < VUNITS;
   const int v_pair = tid & 15;
   const int v_c = (tid >> 4) % CPR;
-  const size_t blk_stride = static_cast<size_t>(p.Hkv) * p.B * D;
-  const size_t base = static_cast<size_t>(p.layer) * p.N * blk_stride + static_cast<size_t>(h) * p.B * D;
-  const uint16_t* kb = p.k_pool + base;
-  const uint16_t* vb = p.v_pool + base;
+  const uint4* kb = layer_head_base(p, p.k_pool, h, D);
+  const uint4* vb = layer_head_base(p, p.v_pool, h, D);
+  const uint32_t blk_chunks = static_cast<uint32_t>(p.Hkv * p.B * D / 8);
   const int t_last = it.n_tok - 1;
-  auto ldg = [&](const uint16_t* src, int t, int c) {
+  auto ldg = [&](const uint4* src, int t, int c) {
     t = min(t, t_last);
-    return *reinterpret_cast<const uint4*>(src + static_cast<size_t>(blk_s[t >> p.log2B]) * blk_stride +
-                                           static_cast<size_t>(t & (p.B - 1)) * D + c * 8);
+    return src[chunk_index(blk_s[t >> p.log2B], blk_chunks, (t & (p.B - 1)) * (D / 8) + c)];
   };
   uint4 rk[kDepth][KPER], rv[kDepth][2];
   auto fetch = [&](int slot, int t0) {
@@ -147,8 +160,11 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
       const uint32_t b[4] = {rv[slot][1].x, rv[slot][1].y, rv[slot][1].z, rv[slot][1].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][v_c * 8 + 2 * j][2 * v_pair]) = (a[j] & 0xFFFFu) | (b[j] << 16);
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][v_c * 8 + 2 * j + 1][2 * v_pair]) = (a[j] >> 16) | (b[j] & 0xFFFF0000u);
+        // (low halves of a and b), (high halves of a and b)
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][v_c * 8 + 2 * j][2 * v_pair]) =
+            __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][v_c * 8 + 2 * j + 1][2 * v_pair]) =
+            __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
       }
     }
     lds_barrier();
@@ -173,14 +189,14 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
       }
     }
     const bool full = t0 + kStep <= it.n_tok && t0 + kStep <= it.tail_start;
-    bf16x8 pf[RT];
+    bf16x8 pf[RT], pf_lo[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float sv[8];
+      float sv[8];   // raw scores; the scale is applied inside the exponent
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[4 * tt + i] = sacc[rt][tt][i] * p.scale_log2;
+        for (int i = 0; i < 4; ++i) sv[4 * tt + i] = sacc[rt][tt][i];
       if (!full) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -194,11 +210,17 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
       float mx = sv[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-      mx = xor32_max(xor16_max(mx));
+      mx = xor32_max(xor16_max(mx)) * p.scale_log2;
+      // The reference max m moves only when a row's max passes it by more
+      // than kSlack (then the whole wave rescales, every row to its exact
+      // max), so P <= 2^kSlack and the O rescale is rare after the first
+      // steps.  P enters the PV product as two bf16 terms, hi = bf16(P) and
+      // lo = bf16(P - hi), which carry it to about 2^-17 relative: a single
+      // bf16 P would leave up to 2^-9 relative error on each weight, which
+      // on rows of a few keys reaches 4e-3 in the output.
       const float m_old = m_run[rt];
-      const bool grow = mx > m_old;
-      if (__ballot(grow)) {
-        const float m_new = grow ? mx : m_old;
+      if (__ballot(mx > m_old + kSlack)) {
+        const float m_new = fmaxf(mx, m_old);
         const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
         l_run[rt] *= alpha;
 #pragma unroll
@@ -207,17 +229,21 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
       }
       const float m_use = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];
       float ps = 0.f;
-      uint32_t pk[4];
+      uint32_t ph[4], pl[4];
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const float p0 = fast_exp2(sv[j] - m_use);
-        const float p1 = fast_exp2(sv[j + 1] - m_use);
+        const float p0 = fast_exp2(fmaf(sv[j], p.scale_log2, -m_use));
+        const float p1 = fast_exp2(fmaf(sv[j + 1], p.scale_log2, -m_use));
         ps += p0 + p1;
-        pk[j >> 1] = pack_bf16x2(p0, p1);
+        const uint32_t h = pack_bf16x2(p0, p1);
+        ph[j >> 1] = h;
+        pl[j >> 1] = pack_bf16x2(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xFFFF0000u));
       }
       l_run[rt] += ps;
-      uint4 pv = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      pf[rt] = *reinterpret_cast<bf16x8*>(&pv);
+      uint4 hv = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+      uint4 lv = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+      pf[rt] = *reinterpret_cast<bf16x8*>(&hv);
+      pf_lo[rt] = *reinterpret_cast<bf16x8*>(&lv);
     }
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
@@ -226,18 +252,26 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
       uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
       const bf16x8 a = *reinterpret_cast<bf16x8*>(&av);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt) {
         o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[rt][dt], 0, 0, 0);
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf_lo[rt], o[rt][dt], 0, 0, 0);
+      }
     }
   };
 
 #pragma unroll
   for (int j = 0; j < kDepth; ++j) fetch(j, j * kStep);
-  for (int s0 = 0; s0 < nsteps; s0 += kDepth) {
+  // whole rounds of the ring in the loop, the last partial round peeled, so
+  // the loop body has no load behind a branch and the waits before each
+  // staging store can count the loads still in flight
+  int s0 = 0;
+  for (; s0 + kDepth <= nsteps; s0 += kDepth) {
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j)
-      if (s0 + j < nsteps) step(j, s0 + j);
+    for (int j = 0; j < kDepth; ++j) step(j, s0 + j);
   }
+#pragma unroll
+  for (int j = 0; j < kDepth - 1; ++j)
+    if (s0 + j < nsteps) step(j, s0 + j);
 
   if (!active) return;
 #pragma unroll
@@ -306,24 +340,22 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
   const int c = tid % CPR;
   const int tp = tid / CPR;
 
-  const size_t blk_stride = static_cast<size_t>(p.Hkv) * p.B * D;
-  const size_t base = static_cast<size_t>(p.layer) * p.N * blk_stride + static_cast<size_t>(h) * p.B * D;
-  const uint16_t* kb = p.k_pool + base;
-  const uint16_t* vb = p.v_pool + base;
+  const uint4* kb = layer_head_base(p, p.k_pool, h, D);
+  const uint4* vb = layer_head_base(p, p.v_pool, h, D);
+  const uint32_t blk_chunks = static_cast<uint32_t>(p.Hkv * p.B * D / 8);
   const int t_last = it.n_tok - 1;
   auto addr = [&](int t) {
     t = min(t, t_last);
-    return static_cast<size_t>(blk_s[t >> p.log2B]) * blk_stride +
-           static_cast<size_t>(t & (p.B - 1)) * D + c * 8;
+    return chunk_index(blk_s[t >> p.log2B], blk_chunks, (t & (p.B - 1)) * (D / 8) + c);
   };
   const int npass = (it.n_tok + TPP - 1) / TPP;
 
   // first passes of K and V, then the queries
   uint4 kv[kUnroll], vv[kUnroll];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) kv[u] = *reinterpret_cast<const uint4*>(kb + addr(u * TPP + tp));
+  for (int u = 0; u < kUnroll; ++u) kv[u] = kb[addr(u * TPP + tp)];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) vv[u] = *reinterpret_cast<const uint4*>(vb + addr(u * TPP + tp));
+  for (int u = 0; u < kUnroll; ++u) vv[u] = vb[addr(u * TPP + tp)];
   uint4 qv[RM];
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
@@ -344,7 +376,7 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
   for (int p0 = 0; p0 < npass; p0 += kUnroll) {
     if (p0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) kv[u] = *reinterpret_cast<const uint4*>(kb + addr((p0 + u) * TPP + tp));
+      for (int u = 0; u < kUnroll; ++u) kv[u] = kb[addr((p0 + u) * TPP + tp)];
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -391,7 +423,7 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
   for (int p0 = 0; p0 < npass; p0 += kUnroll) {
     if (p0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) vv[u] = *reinterpret_cast<const uint4*>(vb + addr((p0 + u) * TPP + tp));
+      for (int u = 0; u < kUnroll; ++u) vv[u] = vb[addr((p0 + u) * TPP + tp)];
     }
     float pr[kUnroll][RM];
 #pragma unroll

@@ -57,6 +57,7 @@ class Agg:
     def done(self, label):
         assert self.n > 0
         mean = self.sum / self.n
+        print(f"[parity] {label}: max |d| {self.max:.3e} mean |d| {mean:.3e}", flush=True)
         assert mean <= TOL_MEAN, f"{label}: mean |d| {mean:.3e}"
         return mean
 
