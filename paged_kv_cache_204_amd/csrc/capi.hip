@@ -58,7 +58,7 @@ PlanLayout layout_of(const pkv::Plan& p) {
   };
   put(o.items, (p.mfma.size() + p.valu.size()) * sizeof(pkv::WorkItem));
   put(o.groups, p.groups.size() * sizeof(pkv::RowGroup));
-  put(o.blocks, p.blocks.size() * sizeof(int32_t));
+  put(o.blocks, p.item_blocks.size() * sizeof(int32_t));
   put(o.merges, p.merges.size() * sizeof(pkv::MergeRow));
   put(o.parts, p.parts.size() * sizeof(int32_t));
   o.total = at;
@@ -73,7 +73,7 @@ void serialize(const pkv::Plan& p, const PlanLayout& o, char* dst) {
   cp(o.items, p.mfma.data(), p.mfma.size() * sizeof(pkv::WorkItem));
   cp(o.items + p.mfma.size() * sizeof(pkv::WorkItem), p.valu.data(), p.valu.size() * sizeof(pkv::WorkItem));
   cp(o.groups, p.groups.data(), p.groups.size() * sizeof(pkv::RowGroup));
-  cp(o.blocks, p.blocks.data(), p.blocks.size() * sizeof(int32_t));
+  cp(o.blocks, p.item_blocks.data(), p.item_blocks.size() * sizeof(int32_t));
   cp(o.merges, p.merges.data(), p.merges.size() * sizeof(pkv::MergeRow));
   cp(o.parts, p.parts.data(), p.parts.size() * sizeof(int32_t));
 }
@@ -194,6 +194,8 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
   float* part_o = static_cast<float*>(p->partials.ptr);
   float* part_lse = part_o + static_cast<size_t>(plan.partial_rows) * sh.head_dim;
 
+  if (plan.stride_mfma > pkv::kMaxItemBlocks || plan.stride_valu > pkv::kMaxItemBlocks)
+    return fail(PKV_ERR_ARG, "attention: a work item spans more blocks than the kernels stage");
   pkv::AttnParams ap{};
   ap.items = reinterpret_cast<const pkv::WorkItem*>(base + lay.items);
   ap.groups = reinterpret_cast<const pkv::RowGroup*>(base + lay.groups);
@@ -206,6 +208,8 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
   ap.part_o = part_o;
   ap.part_lse = part_lse;
   ap.n_mfma = static_cast<int32_t>(plan.mfma.size());
+  ap.stride_mfma = plan.stride_mfma;
+  ap.stride_valu = plan.stride_valu;
   ap.layer = layer;
   ap.N = sh.num_blocks;
   ap.Hq = sh.num_q_heads;
@@ -256,7 +260,7 @@ void apply_env(pkv::PlanConfig* c) {
     if (x >= lo && x <= hi) *v = static_cast<int32_t>(x);
   };
   get("PKV_MFMA_MIN_ROWS", &c->mfma_min_rows, 0, 1 << 20);
-  get("PKV_MFMA_ROW_TILES", &c->mfma_row_tiles, 1, 2);
+  get("PKV_MFMA_ROW_TILES", &c->mfma_row_tiles, 0, 2);
   get("PKV_TARGET_WGS", &c->target_wgs, 1, 1 << 20);
   get("PKV_TARGET_MFMA_WGS", &c->target_mfma_wgs, 1, 1 << 20);
   get("PKV_MAX_CHUNK", &c->max_chunk, 64, 1 << 20);

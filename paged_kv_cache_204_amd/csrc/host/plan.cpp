@@ -58,15 +58,37 @@ void finish_parts(Plan* plan, const std::vector<int32_t>& n_parts, int32_t hq) {
   for (size_t q = 0; q < parts_of.size(); ++q) {
     if (n_parts[q] <= 1) continue;
     merge_of[q] = static_cast<int32_t>(plan->merges.size());
-    MergeRow m;
+    MergeRow m{};
     m.q_index = static_cast<int32_t>(q);
-    m.parts_off = static_cast<int32_t>(plan->parts.size());
     m.n_parts = static_cast<int32_t>(parts_of[q].size());
-    m.pad = 0;
-    plan->parts.insert(plan->parts.end(), parts_of[q].begin(), parts_of[q].end());
+    m.parts_off = static_cast<int32_t>(plan->parts.size());
+    if (m.n_parts <= kMergeInline)
+      std::copy(parts_of[q].begin(), parts_of[q].end(), m.inl);
+    else
+      plan->parts.insert(plan->parts.end(), parts_of[q].begin(), parts_of[q].end());
     plan->merges.push_back(m);
   }
   for (RowGroup& g : plan->groups) g.merge = merge_of[g.q_index];
+}
+
+// Copies every item's block list to a fixed-stride slot (MFMA items first,
+// as the kernel numbers them), padding with the item's last block.
+void pack_item_blocks(Plan* plan, int32_t block_size) {
+  auto nblk = [&](const WorkItem& it) { return (it.n_tok + block_size - 1) / block_size; };
+  plan->stride_mfma = plan->stride_valu = 0;
+  for (const WorkItem& it : plan->mfma) plan->stride_mfma = std::max(plan->stride_mfma, nblk(it));
+  for (const WorkItem& it : plan->valu) plan->stride_valu = std::max(plan->stride_valu, nblk(it));
+  plan->item_blocks.assign(plan->mfma.size() * plan->stride_mfma + plan->valu.size() * plan->stride_valu, 0);
+  int32_t* dst = plan->item_blocks.data();
+  auto put = [&](const std::vector<WorkItem>& items, int32_t stride) {
+    for (const WorkItem& it : items) {
+      const int32_t n = nblk(it);
+      for (int32_t b = 0; b < stride; ++b) dst[b] = plan->blocks[it.blk_off + std::min(b, n - 1)];
+      dst += stride;
+    }
+  };
+  put(plan->mfma, plan->stride_mfma);
+  put(plan->valu, plan->stride_valu);
 }
 
 }  // namespace
@@ -169,12 +191,14 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   // dense contraction and go to the MFMA kernel in row subsets of
   // mfma_item_rows; the rest go to the VALU kernel in subsets of valu_rows.
   // Each kind gets its own key-chunk length.
-  const int32_t mrows = mfma_item_rows(cfg.mfma_row_tiles);
-  plan->mfma_row_tiles = cfg.mfma_row_tiles;
   auto is_mfma = [&](const Segment& s) {
     return G > cfg.valu_rows ||
            (cfg.mfma_min_rows > 0 && static_cast<int64_t>(s.queries.size()) * G >= cfg.mfma_min_rows);
   };
+  bool any_valu = false;
+  for (const Segment& s : segs) any_valu = any_valu || !is_mfma(s);
+  plan->mfma_row_tiles = cfg.mfma_row_tiles > 0 ? cfg.mfma_row_tiles : (any_valu ? 1 : 2);
+  const int32_t mrows = mfma_item_rows(plan->mfma_row_tiles);
   const int32_t unit = std::max(cfg.tile, B);
   const int64_t cap = chunk_cap(cfg, B);
   const int64_t cap_v = std::min<int64_t>(cap, cfg.valu_max_tokens);
@@ -218,6 +242,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     }
   }
   finish_parts(plan, n_parts, sh.num_q_heads);
+  pack_item_blocks(plan, B);
   return Err::ok;
 }
 
@@ -254,8 +279,8 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   }
   const bool mfma = G > cfg.valu_rows ||
                     (cfg.mfma_min_rows > 0 && static_cast<int64_t>(n_nodes) * G >= cfg.mfma_min_rows);
-  plan->mfma_row_tiles = cfg.mfma_row_tiles;
-  const int32_t per = std::max(1, (mfma ? mfma_item_rows(cfg.mfma_row_tiles) : cfg.valu_rows) / G);
+  plan->mfma_row_tiles = cfg.mfma_row_tiles > 0 ? cfg.mfma_row_tiles : 2;
+  const int32_t per = std::max(1, (mfma ? mfma_item_rows(plan->mfma_row_tiles) : cfg.valu_rows) / G);
   const int64_t subsets = ceil_div(n_nodes, per);
   int64_t work = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
@@ -312,6 +337,7 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     }
   }
   finish_parts(plan, n_parts, sh.num_q_heads);
+  pack_item_blocks(plan, B);
   return Err::ok;
 }
 

@@ -26,11 +26,13 @@ namespace pkv {
 struct PlanConfig {
   int32_t valu_rows = 8;         // rows (groups x G) per VALU work item, <= 8
   int32_t valu_max_tokens = 512; // key tokens per VALU work item at most
-  int32_t mfma_row_tiles = 2;    // 16-row tiles per wave of the MFMA path (1 or 2)
+  int32_t mfma_row_tiles = 0;    // 16-row tiles per wave of the MFMA path (1 or 2); 0 picks
+                                 // 2 for calls with MFMA items only and 1 otherwise (the
+                                 // two-tile kernel's registers lower the VALU items' occupancy)
   int32_t mfma_min_rows = 32;    // segments with at least this many rows use MFMA; 0 = only
                                  // when a single query's GQA group exceeds valu_rows
-  int32_t target_wgs = 1024;     // VALU workgroups to aim for over all kv heads
-  int32_t target_mfma_wgs = 256; // MFMA workgroups to aim for over all kv heads
+  int32_t target_wgs = 256;      // VALU workgroups to aim for over all kv heads
+  int32_t target_mfma_wgs = 512; // MFMA workgroups to aim for over all kv heads
   int32_t tile = 64;             // key tokens per kernel tile; chunks are multiples
   int32_t max_chunk = 4096;      // key tokens per work item at most
   int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)
@@ -46,6 +48,8 @@ struct Plan {
   std::vector<int32_t> blocks;
   std::vector<MergeRow> merges;
   std::vector<int32_t> parts;
+  std::vector<int32_t> item_blocks;   // per-item block lists, fixed strides
+  int32_t stride_mfma = 0, stride_valu = 0;
   int64_t partial_rows = 0;
   int32_t mfma_row_tiles = 1;   // row tiles per wave the MFMA items were cut for
   int32_t valu_max_rows = 0;    // most rows in any VALU item

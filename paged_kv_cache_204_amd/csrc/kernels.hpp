@@ -25,10 +25,12 @@ struct AppendParams {
 
 // One attention launch over a list of work items (kv head = blockIdx.y):
 // items [0, n_mfma) take the MFMA path, the rest the VALU path.
+constexpr int kMaxItemBlocks = 512;   // block ids of one work item (LDS staging)
+
 struct AttnParams {
   const WorkItem* items;
   const RowGroup* groups;
-  const int32_t* blocks;
+  const int32_t* blocks;   // per-item block lists at fixed strides
   const uint16_t* q;       // [n_q][Hq][D]
   const uint16_t* k_pool;  // [L][N][Hkv][B][D]
   const uint16_t* v_pool;
@@ -37,6 +39,7 @@ struct AttnParams {
   float* part_o;           // [partial rows][D]
   float* part_lse;         // [partial rows], base-2 log
   int32_t n_mfma;
+  int32_t stride_mfma, stride_valu;   // block-list stride of each item kind
   int32_t layer, N, Hq, Hkv, G, B, log2B;
   float scale_log2;        // sm_scale * log2(e)
 };

@@ -33,7 +33,6 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kThreads = 256;
-constexpr int kMaxBlk = 512;       // block ids of one item staged in LDS
 
 // K or V of layer p.layer, kv head h, as 16-byte chunks: token slot `off` of
 // block `blk` starts at chunk blk * (Hkv * B * D / 8) + off * D / 8.  The pool
@@ -507,12 +506,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     MfmaSmem<D> m;
     ValuSmem<D> v;
   } sm;
-  __shared__ int32_t blk_s[kMaxBlk];
+  __shared__ int32_t blk_s[kMaxItemBlocks];
 
+  // the block list sits at a stride fixed per item kind, so its loads go
+  // out together with the item's
+  const bool is_mfma = static_cast<int>(blockIdx.x) < p.n_mfma;
+  const int nb = is_mfma ? p.stride_mfma : p.stride_valu;
+  const int32_t* lst = p.blocks + (is_mfma ? static_cast<size_t>(blockIdx.x) * p.stride_mfma
+                                           : static_cast<size_t>(p.n_mfma) * p.stride_mfma +
+                                                 static_cast<size_t>(blockIdx.x - p.n_mfma) * p.stride_valu);
+  for (int i = threadIdx.x; i < nb; i += kThreads) blk_s[i] = lst[i];
   const WorkItem it = p.items[blockIdx.x];
   const int h = blockIdx.y;
-  const int nblk = (it.n_tok + p.B - 1) >> p.log2B;
-  for (int i = threadIdx.x; i < nblk; i += kThreads) blk_s[i] = p.blocks[it.blk_off + i];
   lds_barrier();
   if (static_cast<int>(blockIdx.x) < p.n_mfma)
     mfma_item<D, RT>(p, it, h, sm.m, blk_s);

@@ -5,6 +5,8 @@
 // Partial states hold normalised o_i and a base-2 lse_i (-inf for a key set
 // the row could not see).  Grid: merged query vectors x chunks of 256
 // (q head, 4 dims) units; each thread reads its float4 of every partial.
+// Up to kMergeInline part rows travel inside the merge row itself, so all
+// partial loads leave in one round trip.
 #include <math.h>
 
 #include "../kernels.hpp"
@@ -13,6 +15,15 @@
 namespace pkv {
 namespace {
 
+__device__ __forceinline__ void merge_write(const MergeParams& p, const MergeRow& mr, int hq, int d,
+                                            float mx, float wsum, float4 acc) {
+  const float inv = 1.f / wsum;
+  const size_t orow = static_cast<size_t>(mr.q_index) * p.Hq + hq;
+  *reinterpret_cast<float4*>(p.out + orow * p.D + d) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (p.lse && d == 0) p.lse[orow] = (mx + log2f(wsum)) * kLn2;
+}
+
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const MergeRow mr = p.merges[blockIdx.x];
   const int per_head = p.D / 4;
@@ -20,6 +31,38 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   if (u >= p.Hq * per_head) return;
   const int hq = u / per_head;
   const int d = (u % per_head) * 4;
+  if (mr.n_parts <= kMergeInline) {
+    // part rows come with the merge row: every partial is requested at once
+    float l[kMergeInline];
+    float4 v[kMergeInline];
+#pragma unroll
+    for (int k = 0; k < kMergeInline; ++k) {
+      if (k < mr.n_parts) {
+        const size_t row = static_cast<size_t>(mr.inl[k]) + hq;
+        l[k] = p.part_lse[row];
+        v[k] = *reinterpret_cast<const float4*>(p.part_o + row * p.D + d);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMergeInline; ++k)
+      if (k < mr.n_parts) mx = fmaxf(mx, l[k]);
+    float wsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < kMergeInline; ++k) {
+      if (k < mr.n_parts) {
+        const float w = (l[k] == -INFINITY) ? 0.f : exp2f(l[k] - mx);
+        wsum += w;
+        acc.x = fmaf(w, v[k].x, acc.x);
+        acc.y = fmaf(w, v[k].y, acc.y);
+        acc.z = fmaf(w, v[k].z, acc.z);
+        acc.w = fmaf(w, v[k].w, acc.w);
+      }
+    }
+    merge_write(p, mr, hq, d, mx, wsum, acc);
+    return;
+  }
   const int32_t* parts = p.parts + mr.parts_off;
   float mx = -INFINITY;
 #pragma unroll 4
@@ -38,11 +81,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     acc.z = fmaf(w, v.z, acc.z);
     acc.w = fmaf(w, v.w, acc.w);
   }
-  const float inv = 1.f / wsum;
-  const size_t orow = static_cast<size_t>(mr.q_index) * p.Hq + hq;
-  *reinterpret_cast<float4*>(p.out + orow * p.D + d) =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (p.lse && d == 0) p.lse[orow] = (mx + log2f(wsum)) * kLn2;
+  merge_write(p, mr, hq, d, mx, wsum, acc);
 }
 
 }  // namespace

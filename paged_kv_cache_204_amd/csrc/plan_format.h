@@ -3,8 +3,10 @@
 //
 // A work item is one workgroup's share of an attention call for one kv head
 // (the kv head is blockIdx.y):
-//   - keys: n_tok tokens read through plan.blocks[blk_off ...] (token t sits
-//     in block blocks[blk_off + t / B] at slot t % B);
+//   - keys: n_tok tokens read through the item's block list (token t sits in
+//     block list[t / B] at slot t % B).  The device copy of the lists has a
+//     fixed stride per item kind (item_blocks below), so a workgroup finds
+//     its list from its own index, without waiting for the item;
 //   - queries: n_grp row groups from plan.groups[grp_off ...]; a row group is
 //     one query vector (a decode query or a draft-tree node) and expands to
 //     the G = Hq / Hkv query heads that read this kv head;
@@ -22,7 +24,7 @@
 namespace pkv {
 
 struct WorkItem {
-  int32_t blk_off;
+  int32_t blk_off;   // host side: the list at plan.blocks[blk_off ...]
   int32_t n_tok;
   int32_t tail_start;
   int32_t tail_node0;
@@ -42,16 +44,25 @@ struct RowGroup {
 };
 
 // One query vector whose partial states are merged: partial rows
-// parts[parts_off + p] + hq for p < n_parts.
+// part[p] + hq for p < n_parts, where part[] is inl[] when n_parts <=
+// kMergeInline and parts[parts_off ...] otherwise.
+constexpr int kMergeInline = 12;
+
 struct MergeRow {
   int32_t q_index;
-  int32_t parts_off;
   int32_t n_parts;
+  int32_t parts_off;
   int32_t pad;
+  int32_t inl[kMergeInline];
 };
+
+// Device block lists: MFMA item i (kernel order) reads
+// item_blocks[i * stride_mfma ...], VALU item j reads
+// item_blocks[n_mfma * stride_mfma + j * stride_valu ...]; entries past an
+// item's last block repeat that block.
 
 static_assert(sizeof(WorkItem) == 32, "WorkItem layout");
 static_assert(sizeof(RowGroup) == 32, "RowGroup layout");
-static_assert(sizeof(MergeRow) == 16, "MergeRow layout");
+static_assert(sizeof(MergeRow) == 64, "MergeRow layout");
 
 }  // namespace pkv
