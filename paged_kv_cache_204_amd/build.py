@@ -45,6 +45,8 @@ def _flags():
         # MFMA accumulators in VGPRs: the online-softmax rescale works on them
         # with VALU ops, so AGPR copies would cost a move per element per step
         "-mllvm", "-amdgpu-mfma-vgpr-form",
+        # leading kernel arguments arrive in SGPRs at wave start
+        "-mllvm", "-amdgpu-kernarg-preload-count=16",
         f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
     ]
 

@@ -228,7 +228,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
       for (int32_t u = 0; u < ng; ++u)
         plan->groups.push_back(RowGroup{s.queries[u0 + u], -1, 0u, 0u, -1, {0, 0, 0}});
       for (int32_t c = 0; c < nchunk; ++c) {
-        WorkItem it;
+        WorkItem it{};
         it.blk_off = blk_base + c * (chunk / B);
         it.n_tok = std::min(chunk, s.ntok - c * chunk);
         it.tail_start = INT_MAX;
@@ -236,7 +236,9 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
         it.grp_off = grp_off;
         it.n_grp = ng;
         it.part_base = -1;
-        it.xcd_slot = 0;
+        it.pad = 0;
+        for (int32_t u = 0; u < 8; ++u)
+          it.q_index[u] = u < ng ? plan->groups[grp_off + u].q_index : 0;
         (mfma ? plan->mfma : plan->valu).push_back(it);
       }
     }
@@ -315,7 +317,7 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
       }
       for (int32_t c = 0; c < nchunk; ++c) {
         const int32_t start = c * chunk;
-        WorkItem it;
+        WorkItem it{};
         it.blk_off = blk_base + start / B;
         it.n_tok = std::min(chunk, len - start);
         if (ctx - start >= it.n_tok) {
@@ -331,7 +333,9 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
         it.grp_off = grp_off;
         it.n_grp = ng;
         it.part_base = -1;
-        it.xcd_slot = 0;
+        it.pad = 0;
+        for (int32_t u = 0; u < 8; ++u)
+          it.q_index[u] = u < ng ? plan->groups[grp_off + u].q_index : 0;
         (mfma ? plan->mfma : plan->valu).push_back(it);
       }
     }

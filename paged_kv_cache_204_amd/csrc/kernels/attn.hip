@@ -297,13 +297,12 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
 // ---------------------------------------------------------------- VALU path
 constexpr int kValuRows = 8;     // query rows per item at most
 constexpr int kValuTok = 512;    // key tokens per item
-constexpr int kUnroll = 4;       // token passes with loads in flight per thread
+constexpr int kUnroll = 4;       // K token passes with loads in flight
+constexpr int kUnrollV = 8;      // V tokens in flight per lane
 
 template <int D>
 struct alignas(16) ValuSmem {
   float s[kValuTok][kValuRows];   // scores, then probabilities, token-major
-  float red[kThreads / 64][kValuRows][D];
-  float m[kValuRows], l[kValuRows];
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -316,21 +315,34 @@ __device__ __forceinline__ float dot8(const uint4& q, const uint4& k, float acc)
   return acc;
 }
 
-// A token's head_dim row is read by D/8 lanes (128-bit loads, whole row
-// coalesced); K and V of the first passes are requested together.  Phase 1
-// forms the scores of every row for the item's keys (v_dot2_f32_bf16, a DPP
-// butterfly over the row's lanes) into LDS, token-major; phase 2 takes an
-// exact two-pass softmax per row (one wave per row); phase 3 accumulates
-// p * v over each lane's tokens for its 8 dims (the 8 rows' p of a token are
-// two 128-bit LDS reads) and sums lanes and waves holding the same dims.
-// RM (4 or 8) bounds the rows at compile time; rows >= R compute on zero
-// queries and are never written.
+// Orders this wave's LDS writes before its later LDS reads (no other wave
+// takes part, so no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Phase 1 (whole workgroup): a token's head_dim row is read by D/8 lanes
+// with 128-bit loads (the row is one coalesced burst); each lane forms the
+// partial dot products of every row over its 8 dims (v_dot2_f32_bf16), a
+// DPP butterfly over the token's lanes completes them, and the scores land
+// in LDS token-major.  One workgroup barrier.  Phases 2-3 (each wave alone,
+// RM / 4 rows per wave): exact softmax of the wave's rows over the item's
+// keys, then O = P V with lane = (8-dim chunk, token slot): a lane reads the
+// V chunk of its tokens (requested before phase 1) and the wave's P pair of
+// each token with one 64-bit LDS read, and a butterfly over the token slots
+// sums O.  RM (4 or 8) bounds the rows at compile time; rows >= R are never
+// written.
 template <int D, int RM>
 __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& it, int h,
                                           ValuSmem<D>& sm, const int32_t* blk_s) {
-  constexpr int CPR = D / 8;
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
   constexpr int TPP = kThreads / CPR;
+  constexpr int TS = 64 / CPR;      // token slots of a wave in phase 3
+  constexpr int RW = RM / 4;        // rows per wave in phases 2-3
   static_assert(RM <= CPR, "one score row per lane of a token group");
+  static_assert(RW == 1 || RW == 2, "one or two rows per wave");
   const int G = p.G;
   const int R = it.n_grp * G;
   const int tid = threadIdx.x;
@@ -338,6 +350,10 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
   const int wave = tid >> 6;
   const int c = tid % CPR;
   const int tp = tid / CPR;
+  const int ts = lane / CPR;
+  const int r0 = wave * RW;
+  // read from the item in memory (uniform loads), not from its register copy
+  const int32_t* qidx = p.items[blockIdx.x].q_index;
 
   const uint4* kb = layer_head_base(p, p.k_pool, h, D);
   const uint4* vb = layer_head_base(p, p.v_pool, h, D);
@@ -348,20 +364,20 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
     return chunk_index(blk_s[t >> p.log2B], blk_chunks, (t & (p.B - 1)) * (D / 8) + c);
   };
   const int npass = (it.n_tok + TPP - 1) / TPP;
+  const int nv = (it.n_tok + TS - 1) / TS;   // phase-3 tokens per lane
 
-  // first passes of K and V, then the queries
-  uint4 kv[kUnroll], vv[kUnroll];
+  // first K passes, first V tokens of this lane, then the queries
+  uint4 kv[kUnroll], vv[kUnrollV];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) kv[u] = kb[addr(u * TPP + tp)];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) vv[u] = vb[addr(u * TPP + tp)];
+  for (int u = 0; u < kUnrollV; ++u) vv[u] = vb[addr(ts + TS * u)];
   uint4 qv[RM];
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
     qv[r] = make_uint4(0, 0, 0, 0);
     if (r < R) {
-      const RowGroup g = p.groups[it.grp_off + r / G];
-      const size_t qoff = (static_cast<size_t>(g.q_index) * p.Hq + h * G + r % G) * D + c * 8;
+      const size_t qoff = (static_cast<size_t>(qidx[r / G]) * p.Hq + h * G + r % G) * D + c * 8;
       qv[r] = *reinterpret_cast<const uint4*>(p.q + qoff);
     }
   }
@@ -394,8 +410,16 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
     }
   }
   lds_barrier();
-  // ---- phase 2: exact softmax per row -----------------------------------------
-  for (int r = wave; r < R; r += kThreads / 64) {
+  if (r0 >= R) return;   // no workgroup barrier follows
+
+  // ---- phase 2: exact softmax of this wave's rows --------------------------
+  float m_row[RW], l_row[RW];
+#pragma unroll
+  for (int j = 0; j < RW; ++j) {
+    m_row[j] = -INFINITY;
+    l_row[j] = 0.f;
+    const int r = r0 + j;
+    if (r >= R) continue;
     float mx = -INFINITY;
     for (int t = lane; t < it.n_tok; t += 64) mx = fmaxf(mx, sm.s[t][r]);
     mx = wave_max(mx);
@@ -406,102 +430,100 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
       sm.s[t][r] = e;
       sum += e;
     }
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      sm.m[r] = mx;
-      sm.l[r] = sum;
-    }
+    m_row[j] = mx;
+    l_row[j] = wave_sum(sum);
   }
-  lds_barrier();
-  // ---- phase 3: O = P V --------------------------------------------------------
-  float o[RM][8];
+  wave_lds_sync();
+
+  // ---- phase 3: O = P V for this wave's rows --------------------------------
+  float o[RW][8];
 #pragma unroll
-  for (int r = 0; r < RM; ++r)
+  for (int j = 0; j < RW; ++j)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[r][j] = 0.f;
-  for (int p0 = 0; p0 < npass; p0 += kUnroll) {
-    if (p0 > 0) {
+    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+  for (int k0 = 0; k0 < nv; k0 += kUnrollV) {
+    if (k0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) vv[u] = vb[addr((p0 + u) * TPP + tp)];
+      for (int u = 0; u < kUnrollV; ++u) vv[u] = vb[addr(ts + TS * (k0 + u))];
     }
-    float pr[kUnroll][RM];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = (p0 + u) * TPP + tp;
+    for (int u = 0; u < kUnrollV; ++u) {
+      const int t = ts + TS * (k0 + u);
       const int tc = min(t, t_last);
-      const float4 a = *reinterpret_cast<const float4*>(&sm.s[tc][0]);
-      pr[u][0] = a.x; pr[u][1] = a.y; pr[u][2] = a.z; pr[u][3] = a.w;
-      if constexpr (RM == 8) {
-        const float4 b = *reinterpret_cast<const float4*>(&sm.s[tc][4]);
-        pr[u][4] = b.x; pr[u][5] = b.y; pr[u][6] = b.z; pr[u][7] = b.w;
+      float pr[RW];
+      if constexpr (RW == 2) {
+        const float2 a = *reinterpret_cast<const float2*>(&sm.s[tc][r0]);
+        pr[0] = a.x;
+        pr[1] = a.y;
+      } else {
+        pr[0] = sm.s[tc][r0];
       }
       if (t > t_last) {
 #pragma unroll
-        for (int r = 0; r < RM; ++r) pr[u][r] = 0.f;
+        for (int j = 0; j < RW; ++j) pr[j] = 0.f;
       }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
       const float v[8] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y), bf16_hi(vv[u].y),
                           bf16_lo(vv[u].z), bf16_hi(vv[u].z), bf16_lo(vv[u].w), bf16_hi(vv[u].w)};
 #pragma unroll
-      for (int r = 0; r < RM; ++r)
+      for (int j = 0; j < RW; ++j)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[r][j] = fmaf(pr[u][r], v[j], o[r][j]);
+        for (int e = 0; e < 8; ++e) o[j][e] = fmaf(pr[j], v[e], o[j][e]);
     }
   }
-  // lanes of a wave that hold the same dims (token slots tp) sum up ...
+  // sum over the token slots (lanes that hold the same dims)
 #pragma unroll
-  for (int r = 0; r < RM; ++r) {
+  for (int j = 0; j < RW; ++j) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float x = o[r][j];
+    for (int e = 0; e < 8; ++e) {
+      float x = o[j][e];
       if constexpr (CPR == 8) x += dpp_f32<kDppXor8>(x);
-      o[r][j] = xor32_sum(xor16_sum(x));
+      o[j][e] = xor32_sum(xor16_sum(x));
     }
   }
-  // ... then the waves
-  if (lane < CPR) {
+  if (ts != 0) return;
 #pragma unroll
-    for (int r = 0; r < RM; ++r) {
-      *reinterpret_cast<float4*>(&sm.red[wave][r][c * 8]) = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
-      *reinterpret_cast<float4*>(&sm.red[wave][r][c * 8 + 4]) = make_float4(o[r][4], o[r][5], o[r][6], o[r][7]);
-    }
-  }
-  lds_barrier();
-  constexpr int kQuads = D / 4;
-  for (int e = tid; e < R * kQuads; e += kThreads) {
-    const int r = e / kQuads;
-    const int d = (e % kQuads) * 4;
-    float4 acc = *reinterpret_cast<const float4*>(&sm.red[0][r][d]);
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) {
-      const float4 x = *reinterpret_cast<const float4*>(&sm.red[w][r][d]);
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
-    }
-    const float l = sm.l[r];
-    const float m = sm.m[r];
+  for (int j = 0; j < RW; ++j) {
+    const int r = r0 + j;
+    if (r >= R) continue;
+    const float l = l_row[j];
+    const float m = m_row[j];
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float4 val = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    const RowGroup g = p.groups[it.grp_off + r / G];
     const int hq = h * G + r % G;
+    const float4 lo = make_float4(o[j][0] * inv, o[j][1] * inv, o[j][2] * inv, o[j][3] * inv);
+    const float4 hi = make_float4(o[j][4] * inv, o[j][5] * inv, o[j][6] * inv, o[j][7] * inv);
+    float* dst;
     if (it.part_base < 0) {
-      const size_t row = static_cast<size_t>(g.q_index) * p.Hq + hq;
-      *reinterpret_cast<float4*>(p.out + row * D + d) = val;
-      if (p.lse && d == 0) p.lse[row] = (m + log2f(l)) * kLn2;
+      const size_t row = static_cast<size_t>(qidx[r / G]) * p.Hq + hq;
+      dst = p.out + row * D + c * 8;
+      if (p.lse && c == 0) p.lse[row] = (m + log2f(l)) * kLn2;
     } else {
       const size_t row = static_cast<size_t>(it.part_base) + static_cast<size_t>(r / G) * p.Hq + hq;
-      *reinterpret_cast<float4*>(p.part_o + row * D + d) = val;
-      if (d == 0) p.part_lse[row] = l > 0.f ? m + log2f(l) : -INFINITY;
+      dst = p.part_o + row * D + c * 8;
+      if (c == 0) p.part_lse[row] = l > 0.f ? m + log2f(l) : -INFINITY;
     }
+    *reinterpret_cast<float4*>(dst) = lo;
+    *reinterpret_cast<float4*>(dst + 4) = hi;
   }
 }
 
+// The fields a workgroup needs first also come as leading scalar arguments:
+// the build preloads leading kernel arguments into SGPRs, so the item, block
+// list and query loads leave at wave start instead of after a kernel-argument
+// fetch.
 template <int D, int RT, int RM>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads) void attn_kernel(const WorkItem* __restrict__ items,
+                                                        const int32_t* __restrict__ blocks,
+                                                        const RowGroup* __restrict__ groups,
+                                                        const uint16_t* __restrict__ q,
+                                                        int32_t n_mfma, int32_t stride_mfma,
+                                                        int32_t stride_valu, AttnParams p) {
+  p.items = items;
+  p.blocks = blocks;
+  p.groups = groups;
+  p.q = q;
+  p.n_mfma = n_mfma;
+  p.stride_mfma = stride_mfma;
+  p.stride_valu = stride_valu;
   __shared__ union alignas(16) {
     MfmaSmem<D> m;
     ValuSmem<D> v;
@@ -530,9 +552,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 template <int D, int RT>
 hipError_t launch_rows(const AttnParams& p, dim3 grid, int32_t valu_rows, hipStream_t s) {
   if (valu_rows <= 4)
-    hipLaunchKernelGGL((attn_kernel<D, RT, 4>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_kernel<D, RT, 4>), grid, dim3(kThreads), 0, s, p.items, p.blocks, p.groups,
+                       p.q, p.n_mfma, p.stride_mfma, p.stride_valu, p);
   else
-    hipLaunchKernelGGL((attn_kernel<D, RT, 8>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_kernel<D, RT, 8>), grid, dim3(kThreads), 0, s, p.items, p.blocks, p.groups,
+                       p.q, p.n_mfma, p.stride_mfma, p.stride_valu, p);
   return hipGetLastError();
 }
 

@@ -24,8 +24,9 @@ __device__ __forceinline__ void merge_write(const MergeParams& p, const MergeRow
   if (p.lse && d == 0) p.lse[orow] = (mx + log2f(wsum)) * kLn2;
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  const MergeRow mr = p.merges[blockIdx.x];
+// merges leads the arguments so that it arrives preloaded in SGPRs
+__global__ __launch_bounds__(256) void merge_kernel(const MergeRow* __restrict__ merges, MergeParams p) {
+  const MergeRow mr = merges[blockIdx.x];
   const int per_head = p.D / 4;
   const int u = blockIdx.y * blockDim.x + threadIdx.x;
   if (u >= p.Hq * per_head) return;
@@ -90,7 +91,7 @@ hipError_t launch_merge(const MergeParams& p, int32_t n_rows, hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
   const int units = p.Hq * (p.D / 4);
   const dim3 grid(static_cast<uint32_t>(n_rows), static_cast<uint32_t>((units + 255) / 256));
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, s, p.merges, p);
   return hipGetLastError();
 }
 

@@ -31,7 +31,10 @@ struct WorkItem {
   int32_t grp_off;
   int32_t n_grp;
   int32_t part_base;
-  int32_t xcd_slot;  // informational: the XCD the planner aimed this item at
+  int32_t pad;
+  // query vectors of the first min(n_grp, 8) row groups, so the query loads
+  // need only the item itself
+  int32_t q_index[8];
 };
 
 struct RowGroup {
@@ -61,7 +64,7 @@ struct MergeRow {
 // item_blocks[n_mfma * stride_mfma + j * stride_valu ...]; entries past an
 // item's last block repeat that block.
 
-static_assert(sizeof(WorkItem) == 32, "WorkItem layout");
+static_assert(sizeof(WorkItem) == 64, "WorkItem layout");
 static_assert(sizeof(RowGroup) == 32, "RowGroup layout");
 static_assert(sizeof(MergeRow) == 64, "MergeRow layout");
 
