@@ -201,10 +201,11 @@ pkv_status paged_attn_decode_plan_stats(pkv_pool* pool, const int64_t* seqs,
 
 /* ---- kernel timing (benchmarks) --------------------------------------- */
 
-/* When enabled, every paged_attn_decode / paged_attn_tree_verify call records
- * a pair of HIP events on its stream around its attention kernel (the plan
- * upload and the partial-state merge kernel stay outside).  Disabling drops
- * pending pairs. */
+/* enable = n > 0: every n-th paged_attn_decode / paged_attn_tree_verify call
+ * records a pair of HIP events on its stream around its attention kernel (the
+ * plan upload and the partial-state merge kernel stay outside); sampling
+ * keeps the event records from slowing the calls they measure.  enable = 0
+ * turns timing off and drops pending pairs; negative values are an error. */
 pkv_status pkv_timing_enable(pkv_pool* pool, int32_t enable);
 
 /* Synchronise the recorded events and return the summed kernel time in ms

@@ -140,9 +140,21 @@ def _stream(s):
     raise TypeError("stream must be an int address or have .cuda_stream")
 
 
+_SEQ_TYPES = {}
+
+
 def _seq_array(seqs):
+    """(pointer argument, length) for a sequence-id argument: lists and tuples
+    become a ctypes int64 array (the cheap path for per-step calls), anything
+    else goes through numpy."""
+    if type(seqs) is list or type(seqs) is tuple:
+        n = len(seqs)
+        t = _SEQ_TYPES.get(n)
+        if t is None:
+            t = _SEQ_TYPES[n] = ctypes.c_int64 * n
+        return t(*seqs), n
     a = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64).reshape(-1))
-    return a, a.ctypes.data_as(_PI64)
+    return a.ctypes.data_as(_PI64), a.size
 
 
 def _desc(desc):
@@ -195,24 +207,24 @@ def seq_free(pool, seq):
 
 
 def kv_append(pool, seqs, n_tok, k_new=None, v_new=None, stream=None):
-    a, p = _seq_array(seqs)
-    _check(load().kv_append(pool, p, len(a), int(n_tok), _addr(k_new), _addr(v_new),
+    p, n = _seq_array(seqs)
+    _check(load().kv_append(pool, p, n, int(n_tok), _addr(k_new), _addr(v_new),
                             _stream(stream)))
 
 
 def paged_attn_decode(pool, layer, seqs, q, sm_scale, out, lse=None, stream=None):
-    a, p = _seq_array(seqs)
-    _check(load().paged_attn_decode(pool, int(layer), p, len(a), _addr(q), float(sm_scale),
+    p, n = _seq_array(seqs)
+    _check(load().paged_attn_decode(pool, int(layer), p, n, _addr(q), float(sm_scale),
                                     _addr(out), _addr(lse), _stream(stream)))
 
 
 def paged_attn_tree_verify(pool, layer, seqs, n_nodes, parent, q, sm_scale, out, lse=None,
                            stream=None):
-    a, p = _seq_array(seqs)
+    p, n = _seq_array(seqs)
     par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
-    if par.size != len(a) * int(n_nodes):
+    if par.size != n * int(n_nodes):
         raise ValueError("parent must hold n_seqs * n_nodes entries")
-    _check(load().paged_attn_tree_verify(pool, int(layer), p, len(a), int(n_nodes),
+    _check(load().paged_attn_tree_verify(pool, int(layer), p, n, int(n_nodes),
                                          par.ctypes.data_as(_PI32), _addr(q), float(sm_scale),
                                          _addr(out), _addr(lse), _stream(stream)))
 
@@ -253,14 +265,17 @@ def kv_last_append(pool):
 
 
 def paged_attn_decode_plan_stats(pool, seqs) -> dict:
-    a, p = _seq_array(seqs)
+    p, n = _seq_array(seqs)
     st = PkvPlanStats()
-    _check(load().paged_attn_decode_plan_stats(pool, p, len(a), ctypes.byref(st)))
+    _check(load().paged_attn_decode_plan_stats(pool, p, n, ctypes.byref(st)))
     return {f: getattr(st, f) for f, _ in PkvPlanStats._fields_}
 
 
 def pkv_timing_enable(pool, enable=True):
-    _check(load().pkv_timing_enable(pool, 1 if enable else 0))
+    """enable: True (every call), False (off) or a sampling period n > 0."""
+    if enable is True or enable is False:
+        enable = 1 if enable else 0
+    _check(load().pkv_timing_enable(pool, int(enable)))
 
 
 def pkv_timing_read(pool, reset=True):

@@ -119,8 +119,11 @@ struct pkv_pool {
   PlanLayout dlayout;
   pkv::Plan vplan;
   PlanLayout vlayout;
-  // kernel timing: event pairs recorded around attention kernels
+  // kernel timing: event pairs recorded around every timing_every-th
+  // attention kernel
   bool timing = false;
+  int32_t timing_every = 1;
+  int64_t timing_tick = 0;
   std::vector<hipEvent_t> ev_free;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pending;
   double timed_ms = 0.0;
@@ -220,7 +223,8 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
   ap.scale_log2 = sm_scale * pkv::kLog2eHost;
   const int32_t n_items = static_cast<int32_t>(plan.mfma.size() + plan.valu.size());
   hipEvent_t ev_a = nullptr, ev_b = nullptr;
-  if (p->timing) {
+  const bool timed = p->timing && (p->timing_tick++ % p->timing_every) == 0;
+  if (timed) {
     s = take_event(p, &ev_a);
     if (s == PKV_OK) s = take_event(p, &ev_b);
     if (s != PKV_OK) return s;
@@ -228,7 +232,7 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
   }
   PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles,
                             plan.valu_max_rows * ap.G, stream));
-  if (p->timing) {
+  if (timed) {
     PKV_HIP(hipEventRecord(ev_b, stream));
     p->ev_pending.emplace_back(ev_a, ev_b);
   }
@@ -550,7 +554,10 @@ pkv_status paged_attn_decode_plan_stats(pkv_pool* p, const int64_t* seqs, int32_
 pkv_status pkv_timing_enable(pkv_pool* p, int32_t enable) {
   if (!p) return fail(PKV_ERR_ARG, "pkv_timing_enable: NULL pool");
   if (!p->device) return fail(PKV_ERR_ARG, "pkv_timing_enable: the pool has no device storage");
+  if (enable < 0) return fail(PKV_ERR_ARG, "pkv_timing_enable: negative sampling period");
   p->timing = enable != 0;
+  p->timing_every = enable > 0 ? enable : 1;
+  p->timing_tick = 0;
   if (!p->timing) {
     for (auto& pr : p->ev_pending) {
       p->ev_free.push_back(pr.first);
