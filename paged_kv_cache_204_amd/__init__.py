@@ -25,6 +25,7 @@ __all__ = [
     "paged_attn_decode", "paged_attn_tree_verify",
     "seq_block_table", "block_refcount", "free_list", "kv_last_append",
     "paged_attn_decode_plan_stats", "pkv_timing_enable", "pkv_timing_read", "pkv_last_error",
+    "seq_ids",
     "PKV_OK", "PKV_ERR_ARG", "PKV_ERR_OOM", "PKV_ERR_SEQ", "PKV_ERR_HIP",
     "PKV_ERR_EMPTY", "PKV_ERR_UNSUPPORTED",
 ]
@@ -121,12 +122,14 @@ def _check(code):
 def _addr(x):
     if x is None:
         return None
+    dp = getattr(x, "data_ptr", None)
+    if dp is not None:
+        contiguous = getattr(x, "is_contiguous", None)
+        if contiguous is not None and not contiguous():
+            raise ValueError("device arguments must be contiguous")
+        return dp()
     if isinstance(x, int):
         return x or None
-    if hasattr(x, "data_ptr"):
-        if hasattr(x, "is_contiguous") and not x.is_contiguous():
-            raise ValueError("device arguments must be contiguous")
-        return x.data_ptr()
     raise TypeError(f"cannot take a device address from {type(x).__name__}")
 
 
@@ -143,10 +146,20 @@ def _stream(s):
 _SEQ_TYPES = {}
 
 
+def seq_ids(seqs):
+    """A ctypes int64 array of sequence ids: pass it to the per-step calls in
+    place of a list to skip the conversion on every call."""
+    return (ctypes.c_int64 * len(seqs))(*seqs)
+
+
 def _seq_array(seqs):
-    """(pointer argument, length) for a sequence-id argument: lists and tuples
-    become a ctypes int64 array (the cheap path for per-step calls), anything
+    """(pointer argument, length) for a sequence-id argument: ctypes int64
+    arrays (see seq_ids) pass through, lists and tuples become one, anything
     else goes through numpy."""
+    if isinstance(seqs, ctypes.Array):
+        if seqs._type_ is not ctypes.c_int64:
+            raise TypeError("sequence ids must be int64")
+        return seqs, len(seqs)
     if type(seqs) is list or type(seqs) is tuple:
         n = len(seqs)
         t = _SEQ_TYPES.get(n)
@@ -214,8 +227,10 @@ def kv_append(pool, seqs, n_tok, k_new=None, v_new=None, stream=None):
 
 def paged_attn_decode(pool, layer, seqs, q, sm_scale, out, lse=None, stream=None):
     p, n = _seq_array(seqs)
-    _check(load().paged_attn_decode(pool, int(layer), p, n, _addr(q), float(sm_scale),
-                                    _addr(out), _addr(lse), _stream(stream)))
+    code = (_lib or load()).paged_attn_decode(pool, int(layer), p, n, _addr(q), float(sm_scale),
+                                              _addr(out), _addr(lse), _stream(stream))
+    if code != PKV_OK:
+        _check(code)
 
 
 def paged_attn_tree_verify(pool, layer, seqs, n_nodes, parent, q, sm_scale, out, lse=None,

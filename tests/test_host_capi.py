@@ -315,3 +315,35 @@ def test_fork_cost_is_independent_of_data():
             pkv.seq_free(pool, k)
     finally:
         pkv.kv_pool_destroy(pool)
+
+
+def test_seq_id_arguments_accept_lists_arrays_and_ctypes():
+    """The binding takes sequence ids as a list, a numpy array or a ctypes
+    int64 array (seq_ids) and passes the same ids to the library."""
+    import ctypes
+    import numpy as np
+    desc = dict(num_blocks=64, block_size=16, num_layers=1, num_q_heads=8, num_kv_heads=2, head_dim=64)
+    pool = pkv.kv_pool_create(desc, None, None)
+    try:
+        ids = [pkv.seq_allocate(pool) for _ in range(3)]
+        pkv.kv_append(pool, pkv.seq_ids(ids), 20, None, None, None)
+        for form in (ids, tuple(ids), np.array(ids, dtype=np.int64), pkv.seq_ids(ids)):
+            st = pkv.paged_attn_decode_plan_stats(pool, form)
+            assert st["logical_tokens"] == 60
+        with pytest.raises(TypeError):
+            pkv.paged_attn_decode_plan_stats(pool, (ctypes.c_int32 * 3)(*ids))
+    finally:
+        pkv.kv_pool_destroy(pool)
+
+
+def test_timing_sampling_period_is_validated():
+    desc = dict(num_blocks=8, block_size=16, num_layers=1, num_q_heads=8, num_kv_heads=2, head_dim=64)
+    pool = pkv.kv_pool_create(desc, None, None)
+    try:
+        # host-only pools have no device timing at all
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_timing_enable(pool, 16)
+    finally:
+        pkv.kv_pool_destroy(pool)
+    lib = pkv.load()
+    assert lib.pkv_timing_enable(None, 1) == pkv.PKV_ERR_ARG
