@@ -231,7 +231,7 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
     PKV_HIP(hipEventRecord(ev_a, stream));
   }
   PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles,
-                            plan.valu_max_rows * ap.G, stream));
+                            plan.valu_max_rows * ap.G, plan.mfma_waves, stream));
   if (timed) {
     PKV_HIP(hipEventRecord(ev_b, stream));
     p->ev_pending.emplace_back(ev_a, ev_b);
@@ -265,6 +265,7 @@ void apply_env(pkv::PlanConfig* c) {
   };
   get("PKV_MFMA_MIN_ROWS", &c->mfma_min_rows, 0, 1 << 20);
   get("PKV_MFMA_ROW_TILES", &c->mfma_row_tiles, 0, 2);
+  get("PKV_MFMA_WAVES", &c->mfma_waves, 0, 8);
   get("PKV_TARGET_WGS", &c->target_wgs, 1, 1 << 20);
   get("PKV_TARGET_MFMA_WGS", &c->target_mfma_wgs, 1, 1 << 20);
   get("PKV_MAX_CHUNK", &c->max_chunk, 64, 1 << 20);

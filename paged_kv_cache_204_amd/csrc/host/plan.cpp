@@ -34,6 +34,13 @@ int64_t chunk_cap(const PlanConfig& cfg, int32_t block_size) {
 // Partial-row bookkeeping shared by both planners: `owner[g]` is the query
 // vector of row group g; items that do not cover all keys of their queries
 // get partial rows, and every such query gets a merge row.
+// Waves per MFMA workgroup: eight (one K/V tile staged for 256 rows) only
+// when the launch has no VALU items and some query tile fills 256 rows.
+int32_t pick_waves(const PlanConfig& cfg, bool any_valu, int32_t row_tiles, int64_t max_rows) {
+  if (cfg.mfma_waves == 4 || cfg.mfma_waves == 8) return any_valu || row_tiles != 2 ? 4 : cfg.mfma_waves;
+  return !any_valu && row_tiles == 2 && max_rows >= mfma_item_rows(2, 8) ? 8 : 4;
+}
+
 void finish_parts(Plan* plan, const std::vector<int32_t>& n_parts, int32_t hq) {
   std::vector<std::vector<int32_t>> parts_of(n_parts.size());
   auto assign = [&](std::vector<WorkItem>& items) {
@@ -196,9 +203,14 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
            (cfg.mfma_min_rows > 0 && static_cast<int64_t>(s.queries.size()) * G >= cfg.mfma_min_rows);
   };
   bool any_valu = false;
-  for (const Segment& s : segs) any_valu = any_valu || !is_mfma(s);
+  int64_t max_rows = 0;
+  for (const Segment& s : segs) {
+    any_valu = any_valu || !is_mfma(s);
+    max_rows = std::max<int64_t>(max_rows, static_cast<int64_t>(s.queries.size()) * G);
+  }
   plan->mfma_row_tiles = cfg.mfma_row_tiles > 0 ? cfg.mfma_row_tiles : (any_valu ? 1 : 2);
-  const int32_t mrows = mfma_item_rows(plan->mfma_row_tiles);
+  plan->mfma_waves = pick_waves(cfg, any_valu, plan->mfma_row_tiles, max_rows);
+  const int32_t mrows = mfma_item_rows(plan->mfma_row_tiles, plan->mfma_waves);
   const int32_t unit = std::max(cfg.tile, B);
   const int64_t cap = chunk_cap(cfg, B);
   const int64_t cap_v = std::min<int64_t>(cap, cfg.valu_max_tokens);
@@ -211,7 +223,8 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     (m ? work_m : work_v) += static_cast<int64_t>(s.ntok) * ceil_div(static_cast<int64_t>(s.queries.size()), per);
   }
   const int32_t chunk_v = pick_chunk(work_v, sh.num_kv_heads, unit, cfg.target_wgs, cap_v);
-  const int32_t chunk_m = pick_chunk(work_m, sh.num_kv_heads, unit, cfg.target_mfma_wgs, cap);
+  const int32_t chunk_m = pick_chunk(work_m, sh.num_kv_heads, unit,
+                                     cfg.target_mfma_wgs * 4 / plan->mfma_waves, cap);
 
   std::vector<int32_t> n_parts(n_seqs, 0);
   for (const Segment& s : segs) {
@@ -282,7 +295,11 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   const bool mfma = G > cfg.valu_rows ||
                     (cfg.mfma_min_rows > 0 && static_cast<int64_t>(n_nodes) * G >= cfg.mfma_min_rows);
   plan->mfma_row_tiles = cfg.mfma_row_tiles > 0 ? cfg.mfma_row_tiles : 2;
-  const int32_t per = std::max(1, (mfma ? mfma_item_rows(plan->mfma_row_tiles) : cfg.valu_rows) / G);
+  plan->mfma_waves = mfma ? pick_waves(cfg, false, plan->mfma_row_tiles,
+                                       static_cast<int64_t>(n_nodes) * G)
+                          : 4;
+  const int32_t per = std::max(1, (mfma ? mfma_item_rows(plan->mfma_row_tiles, plan->mfma_waves)
+                                        : cfg.valu_rows) / G);
   const int64_t subsets = ceil_div(n_nodes, per);
   int64_t work = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
@@ -294,7 +311,8 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   const int64_t cap = mfma ? chunk_cap(cfg, B)
                            : std::min<int64_t>(chunk_cap(cfg, B), cfg.valu_max_tokens);
   const int32_t chunk = pick_chunk(work, sh.num_kv_heads, std::max(cfg.tile, B),
-                                   mfma ? cfg.target_mfma_wgs : cfg.target_wgs, cap);
+                                   mfma ? cfg.target_mfma_wgs * 4 / plan->mfma_waves : cfg.target_wgs,
+                                   cap);
   std::vector<int32_t> n_parts(static_cast<size_t>(n_seqs) * n_nodes, 0);
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t len = st[i]->len;

@@ -29,6 +29,9 @@ struct PlanConfig {
   int32_t mfma_row_tiles = 0;    // 16-row tiles per wave of the MFMA path (1 or 2); 0 picks
                                  // 2 for calls with MFMA items only and 1 otherwise (the
                                  // two-tile kernel's registers lower the VALU items' occupancy)
+  int32_t mfma_waves = 0;        // waves per MFMA workgroup (4 or 8); 0 picks 8 for calls
+                                 // with MFMA items only whose query tiles fill 256 rows (one
+                                 // K/V tile then feeds all of them), else 4
   int32_t mfma_min_rows = 32;    // segments with at least this many rows use MFMA; 0 = only
                                  // when a single query's GQA group exceeds valu_rows
   int32_t target_wgs = 256;      // VALU workgroups to aim for over all kv heads
@@ -39,7 +42,7 @@ struct PlanConfig {
 };
 
 // Rows of one MFMA work item for a row-tile setting (4 waves x 16 x tiles).
-inline int32_t mfma_item_rows(int32_t row_tiles) { return 4 * 16 * row_tiles; }
+inline int32_t mfma_item_rows(int32_t row_tiles, int32_t waves) { return waves * 16 * row_tiles; }
 
 struct Plan {
   std::vector<WorkItem> valu;   // items for the VALU kernel
@@ -52,6 +55,7 @@ struct Plan {
   int32_t stride_mfma = 0, stride_valu = 0;
   int64_t partial_rows = 0;
   int32_t mfma_row_tiles = 1;   // row tiles per wave the MFMA items were cut for
+  int32_t mfma_waves = 4;       // waves per MFMA workgroup (8 only without VALU items)
   int32_t valu_max_rows = 0;    // most rows in any VALU item
   // what the call reads
   int64_t unique_tokens = 0;

@@ -45,9 +45,10 @@ struct AttnParams {
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
-// valu_rows: the most rows any VALU item of the launch holds (<= 8).
+// valu_rows: the most rows any VALU item of the launch holds (<= 8);
+// waves: 4, or 8 for launches of MFMA items only (row_tiles 2).
 hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t row_tiles,
-                       int32_t valu_rows, hipStream_t s);
+                       int32_t valu_rows, int32_t waves, hipStream_t s);
 
 // Log-sum-exp merge of the partial states of several work items.
 struct MergeParams {

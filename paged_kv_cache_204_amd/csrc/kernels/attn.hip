@@ -67,14 +67,17 @@ struct MfmaSmem {
 // O^T keeps each lane on the same row, so the online rescale is lane local.
 // The O rescale runs only when some row of the wave outgrows its reference
 // max by more than kSlack (see the softmax step below).
-template <int D, int RT>
+template <int D, int RT, int W>
 __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& it, int h,
                                           MfmaSmem<D>& sm, const int32_t* blk_s) {
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
   constexpr int CPR = D / 8;
-  constexpr int KPER = kStep * CPR / kThreads;   // K chunks per thread per step
+  constexpr int NT = 64 * W;                     // threads of the workgroup
+  constexpr int KCH = kStep * CPR;               // K chunks per step
+  constexpr int KPER = KCH >= NT ? KCH / NT : 1; // K chunks per thread per step
   constexpr int VUNITS = 16 * CPR;               // (token pair, chunk) units per step
+  static_assert(KCH % NT == 0 || NT % KCH == 0, "K chunks split evenly over the threads");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -120,11 +123,13 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
     for (int dt = 0; dt < ND; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Staging: K chunk ci = tid + 256 i is (token ci / CPR, 16-byte chunk
-  // ci % CPR); V unit tid is chunk (tid / 16) of tokens 2q and 2q + 1
+  // Staging: K chunk ci = tid + NT i is (token ci / CPR, 16-byte chunk
+  // ci % CPR; threads past the step's chunks load a duplicate and store
+  // nothing); V unit tid is chunk (tid / 16) of tokens 2q and 2q + 1
   // (q = tid % 16), written transposed as 32-bit words (one dim, two tokens)
   // -- with the 18-word V^T pitch the 64 lanes of a store hit 64 banks.
   const bool v_on = tid < VUNITS;
+  const bool k_on = KCH >= NT || tid < KCH;
   const int v_pair = tid & 15;
   const int v_c = (tid >> 4) % CPR;
   const uint4* kb = layer_head_base(p, p.k_pool, h, D);
@@ -139,7 +144,7 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
   auto fetch = [&](int slot, int t0) {
 #pragma unroll
     for (int i = 0; i < KPER; ++i) {
-      const int ci = tid + kThreads * i;
+      const int ci = (tid + NT * i) % KCH;
       rk[slot][i] = ldg(kb, t0 + ci / CPR, ci % CPR);
     }
     rv[slot][0] = ldg(vb, t0 + 2 * v_pair, v_c);
@@ -149,10 +154,12 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
 
   auto step = [&](int slot, int s) {
     const int buf = s & 1;
+    if (k_on) {
 #pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int ci = tid + kThreads * i;
-      *reinterpret_cast<uint4*>(&sm.k[buf][ci / CPR][(ci % CPR) * 8]) = rk[slot][i];
+      for (int i = 0; i < KPER; ++i) {
+        const int ci = tid + NT * i;
+        *reinterpret_cast<uint4*>(&sm.k[buf][ci / CPR][(ci % CPR) * 8]) = rk[slot][i];
+      }
     }
     if (v_on) {
       const uint32_t a[4] = {rv[slot][0].x, rv[slot][0].y, rv[slot][0].z, rv[slot][0].w};
@@ -510,8 +517,8 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
 // the build preloads leading kernel arguments into SGPRs, so the item, block
 // list and query loads leave at wave start instead of after a kernel-argument
 // fetch.
-template <int D, int RT, int RM>
-__global__ __launch_bounds__(kThreads) void attn_kernel(const WorkItem* __restrict__ items,
+template <int D, int RT, int RM, int W>
+__global__ __launch_bounds__(64 * W) void attn_kernel(const WorkItem* __restrict__ items,
                                                         const int32_t* __restrict__ blocks,
                                                         const RowGroup* __restrict__ groups,
                                                         const uint16_t* __restrict__ q,
@@ -537,37 +544,50 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const WorkItem* __restri
   const int32_t* lst = p.blocks + (is_mfma ? static_cast<size_t>(blockIdx.x) * p.stride_mfma
                                            : static_cast<size_t>(p.n_mfma) * p.stride_mfma +
                                                  static_cast<size_t>(blockIdx.x - p.n_mfma) * p.stride_valu);
-  for (int i = threadIdx.x; i < nb; i += kThreads) blk_s[i] = lst[i];
+  for (int i = threadIdx.x; i < nb; i += 64 * W) blk_s[i] = lst[i];
   const WorkItem it = p.items[blockIdx.x];
   const int h = blockIdx.y;
   lds_barrier();
-  if (static_cast<int>(blockIdx.x) < p.n_mfma)
-    mfma_item<D, RT>(p, it, h, sm.m, blk_s);
-  else
-    valu_item<D, RM>(p, it, h, sm.v, blk_s);
+  if constexpr (W == 4) {
+    if (static_cast<int>(blockIdx.x) < p.n_mfma)
+      mfma_item<D, RT, 4>(p, it, h, sm.m, blk_s);
+    else
+      valu_item<D, RM>(p, it, h, sm.v, blk_s);
+  } else {
+    // eight-wave workgroups serve launches whose items are all MFMA items
+    mfma_item<D, RT, W>(p, it, h, sm.m, blk_s);
+  }
 }
 
 }  // namespace
 
 template <int D, int RT>
-hipError_t launch_rows(const AttnParams& p, dim3 grid, int32_t valu_rows, hipStream_t s) {
-  if (valu_rows <= 4)
-    hipLaunchKernelGGL((attn_kernel<D, RT, 4>), grid, dim3(kThreads), 0, s, p.items, p.blocks, p.groups,
+hipError_t launch_rows(const AttnParams& p, dim3 grid, int32_t valu_rows, int32_t waves, hipStream_t s) {
+  if (waves == 8) {
+    if constexpr (RT == 2)
+      hipLaunchKernelGGL((attn_kernel<D, RT, 4, 8>), grid, dim3(512), 0, s, p.items, p.blocks, p.groups,
+                         p.q, p.n_mfma, p.stride_mfma, p.stride_valu, p);
+    else
+      return hipErrorInvalidValue;
+  } else if (valu_rows <= 4) {
+    hipLaunchKernelGGL((attn_kernel<D, RT, 4, 4>), grid, dim3(kThreads), 0, s, p.items, p.blocks, p.groups,
                        p.q, p.n_mfma, p.stride_mfma, p.stride_valu, p);
-  else
-    hipLaunchKernelGGL((attn_kernel<D, RT, 8>), grid, dim3(kThreads), 0, s, p.items, p.blocks, p.groups,
+  } else {
+    hipLaunchKernelGGL((attn_kernel<D, RT, 8, 4>), grid, dim3(kThreads), 0, s, p.items, p.blocks, p.groups,
                        p.q, p.n_mfma, p.stride_mfma, p.stride_valu, p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t row_tiles,
-                       int32_t valu_rows, hipStream_t s) {
+                       int32_t valu_rows, int32_t waves, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
+  if (waves == 8 && n_items != p.n_mfma) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(n_items), static_cast<uint32_t>(p.Hkv));
-  if (head_dim == 64 && row_tiles == 1) return launch_rows<64, 1>(p, grid, valu_rows, s);
-  if (head_dim == 64 && row_tiles == 2) return launch_rows<64, 2>(p, grid, valu_rows, s);
-  if (head_dim == 128 && row_tiles == 1) return launch_rows<128, 1>(p, grid, valu_rows, s);
-  if (head_dim == 128 && row_tiles == 2) return launch_rows<128, 2>(p, grid, valu_rows, s);
+  if (head_dim == 64 && row_tiles == 1) return launch_rows<64, 1>(p, grid, valu_rows, waves, s);
+  if (head_dim == 64 && row_tiles == 2) return launch_rows<64, 2>(p, grid, valu_rows, waves, s);
+  if (head_dim == 128 && row_tiles == 1) return launch_rows<128, 1>(p, grid, valu_rows, waves, s);
+  if (head_dim == 128 && row_tiles == 2) return launch_rows<128, 2>(p, grid, valu_rows, waves, s);
   return hipErrorInvalidValue;
 }
 
