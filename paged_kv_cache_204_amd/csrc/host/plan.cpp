@@ -31,9 +31,6 @@ int64_t chunk_cap(const PlanConfig& cfg, int32_t block_size) {
   return std::min<int64_t>(cfg.max_chunk, static_cast<int64_t>(cfg.max_chunk_blocks) * block_size);
 }
 
-// Partial-row bookkeeping shared by both planners: `owner[g]` is the query
-// vector of row group g; items that do not cover all keys of their queries
-// get partial rows, and every such query gets a merge row.
 // Waves per MFMA workgroup: eight (one K/V tile staged for 256 rows) only
 // when the launch has no VALU items and some query tile fills 256 rows.
 int32_t pick_waves(const PlanConfig& cfg, bool any_valu, int32_t row_tiles, int64_t max_rows) {
@@ -41,38 +38,51 @@ int32_t pick_waves(const PlanConfig& cfg, bool any_valu, int32_t row_tiles, int6
   return !any_valu && row_tiles == 2 && max_rows >= mfma_item_rows(2, 8) ? 8 : 4;
 }
 
+// Partial-row bookkeeping shared by both planners: `owner[g]` is the query
+// vector of row group g; items that do not cover all keys of their queries
+// get partial rows, and every such query gets a merge row.
 void finish_parts(Plan* plan, const std::vector<int32_t>& n_parts, int32_t hq) {
-  std::vector<std::vector<int32_t>> parts_of(n_parts.size());
-  auto assign = [&](std::vector<WorkItem>& items) {
-    for (WorkItem& it : items) {
-      bool direct = true;
-      for (int32_t u = 0; u < it.n_grp; ++u)
-        if (n_parts[plan->groups[it.grp_off + u].q_index] != 1) direct = false;
-      if (direct) {
+  const size_t nq = n_parts.size();
+  // partial rows of every query as one flat list (count, prefix sums, fill):
+  // no allocation per query
+  auto direct = [&](const WorkItem& it) {
+    for (int32_t u = 0; u < it.n_grp; ++u)
+      if (n_parts[plan->groups[it.grp_off + u].q_index] != 1) return false;
+    return true;
+  };
+  std::vector<int32_t> start(nq + 1, 0);
+  for (const auto* items : {&plan->valu, &plan->mfma})
+    for (const WorkItem& it : *items)
+      if (!direct(it))
+        for (int32_t u = 0; u < it.n_grp; ++u) ++start[plan->groups[it.grp_off + u].q_index + 1];
+  for (size_t q = 0; q < nq; ++q) start[q + 1] += start[q];
+  std::vector<int32_t> flat(start[nq]);
+  std::vector<int32_t> fill(start.begin(), start.end() - 1);
+  for (auto* items : {&plan->valu, &plan->mfma}) {
+    for (WorkItem& it : *items) {
+      if (direct(it)) {
         it.part_base = -1;
         continue;
       }
       it.part_base = static_cast<int32_t>(plan->partial_rows);
       plan->partial_rows += static_cast<int64_t>(it.n_grp) * hq;
       for (int32_t u = 0; u < it.n_grp; ++u)
-        parts_of[plan->groups[it.grp_off + u].q_index].push_back(it.part_base + u * hq);
+        flat[fill[plan->groups[it.grp_off + u].q_index]++] = it.part_base + u * hq;
     }
-  };
-  assign(plan->valu);
-  assign(plan->mfma);
+  }
   for (const WorkItem& it : plan->valu) plan->valu_max_rows = std::max(plan->valu_max_rows, it.n_grp);
-  std::vector<int32_t> merge_of(n_parts.size(), -1);
-  for (size_t q = 0; q < parts_of.size(); ++q) {
+  std::vector<int32_t> merge_of(nq, -1);
+  for (size_t q = 0; q < nq; ++q) {
     if (n_parts[q] <= 1) continue;
     merge_of[q] = static_cast<int32_t>(plan->merges.size());
     MergeRow m{};
     m.q_index = static_cast<int32_t>(q);
-    m.n_parts = static_cast<int32_t>(parts_of[q].size());
+    m.n_parts = start[q + 1] - start[q];
     m.parts_off = static_cast<int32_t>(plan->parts.size());
     if (m.n_parts <= kMergeInline)
-      std::copy(parts_of[q].begin(), parts_of[q].end(), m.inl);
+      std::copy(flat.begin() + start[q], flat.begin() + start[q + 1], m.inl);
     else
-      plan->parts.insert(plan->parts.end(), parts_of[q].begin(), parts_of[q].end());
+      plan->parts.insert(plan->parts.end(), flat.begin() + start[q], flat.begin() + start[q + 1]);
     plan->merges.push_back(m);
   }
   for (RowGroup& g : plan->groups) g.merge = merge_of[g.q_index];
@@ -112,7 +122,7 @@ bool ancestor_masks(const int32_t* parent, int32_t n_nodes, uint64_t* anc) {
 
 Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
                 const PlanConfig& cfg, Plan* plan, std::string* why) {
-  *plan = Plan{};
+  plan->reset();
   const Shape& sh = pool.shape();
   const int32_t B = sh.block_size;
   const int32_t G = sh.num_q_heads / sh.num_kv_heads;
@@ -264,7 +274,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
 Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
                 int32_t n_nodes, const int32_t* parent, const PlanConfig& cfg,
                 Plan* plan, std::string* why) {
-  *plan = Plan{};
+  plan->reset();
   const Shape& sh = pool.shape();
   const int32_t B = sh.block_size;
   const int32_t G = sh.num_q_heads / sh.num_kv_heads;

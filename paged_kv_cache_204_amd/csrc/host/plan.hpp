@@ -62,6 +62,25 @@ struct Plan {
   int64_t logical_tokens = 0;
   int32_t unique_blocks = 0;
   int32_t segments = 0;
+
+  // Empties the plan for reuse; the vectors keep their capacity, so
+  // repeated planning of similar calls does not allocate.
+  void reset() {
+    valu.clear();
+    mfma.clear();
+    groups.clear();
+    blocks.clear();
+    merges.clear();
+    parts.clear();
+    item_blocks.clear();
+    stride_mfma = stride_valu = 0;
+    partial_rows = 0;
+    mfma_row_tiles = 1;
+    mfma_waves = 4;
+    valu_max_rows = 0;
+    unique_tokens = logical_tokens = 0;
+    unique_blocks = segments = 0;
+  }
 };
 
 Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
