@@ -155,6 +155,39 @@ def test_shape_edges(dev, shape, label):
     parity(tree)
 
 
+# Planner settings (read from the environment when a pool is created) pick
+# different kernel variants for the same call: four- or eight-wave MFMA
+# workgroups, one or two row tiles per wave, few or many key chunks, the
+# VALU path for everything it can take.  Every setting must keep parity.
+KNOBS = [
+    {"PKV_MFMA_WAVES": "4", "PKV_MFMA_ROW_TILES": "2"},
+    {"PKV_MFMA_WAVES": "8", "PKV_MFMA_ROW_TILES": "2"},
+    {"PKV_MFMA_ROW_TILES": "1"},
+    {"PKV_TARGET_MFMA_WGS": "16", "PKV_TARGET_WGS": "16"},
+    {"PKV_TARGET_MFMA_WGS": "4096", "PKV_TARGET_WGS": "4096", "PKV_MAX_CHUNK": "64"},
+    {"PKV_MFMA_MIN_ROWS": "0"},
+]
+
+
+@pytest.mark.parametrize("knobs", KNOBS, ids=["-".join(f"{k[4:].lower()}{v}" for k, v in kn.items())
+                                              for kn in KNOBS])
+def test_planner_settings_keep_parity(dev, knobs, monkeypatch):
+    for k, v in knobs.items():
+        monkeypatch.setenv(k, v)
+    tag = "-".join(f"{k[4:].lower()}{v}" for k, v in knobs.items())
+    # 64 nodes x G 4 = 256 rows per sequence: eight-wave tiles are possible
+    parity(synth.verify_workload(f"knob_verify_{tag}", 60, Shape(32, 8, 128, 16, 1, 128), n_seqs=2,
+                                 ctx_len=301, n_nodes=64, tree_depth=6), check_pool=False)
+    # G 16 (MFMA only) with 16 branches over one prefix: a 256-row shared tile
+    parity(synth.fork_workload(f"knob_fork_{tag}", 61, Shape(16, 1, 128, 16, 1, 256),
+                               prefix_len=203, n_branches=16, branch_len=29, decode_steps=2,
+                               permute=True), check_pool=False)
+    # G 4 decode with a prefix shared by 3 branches: VALU and MFMA items mixed
+    parity(synth.fork_workload(f"knob_mixed_{tag}", 62, Shape(32, 8, 64, 16, 1, 256),
+                               prefix_len=260, n_branches=12, branch_len=41, decode_steps=2),
+           check_pool=False)
+
+
 # ------------------------------------------------------- full-size workloads
 
 def sample_ops(wl, every):
