@@ -218,6 +218,7 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
   ap.Hq = sh.num_q_heads;
   ap.Hkv = sh.num_kv_heads;
   ap.G = sh.num_q_heads / sh.num_kv_heads;
+  ap.g_magic = static_cast<uint32_t>((65536 + ap.G - 1) / ap.G);
   ap.B = sh.block_size;
   ap.log2B = p->core.log2_block();
   ap.scale_log2 = sm_scale * pkv::kLog2eHost;

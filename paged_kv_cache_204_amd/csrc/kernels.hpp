@@ -41,6 +41,7 @@ struct AttnParams {
   int32_t n_mfma;
   int32_t stride_mfma, stride_valu;   // block-list stride of each item kind
   int32_t layer, N, Hq, Hkv, G, B, log2B;
+  uint32_t g_magic;        // ceil(2^16 / G): r / G == (r * g_magic) >> 16 for r < 1024
   float scale_log2;        // sm_scale * log2(e)
 };
 

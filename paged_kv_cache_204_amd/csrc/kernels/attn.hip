@@ -49,6 +49,19 @@ __device__ __forceinline__ uint32_t chunk_index(int32_t blk, uint32_t blk_chunks
   return __umul24(static_cast<uint32_t>(blk), blk_chunks) + static_cast<uint32_t>(within);
 }
 
+// Row r of an item belongs to row group r / G (query head r % G of the kv
+// head's group).  G is a run-time value of at most 16 and r stays below
+// 1024, so r * ceil(2^16 / G) >> 16 is exactly r / G (the rounding of the
+// multiplier adds less than 1/64 to a quotient whose fraction is at most
+// 15/16), one multiply instead of an integer division sequence.
+struct RowOf {
+  int grp, head;
+};
+__device__ __forceinline__ RowOf row_of(const AttnParams& p, int r) {
+  const int grp = static_cast<int>((static_cast<uint32_t>(r) * p.g_magic) >> 16);
+  return {grp, r - grp * p.G};
+}
+
 // ---------------------------------------------------------------- MFMA path
 constexpr int kStep = 32;          // key tokens per step (two 16-token tiles)
 constexpr int kDepth = 2;          // steps of K/V requested ahead
@@ -99,8 +112,9 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) qf[rt][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
     if (row_ok[rt]) {
-      const RowGroup g = p.groups[it.grp_off + r / G];
-      const int hq = h * G + r % G;
+      const RowOf ro = row_of(p, r);
+      const RowGroup g = p.groups[it.grp_off + ro.grp];
+      const int hq = h * G + ro.head;
       const uint16_t* qrow = p.q + (static_cast<size_t>(g.q_index) * p.Hq + hq) * D;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
@@ -108,7 +122,7 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
       anc[rt] = (static_cast<uint64_t>(g.anc_hi) << 32) | g.anc_lo;
       dst_row[rt] = it.part_base < 0
                         ? static_cast<size_t>(g.q_index) * p.Hq + hq
-                        : static_cast<size_t>(it.part_base) + static_cast<size_t>(r / G) * p.Hq + hq;
+                        : static_cast<size_t>(it.part_base) + static_cast<size_t>(ro.grp) * p.Hq + hq;
     }
   }
   const bool active = wave * RT * 16 < R;
@@ -384,13 +398,14 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
   for (int r = 0; r < RM; ++r) {
     qv[r] = make_uint4(0, 0, 0, 0);
     if (r < R) {
-      const size_t qoff = (static_cast<size_t>(qidx[r / G]) * p.Hq + h * G + r % G) * D + c * 8;
+      const RowOf ro = row_of(p, r);
+      const size_t qoff = (static_cast<size_t>(qidx[ro.grp]) * p.Hq + h * G + ro.head) * D + c * 8;
       qv[r] = *reinterpret_cast<const uint4*>(p.q + qoff);
     }
   }
   uint64_t anc_mine = 0;
   if (c < R) {
-    const RowGroup g = p.groups[it.grp_off + c / G];
+    const RowGroup g = p.groups[it.grp_off + row_of(p, c).grp];
     anc_mine = (static_cast<uint64_t>(g.anc_hi) << 32) | g.anc_lo;
   }
 
@@ -420,25 +435,37 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
   if (r0 >= R) return;   // no workgroup barrier follows
 
   // ---- phase 2: exact softmax of this wave's rows --------------------------
+  // The wave's rows go through together (their reductions interleave); a
+  // row past R (odd G only) computes on unused LDS and is never stored.
   float m_row[RW], l_row[RW];
+  {
+    float mx[RW], sum[RW];
 #pragma unroll
-  for (int j = 0; j < RW; ++j) {
-    m_row[j] = -INFINITY;
-    l_row[j] = 0.f;
-    const int r = r0 + j;
-    if (r >= R) continue;
-    float mx = -INFINITY;
-    for (int t = lane; t < it.n_tok; t += 64) mx = fmaxf(mx, sm.s[t][r]);
-    mx = wave_max(mx);
-    const float m_use = (mx == -INFINITY) ? 0.f : mx;
-    float sum = 0.f;
+    for (int j = 0; j < RW; ++j) mx[j] = -INFINITY;
     for (int t = lane; t < it.n_tok; t += 64) {
-      const float e = fast_exp2(sm.s[t][r] - m_use);
-      sm.s[t][r] = e;
-      sum += e;
+#pragma unroll
+      for (int j = 0; j < RW; ++j) mx[j] = fmaxf(mx[j], sm.s[t][r0 + j]);
     }
-    m_row[j] = mx;
-    l_row[j] = wave_sum(sum);
+    float m_use[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      mx[j] = wave_max(mx[j]);
+      m_use[j] = (mx[j] == -INFINITY) ? 0.f : mx[j];
+      sum[j] = 0.f;
+    }
+    for (int t = lane; t < it.n_tok; t += 64) {
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const float e = fast_exp2(sm.s[t][r0 + j] - m_use[j]);
+        sm.s[t][r0 + j] = e;
+        sum[j] += e;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      m_row[j] = mx[j];
+      l_row[j] = wave_sum(sum[j]);
+    }
   }
   wave_lds_sync();
 
@@ -495,16 +522,17 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
     const float l = l_row[j];
     const float m = m_row[j];
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int hq = h * G + r % G;
+    const RowOf ro = row_of(p, r);
+    const int hq = h * G + ro.head;
     const float4 lo = make_float4(o[j][0] * inv, o[j][1] * inv, o[j][2] * inv, o[j][3] * inv);
     const float4 hi = make_float4(o[j][4] * inv, o[j][5] * inv, o[j][6] * inv, o[j][7] * inv);
     float* dst;
     if (it.part_base < 0) {
-      const size_t row = static_cast<size_t>(qidx[r / G]) * p.Hq + hq;
+      const size_t row = static_cast<size_t>(qidx[ro.grp]) * p.Hq + hq;
       dst = p.out + row * D + c * 8;
       if (p.lse && c == 0) p.lse[row] = (m + log2f(l)) * kLn2;
     } else {
-      const size_t row = static_cast<size_t>(it.part_base) + static_cast<size_t>(r / G) * p.Hq + hq;
+      const size_t row = static_cast<size_t>(it.part_base) + static_cast<size_t>(ro.grp) * p.Hq + hq;
       dst = p.part_o + row * D + c * 8;
       if (c == 0) p.part_lse[row] = l > 0.f ? m + log2f(l) : -INFINITY;
     }
