@@ -184,6 +184,20 @@ pkv_status take_event(pkv_pool* p, hipEvent_t* ev) {
   return PKV_OK;
 }
 
+// Every item must fit the tiles its kernel path assumes (LDS arrays, rows
+// per workgroup); the planner guarantees it, this re-checks before launch.
+bool plan_fits_kernels(const pkv::Plan& plan, const pkv::Shape& sh) {
+  const int32_t G = sh.num_q_heads / sh.num_kv_heads;
+  const int32_t mrows = pkv::mfma_item_rows(plan.mfma_row_tiles, plan.mfma_waves);
+  if (plan.mfma_waves == 8 && !plan.valu.empty()) return false;
+  for (const pkv::WorkItem& it : plan.valu)
+    if (it.n_tok < 1 || it.n_tok > pkv::kValuMaxTokens || it.n_grp < 1 || it.n_grp * G > pkv::kValuMaxRows)
+      return false;
+  for (const pkv::WorkItem& it : plan.mfma)
+    if (it.n_tok < 1 || it.n_grp < 1 || it.n_grp * G > mrows) return false;
+  return true;
+}
+
 // The attention kernel of one call and, when some queries have several
 // partial states, the merge kernel.  With timing enabled, a pair of events
 // brackets the attention kernel alone.
@@ -449,6 +463,8 @@ pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, in
     std::string why;
     pkv::Err e = pkv::plan_decode(p->core, seqs, n_seqs, p->cfg, &p->dplan, &why);
     if (e != pkv::Err::ok) return fail(to_status(e), why);
+    if (!plan_fits_kernels(p->dplan, p->core.shape()))
+      return fail(PKV_ERR_ARG, "paged_attn_decode: internal plan exceeds the kernels' tile limits");
     p->dlayout = layout_of(p->dplan);
     pkv_status s = upload(p, p->decode_plan, p->dlayout.total, st,
                           [&](char* dst) { serialize(p->dplan, p->dlayout, dst); });
@@ -479,6 +495,8 @@ pkv_status paged_attn_tree_verify(pkv_pool* p, int32_t layer, const int64_t* seq
   DeviceGuard g(p->dev);
   PKV_HIP(g.err);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!plan_fits_kernels(p->vplan, p->core.shape()))
+    return fail(PKV_ERR_ARG, "paged_attn_tree_verify: internal plan exceeds the kernels' tile limits");
   p->vlayout = layout_of(p->vplan);
   pkv_status s = upload(p, p->verify_plan, p->vlayout.total, st,
                         [&](char* dst) { serialize(p->vplan, p->vlayout, dst); });

@@ -26,6 +26,8 @@ struct AppendParams {
 // One attention launch over a list of work items (kv head = blockIdx.y):
 // items [0, n_mfma) take the MFMA path, the rest the VALU path.
 constexpr int kMaxItemBlocks = 512;   // block ids of one work item (LDS staging)
+constexpr int kValuMaxRows = 8;       // query rows of one VALU work item
+constexpr int kValuMaxTokens = 512;   // key tokens of one VALU work item (LDS scores)
 
 struct AttnParams {
   const WorkItem* items;

@@ -316,8 +316,8 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
 }
 
 // ---------------------------------------------------------------- VALU path
-constexpr int kValuRows = 8;     // query rows per item at most
-constexpr int kValuTok = 512;    // key tokens per item
+constexpr int kValuRows = kValuMaxRows;
+constexpr int kValuTok = kValuMaxTokens;
 constexpr int kUnroll = 4;       // K token passes with loads in flight
 constexpr int kUnrollV = 8;      // V tokens in flight per lane
 
