@@ -281,6 +281,8 @@ void apply_env(pkv::PlanConfig* c) {
   get("PKV_MFMA_MIN_ROWS", &c->mfma_min_rows, 0, 1 << 20);
   get("PKV_MFMA_ROW_TILES", &c->mfma_row_tiles, 0, 2);
   get("PKV_MFMA_WAVES", &c->mfma_waves, 0, 8);
+  get("PKV_UNSHARE_MAX_QUERIES", &c->unshare_max_queries, 0, 1 << 20);
+  get("PKV_UNSHARE_MAX_TOKENS", &c->unshare_max_tokens, 0, 1 << 20);
   get("PKV_TARGET_WGS", &c->target_wgs, 1, 1 << 20);
   get("PKV_TARGET_MFMA_WGS", &c->target_mfma_wgs, 1, 1 << 20);
   get("PKV_MAX_CHUNK", &c->max_chunk, 64, 1 << 20);

@@ -145,15 +145,26 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   };
 
   // ---- trie over block ids, compressed into segments ----
+  // A trie node owns the block run [own, e) that its queries share.  A
+  // small node (few queries, few tokens, every query continuing below it,
+  // not dense enough for the MFMA path) is not made a segment of its own:
+  // its run is handed down, so each child's segment starts at the node's
+  // start (pos < own) and the run is read once per child instead of costing
+  // every query an extra partial state and merge part.
   std::vector<Segment> segs;
   struct Frame {
     std::vector<int32_t> qs;
-    int32_t pos;
+    int32_t pos;   // first block of the segment this frame emits
+    int32_t own;   // first block of the run this frame's queries share
+  };
+  auto dense = [&](size_t nq) {
+    return G > cfg.valu_rows ||
+           (cfg.mfma_min_rows > 0 && static_cast<int64_t>(nq) * G >= cfg.mfma_min_rows);
   };
   std::vector<Frame> stack;
   if (n_seqs > 0) {
     Frame root;
-    root.pos = 0;
+    root.pos = root.own = 0;
     for (int32_t i = 0; i < n_seqs; ++i) root.qs.push_back(i);
     stack.push_back(std::move(root));
   }
@@ -161,7 +172,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     Frame f = std::move(stack.back());
     stack.pop_back();
     const std::vector<int32_t>& t0 = st[f.qs[0]]->table;
-    int32_t e = f.pos;
+    int32_t e = f.own;
     for (;;) {
       bool same = true;
       for (int32_t q : f.qs)
@@ -172,18 +183,28 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
       if (!same) break;
       ++e;
     }
-    if (e > f.pos) {
-      Segment s;
-      s.queries = f.qs;
-      s.blocks = t0.data() + f.pos;
-      s.nblk = e - f.pos;
-      s.ntok = (s.nblk - 1) * B + fill(f.qs[0], e - 1);
+    bool hand_down = false;
+    if (e > f.own) {
       for (int32_t q : f.qs)
         if (fill(q, e - 1) != fill(f.qs[0], e - 1)) {
           *why = "paged_attn_decode: a shared block has different fills (pool invariant broken)";
           return Err::arg;
         }
-      segs.push_back(std::move(s));
+      plan->unique_blocks += e - f.own;
+      plan->unique_tokens += static_cast<int64_t>(e - f.own - 1) * B + fill(f.qs[0], e - 1);
+      bool all_continue = true;
+      for (int32_t q : f.qs) all_continue = all_continue && nblk(q) > e;
+      hand_down = all_continue && !dense(f.qs.size()) &&
+                  static_cast<int32_t>(f.qs.size()) <= cfg.unshare_max_queries &&
+                  static_cast<int64_t>(e - f.pos) * B <= cfg.unshare_max_tokens;
+      if (!hand_down) {
+        Segment sg;
+        sg.queries = f.qs;
+        sg.blocks = t0.data() + f.pos;
+        sg.nblk = e - f.pos;
+        sg.ntok = (sg.nblk - 1) * B + fill(f.qs[0], e - 1);
+        segs.push_back(std::move(sg));
+      }
     }
     // children keyed by the next block id, in first-appearance order
     std::vector<Frame> kids;
@@ -194,7 +215,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
       auto it = index.find(b);
       if (it == index.end()) {
         index.emplace(b, kids.size());
-        kids.push_back(Frame{{q}, e});
+        kids.push_back(Frame{{q}, hand_down || e == f.own ? f.pos : e, e});
       } else {
         kids[it->second].qs.push_back(q);
       }
@@ -226,8 +247,6 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   const int64_t cap_v = std::min<int64_t>(cap, cfg.valu_max_tokens);
   int64_t work_v = 0, work_m = 0;
   for (const Segment& s : segs) {
-    plan->unique_tokens += s.ntok;
-    plan->unique_blocks += s.nblk;
     const bool m = is_mfma(s);
     const int64_t per = std::max(1, (m ? mrows : cfg.valu_rows) / G);
     (m ? work_m : work_v) += static_cast<int64_t>(s.ntok) * ceil_div(static_cast<int64_t>(s.queries.size()), per);

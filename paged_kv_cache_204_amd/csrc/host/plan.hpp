@@ -36,6 +36,9 @@ struct PlanConfig {
                                  // when a single query's GQA group exceeds valu_rows
   int32_t target_wgs = 256;      // VALU workgroups to aim for over all kv heads
   int32_t target_mfma_wgs = 512; // MFMA workgroups to aim for over all kv heads
+  int32_t unshare_max_queries = 4;   // a shared run of at most this many queries ...
+  int32_t unshare_max_tokens = 256;  // ... and tokens, too sparse for the MFMA path,
+                                     // is read by each query's own item instead
   int32_t tile = 64;             // key tokens per kernel tile; chunks are multiples
   int32_t max_chunk = 4096;      // key tokens per work item at most
   int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)

@@ -166,6 +166,8 @@ KNOBS = [
     {"PKV_TARGET_MFMA_WGS": "16", "PKV_TARGET_WGS": "16"},
     {"PKV_TARGET_MFMA_WGS": "4096", "PKV_TARGET_WGS": "4096", "PKV_MAX_CHUNK": "64"},
     {"PKV_MFMA_MIN_ROWS": "0"},
+    {"PKV_UNSHARE_MAX_QUERIES": "0"},
+    {"PKV_UNSHARE_MAX_QUERIES": "64", "PKV_UNSHARE_MAX_TOKENS": "100000"},
 ]
 
 

@@ -347,3 +347,37 @@ def test_timing_sampling_period_is_validated():
         pkv.kv_pool_destroy(pool)
     lib = pkv.load()
     assert lib.pkv_timing_enable(None, 1) == pkv.PKV_ERR_ARG
+
+
+def test_small_shared_runs_are_handed_down(monkeypatch):
+    """A run shared by a few queries (too sparse for the MFMA path) is read by
+    each query's own work item instead of being a segment of its own: fewer
+    segments and items, the same unique and logical token counts."""
+    wl = synth.named("c4_mcts")
+
+    def stats(unshare):
+        monkeypatch.setenv("PKV_UNSHARE_MAX_QUERIES", str(unshare))
+        s = wl.shape
+        desc = dict(num_blocks=s.num_blocks, block_size=s.block_size, num_layers=s.num_layers,
+                    num_q_heads=s.num_q_heads, num_kv_heads=s.num_kv_heads, head_dim=s.head_dim)
+        pool = pkv.kv_pool_create(desc, None, None, free_order=wl.free_order())
+        try:
+            hs = {}
+            for op in wl.ops:
+                if op[0] == "alloc":
+                    hs[op[1]] = pkv.seq_allocate(pool)
+                elif op[0] == "fork":
+                    hs[op[2]] = pkv.seq_fork(pool, hs[op[1]])
+                elif op[0] == "append":
+                    pkv.kv_append(pool, [hs[h] for h in op[1]], op[2], None, None, None)
+                elif op[0] == "decode":
+                    return pkv.paged_attn_decode_plan_stats(pool, [hs[h] for h in op[1]])
+        finally:
+            pkv.kv_pool_destroy(pool)
+
+    shared, handed = stats(0), stats(4)
+    for k in ("unique_tokens", "unique_blocks", "logical_tokens", "merged_rows"):
+        assert shared[k] == handed[k], k
+    # the level-3 edges (4 leaves, 64 tokens) are handed to the leaves
+    assert shared["segments"] - handed["segments"] == 64
+    assert handed["work_items"] < shared["work_items"]
