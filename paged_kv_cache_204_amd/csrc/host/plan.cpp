@@ -42,6 +42,10 @@ int32_t pick_waves(const PlanConfig& cfg, bool any_valu, int32_t row_tiles, int6
 // vector of row group g; items that do not cover all keys of their queries
 // get partial rows, and every such query gets a merge row.
 void finish_parts(Plan* plan, const std::vector<int32_t>& n_parts, int32_t hq) {
+  // longest items first within each kind: the kernel starts them first
+  auto longer = [](const WorkItem& a, const WorkItem& b) { return a.n_tok > b.n_tok; };
+  std::stable_sort(plan->mfma.begin(), plan->mfma.end(), longer);
+  std::stable_sort(plan->valu.begin(), plan->valu.end(), longer);
   const size_t nq = n_parts.size();
   // partial rows of every query as one flat list (count, prefix sums, fill):
   // no allocation per query

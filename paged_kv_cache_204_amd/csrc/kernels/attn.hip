@@ -1,13 +1,14 @@
 // Paged attention over the block pool: one launch per call.
 //
-// Each workgroup (256 threads, blockIdx.y = kv head) runs one work item from
-// the plan -- a run of key tokens reached through the block table and up to
+// Each workgroup (256 or 512 threads) runs one work item of the plan for one
+// kv head -- a run of key tokens reached through the block table and up to
 // a tile of query rows (row groups x the G query heads of this kv head):
 //
-//  * MFMA items (blockIdx.x < n_mfma): the query tile is a real dense
+//  * MFMA items (the first n_mfma): the query tile is a real dense
 //    contraction -- every node of a draft tree (CAST page, technical
 //    summary "Problem": the target checks the whole tree in one pass) or a
-//    shared prefix under many queries.  4 waves x RT row tiles of 16 rows.
+//    shared prefix under many queries.  W (4 or 8) waves x RT row tiles of
+//    16 rows.
 //  * VALU items: one decode query's GQA group (or two); up to 8 rows.
 //
 // Decode is bound by memory bandwidth (SGLang RadixAttention page, section on
@@ -318,12 +319,14 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
 // ---------------------------------------------------------------- VALU path
 constexpr int kValuRows = kValuMaxRows;
 constexpr int kValuTok = kValuMaxTokens;
-constexpr int kUnroll = 4;       // K token passes with loads in flight
-constexpr int kUnrollV = 8;      // V tokens in flight per lane
+constexpr int kTokPerRound = 128;  // K tokens with loads in flight per workgroup
+constexpr int kUnrollV = 8;        // V tokens in flight per lane
 
 template <int D>
 struct alignas(16) ValuSmem {
   float s[kValuTok][kValuRows];   // scores, then probabilities, token-major
+  float red[kThreads / 64][4][D]; // per-wave P V sums (one-row-per-wave items)
+  float m[kValuRows], l[kValuRows];
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -344,6 +347,94 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// Phase 3 for items of one row per wave (RM = 4): the waves split the
+// tokens, each lane accumulates all rows for its 8 dims, a butterfly over
+// the token slots and a sum over the waves through LDS give O.
+template <int D, int RM, class Addr, class VTok>
+__device__ __forceinline__ void valu_pv_split(const AttnParams& p, const WorkItem& it, int h,
+                                              ValuSmem<D>& sm, uint4 (&vv)[kUnrollV], const uint4* vb,
+                                              Addr addr, VTok vtok, int nv, const int32_t* qidx) {
+  constexpr int CPR = D / 8;
+  static_assert(RM == 4, "one row per wave");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = tid % CPR;
+  const int ts = lane / CPR;
+  const int t_last = it.n_tok - 1;
+  const int R = it.n_grp * p.G;
+  float o[RM][8];
+#pragma unroll
+  for (int r = 0; r < RM; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+  for (int k0 = 0; k0 < nv; k0 += kUnrollV) {
+    if (k0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kUnrollV; ++u) vv[u] = vb[addr(vtok(k0 + u))];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnrollV; ++u) {
+      const int t = vtok(k0 + u);
+      float4 pr = *reinterpret_cast<const float4*>(&sm.s[min(t, t_last)][0]);
+      if (t > t_last) pr = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float pa[4] = {pr.x, pr.y, pr.z, pr.w};
+      const float v[8] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y), bf16_hi(vv[u].y),
+                          bf16_lo(vv[u].z), bf16_hi(vv[u].z), bf16_lo(vv[u].w), bf16_hi(vv[u].w)};
+#pragma unroll
+      for (int r = 0; r < RM; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[r][e] = fmaf(pa[r], v[e], o[r][e]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = o[r][e];
+      if constexpr (CPR == 8) x += dpp_f32<kDppXor8>(x);
+      o[r][e] = xor32_sum(xor16_sum(x));
+    }
+  }
+  if (ts == 0) {
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      *reinterpret_cast<float4*>(&sm.red[wave][r][c * 8]) = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
+      *reinterpret_cast<float4*>(&sm.red[wave][r][c * 8 + 4]) = make_float4(o[r][4], o[r][5], o[r][6], o[r][7]);
+    }
+  }
+  lds_barrier();
+  constexpr int kQuads = D / 4;
+  for (int e = tid; e < R * kQuads; e += kThreads) {
+    const int r = e / kQuads;
+    const int d = (e % kQuads) * 4;
+    float4 acc = *reinterpret_cast<const float4*>(&sm.red[0][r][d]);
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) {
+      const float4 x = *reinterpret_cast<const float4*>(&sm.red[w][r][d]);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    const float l = sm.l[r];
+    const float m = sm.m[r];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const RowOf ro = row_of(p, r);
+    const int hq = h * p.G + ro.head;
+    const float4 val = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (it.part_base < 0) {
+      const size_t row = static_cast<size_t>(qidx[ro.grp]) * p.Hq + hq;
+      *reinterpret_cast<float4*>(p.out + row * D + d) = val;
+      if (p.lse && d == 0) p.lse[row] = (m + log2f(l)) * kLn2;
+    } else {
+      const size_t row = static_cast<size_t>(it.part_base) + static_cast<size_t>(ro.grp) * p.Hq + hq;
+      *reinterpret_cast<float4*>(p.part_o + row * D + d) = val;
+      if (d == 0) p.part_lse[row] = l > 0.f ? m + log2f(l) : -INFINITY;
+    }
+  }
+}
+
 // Phase 1 (whole workgroup): a token's head_dim row is read by D/8 lanes
 // with 128-bit loads (the row is one coalesced burst); each lane forms the
 // partial dot products of every row over its 8 dims (v_dot2_f32_bf16), a
@@ -356,12 +447,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 // sums O.  RM (4 or 8) bounds the rows at compile time; rows >= R are never
 // written.
 template <int D, int RM>
-__device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& it, int h,
+__device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& it, int item, int h,
                                           ValuSmem<D>& sm, const int32_t* blk_s) {
   constexpr int CPR = D / 8;        // 16-byte chunks per row
   constexpr int TPP = kThreads / CPR;
   constexpr int TS = 64 / CPR;      // token slots of a wave in phase 3
-  constexpr int RW = RM / 4;        // rows per wave in phases 2-3
+  constexpr int RW = RM / 4;        // rows per wave in phase 2 (and phase 3 when 2)
+  constexpr int kUnroll = kTokPerRound / TPP;   // K passes with loads in flight
   static_assert(RM <= CPR, "one score row per lane of a token group");
   static_assert(RW == 1 || RW == 2, "one or two rows per wave");
   const int G = p.G;
@@ -374,7 +466,7 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
   const int ts = lane / CPR;
   const int r0 = wave * RW;
   // read from the item in memory (uniform loads), not from its register copy
-  const int32_t* qidx = p.items[blockIdx.x].q_index;
+  const int32_t* qidx = p.items[item].q_index;
 
   const uint4* kb = layer_head_base(p, p.k_pool, h, D);
   const uint4* vb = layer_head_base(p, p.v_pool, h, D);
@@ -385,14 +477,18 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
     return chunk_index(blk_s[t >> p.log2B], blk_chunks, (t & (p.B - 1)) * (D / 8) + c);
   };
   const int npass = (it.n_tok + TPP - 1) / TPP;
-  const int nv = (it.n_tok + TS - 1) / TS;   // phase-3 tokens per lane
+  // Phase-3 token k of a lane: with two rows per wave every wave walks all
+  // tokens (slot ts of each TS); with one row per wave the waves split the
+  // tokens (wave w takes every fourth group of TS) and sum through LDS.
+  auto vtok = [&](int k) { return RW == 2 ? ts + TS * k : ts + TS * (wave + 4 * k); };
+  const int nv = RW == 2 ? (it.n_tok + TS - 1) / TS : (it.n_tok + 4 * TS - 1) / (4 * TS);
 
   // first K passes, first V tokens of this lane, then the queries
   uint4 kv[kUnroll], vv[kUnrollV];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) kv[u] = kb[addr(u * TPP + tp)];
 #pragma unroll
-  for (int u = 0; u < kUnrollV; ++u) vv[u] = vb[addr(ts + TS * u)];
+  for (int u = 0; u < kUnrollV; ++u) vv[u] = vb[addr(vtok(u))];
   uint4 qv[RM];
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
@@ -432,7 +528,7 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
     }
   }
   lds_barrier();
-  if (r0 >= R) return;   // no workgroup barrier follows
+  if (RW == 2 && r0 >= R) return;   // no workgroup barrier follows on this path
 
   // ---- phase 2: exact softmax of this wave's rows --------------------------
   // The wave's rows go through together (their reductions interleave); a
@@ -467,6 +563,16 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
       l_row[j] = wave_sum(sum[j]);
     }
   }
+  if constexpr (RW == 1) {
+    // phase 3 reads every row's P and the final step every row's m, l
+    if (lane == 0) {
+      sm.m[r0] = m_row[0];
+      sm.l[r0] = l_row[0];
+    }
+    lds_barrier();
+    valu_pv_split<D, RM>(p, it, h, sm, vv, vb, addr, vtok, nv, qidx);
+    return;
+  }
   wave_lds_sync();
 
   // ---- phase 3: O = P V for this wave's rows --------------------------------
@@ -478,11 +584,11 @@ __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& i
   for (int k0 = 0; k0 < nv; k0 += kUnrollV) {
     if (k0 > 0) {
 #pragma unroll
-      for (int u = 0; u < kUnrollV; ++u) vv[u] = vb[addr(ts + TS * (k0 + u))];
+      for (int u = 0; u < kUnrollV; ++u) vv[u] = vb[addr(vtok(k0 + u))];
     }
 #pragma unroll
     for (int u = 0; u < kUnrollV; ++u) {
-      const int t = ts + TS * (k0 + u);
+      const int t = vtok(k0 + u);
       const int tc = min(t, t_last);
       float pr[RW];
       if constexpr (RW == 2) {
@@ -565,22 +671,28 @@ __global__ __launch_bounds__(64 * W) void attn_kernel(const WorkItem* __restrict
   } sm;
   __shared__ int32_t blk_s[kMaxItemBlocks];
 
+  // Workgroup -> (item, kv head): the MFMA items of every head first, item
+  // by item (the planner sorts each kind longest first), then the VALU
+  // items, so the long items start early and the short ones fill in.
+  const int L = static_cast<int>(blockIdx.x);
+  const bool is_mfma = L < p.n_mfma * p.Hkv;
+  const int wi = is_mfma ? L : L - p.n_mfma * p.Hkv;
+  const int h = wi % p.Hkv;
+  const int item = (is_mfma ? 0 : p.n_mfma) + wi / p.Hkv;
   // the block list sits at a stride fixed per item kind, so its loads go
   // out together with the item's
-  const bool is_mfma = static_cast<int>(blockIdx.x) < p.n_mfma;
   const int nb = is_mfma ? p.stride_mfma : p.stride_valu;
-  const int32_t* lst = p.blocks + (is_mfma ? static_cast<size_t>(blockIdx.x) * p.stride_mfma
+  const int32_t* lst = p.blocks + (is_mfma ? static_cast<size_t>(item) * p.stride_mfma
                                            : static_cast<size_t>(p.n_mfma) * p.stride_mfma +
-                                                 static_cast<size_t>(blockIdx.x - p.n_mfma) * p.stride_valu);
+                                                 static_cast<size_t>(item - p.n_mfma) * p.stride_valu);
   for (int i = threadIdx.x; i < nb; i += 64 * W) blk_s[i] = lst[i];
-  const WorkItem it = p.items[blockIdx.x];
-  const int h = blockIdx.y;
+  const WorkItem it = p.items[item];
   lds_barrier();
   if constexpr (W == 4) {
-    if (static_cast<int>(blockIdx.x) < p.n_mfma)
+    if (is_mfma)
       mfma_item<D, RT, 4>(p, it, h, sm.m, blk_s);
     else
-      valu_item<D, RM>(p, it, h, sm.v, blk_s);
+      valu_item<D, RM>(p, it, item, h, sm.v, blk_s);
   } else {
     // eight-wave workgroups serve launches whose items are all MFMA items
     mfma_item<D, RT, W>(p, it, h, sm.m, blk_s);
@@ -611,7 +723,9 @@ hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, i
                        int32_t valu_rows, int32_t waves, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   if (waves == 8 && n_items != p.n_mfma) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<uint32_t>(n_items), static_cast<uint32_t>(p.Hkv));
+  const int64_t n_wg = static_cast<int64_t>(n_items) * p.Hkv;
+  if (n_wg > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(n_wg));
   if (head_dim == 64 && row_tiles == 1) return launch_rows<64, 1>(p, grid, valu_rows, waves, s);
   if (head_dim == 64 && row_tiles == 2) return launch_rows<64, 2>(p, grid, valu_rows, waves, s);
   if (head_dim == 128 && row_tiles == 1) return launch_rows<128, 1>(p, grid, valu_rows, waves, s);

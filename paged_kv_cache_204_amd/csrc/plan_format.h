@@ -1,8 +1,8 @@
 // Work description that the host planner writes and the attention kernels
 // read.  Plain structs, identical layout on host and device.
 //
-// A work item is one workgroup's share of an attention call for one kv head
-// (the kv head is blockIdx.y):
+// A work item is an attention call's share for one workgroup per kv head
+// (the launch runs every item once for each kv head):
 //   - keys: n_tok tokens read through the item's block list (token t sits in
 //     block list[t / B] at slot t % B).  The device copy of the lists has a
 //     fixed stride per item kind (item_blocks below), so a workgroup finds
