@@ -23,7 +23,7 @@ struct AppendParams {
   int32_t L, N, Hkv, B, log2B, D;
 };
 
-// One attention launch over a list of work items (kv head = blockIdx.y):
+// One attention launch over a list of work items, each run once per kv head:
 // items [0, n_mfma) take the MFMA path, the rest the VALU path.
 constexpr int kMaxItemBlocks = 512;   // block ids of one work item (LDS staging)
 constexpr int kValuMaxRows = 8;       // query rows of one VALU work item

@@ -439,13 +439,17 @@ __device__ __forceinline__ void valu_pv_split(const AttnParams& p, const WorkIte
 // with 128-bit loads (the row is one coalesced burst); each lane forms the
 // partial dot products of every row over its 8 dims (v_dot2_f32_bf16), a
 // DPP butterfly over the token's lanes completes them, and the scores land
-// in LDS token-major.  One workgroup barrier.  Phases 2-3 (each wave alone,
+// in LDS token-major.  One workgroup barrier.  Phase 2 (each wave alone,
 // RM / 4 rows per wave): exact softmax of the wave's rows over the item's
-// keys, then O = P V with lane = (8-dim chunk, token slot): a lane reads the
-// V chunk of its tokens (requested before phase 1) and the wave's P pair of
-// each token with one 64-bit LDS read, and a butterfly over the token slots
-// sums O.  RM (4 or 8) bounds the rows at compile time; rows >= R are never
-// written.
+// keys.  Phase 3, O = P V with lane = (8-dim chunk, token slot), the V
+// chunks of a lane's first tokens requested before phase 1:
+//  * RM = 8 (two rows per wave): each wave walks all tokens for its own
+//    rows, reading the rows' P pair of a token with one 64-bit LDS read; a
+//    butterfly over the token slots sums O, with no further barrier;
+//  * RM = 4 (one row per wave): the waves split the tokens instead and
+//    every lane keeps all four rows (valu_pv_split), so each V row is
+//    loaded once per workgroup; O is summed over slots and waves.
+// RM bounds the rows at compile time; rows >= R are never written.
 template <int D, int RM>
 __device__ __forceinline__ void valu_item(const AttnParams& p, const WorkItem& it, int item, int h,
                                           ValuSmem<D>& sm, const int32_t* blk_s) {
