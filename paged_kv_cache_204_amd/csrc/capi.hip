@@ -6,6 +6,7 @@
 // buffers for plan uploads, and the kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -56,7 +57,7 @@ PlanLayout layout_of(const pkv::Plan& p) {
     field = at;
     at += align16(bytes);
   };
-  put(o.items, (p.mfma.size() + p.valu.size()) * sizeof(pkv::WorkItem));
+  put(o.items, (p.mfma.size() + p.valu.size() + p.direct.size()) * sizeof(pkv::WorkItem));
   put(o.groups, p.groups.size() * sizeof(pkv::RowGroup));
   put(o.blocks, p.item_blocks.size() * sizeof(int32_t));
   put(o.merges, p.merges.size() * sizeof(pkv::MergeRow));
@@ -72,6 +73,8 @@ void serialize(const pkv::Plan& p, const PlanLayout& o, char* dst) {
   // MFMA items first: the kernel picks its path by block index
   cp(o.items, p.mfma.data(), p.mfma.size() * sizeof(pkv::WorkItem));
   cp(o.items + p.mfma.size() * sizeof(pkv::WorkItem), p.valu.data(), p.valu.size() * sizeof(pkv::WorkItem));
+  cp(o.items + (p.mfma.size() + p.valu.size()) * sizeof(pkv::WorkItem), p.direct.data(),
+     p.direct.size() * sizeof(pkv::WorkItem));
   cp(o.groups, p.groups.data(), p.groups.size() * sizeof(pkv::RowGroup));
   cp(o.blocks, p.item_blocks.data(), p.item_blocks.size() * sizeof(int32_t));
   cp(o.merges, p.merges.data(), p.merges.size() * sizeof(pkv::MergeRow));
@@ -195,11 +198,17 @@ bool plan_fits_kernels(const pkv::Plan& plan, const pkv::Shape& sh) {
       return false;
   for (const pkv::WorkItem& it : plan.mfma)
     if (it.n_tok < 1 || it.n_grp < 1 || it.n_grp * G > mrows) return false;
+  if (!plan.direct.empty()) {
+    // a direct plan holds nothing else: the direct kernel numbers its items from 0
+    if (!plan.mfma.empty() || !plan.valu.empty() || !plan.merges.empty() || G > 16) return false;
+    for (const pkv::WorkItem& it : plan.direct)
+      if (it.n_tok < 1 || it.n_grp != 1 || it.tail_start != INT_MAX) return false;
+  }
   return true;
 }
 
-// The attention kernel of one call and, when some queries have several
-// partial states, the merge kernel.  With timing enabled, a pair of events
+// The attention kernel of one call (the direct kernel for direct plans)
+// and, when some queries have several partial states, the merge kernel.  With timing enabled, a pair of events
 // brackets the attention kernel alone.
 pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
                           const DevBuf& buf, int32_t layer, const void* q, float sm_scale,
@@ -211,7 +220,8 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
   float* part_o = static_cast<float*>(p->partials.ptr);
   float* part_lse = part_o + static_cast<size_t>(plan.partial_rows) * sh.head_dim;
 
-  if (plan.stride_mfma > pkv::kMaxItemBlocks || plan.stride_valu > pkv::kMaxItemBlocks)
+  if (plan.stride_mfma > pkv::kMaxItemBlocks || plan.stride_valu > pkv::kMaxItemBlocks ||
+      plan.stride_direct > pkv::kMaxItemBlocks)
     return fail(PKV_ERR_ARG, "attention: a work item spans more blocks than the kernels stage");
   pkv::AttnParams ap{};
   ap.items = reinterpret_cast<const pkv::WorkItem*>(base + lay.items);
@@ -245,8 +255,12 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
     if (s != PKV_OK) return s;
     PKV_HIP(hipEventRecord(ev_a, stream));
   }
-  PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles,
-                            plan.valu_max_rows * ap.G, plan.mfma_waves, stream));
+  if (plan.direct.empty())
+    PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles,
+                              plan.valu_max_rows * ap.G, plan.mfma_waves, stream));
+  else
+    PKV_HIP(pkv::launch_direct(ap, static_cast<int32_t>(plan.direct.size()), sh.head_dim,
+                                plan.stride_direct, stream));
   if (timed) {
     PKV_HIP(hipEventRecord(ev_b, stream));
     p->ev_pending.emplace_back(ev_a, ev_b);
@@ -270,7 +284,9 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15)
 
 // Planner knobs may be overridden from the environment for tuning sweeps:
 // PKV_MFMA_MIN_ROWS (0 turns the MFMA kernel off), PKV_MFMA_ROW_TILES (1|2),
-// PKV_TARGET_WGS, PKV_TARGET_MFMA_WGS, PKV_MAX_CHUNK.
+// PKV_MFMA_WAVES (4|8), PKV_UNSHARE_MAX_QUERIES, PKV_UNSHARE_MAX_TOKENS,
+// PKV_TARGET_WGS, PKV_TARGET_MFMA_WGS, PKV_MAX_CHUNK, PKV_DIRECT_MAX_TOKENS
+// and PKV_DIRECT_MAX_WGS (either 0 turns direct decode plans off).
 void apply_env(pkv::PlanConfig* c) {
   auto get = [](const char* name, int32_t* v, int32_t lo, int32_t hi) {
     const char* e = std::getenv(name);
@@ -286,6 +302,8 @@ void apply_env(pkv::PlanConfig* c) {
   get("PKV_TARGET_WGS", &c->target_wgs, 1, 1 << 20);
   get("PKV_TARGET_MFMA_WGS", &c->target_mfma_wgs, 1, 1 << 20);
   get("PKV_MAX_CHUNK", &c->max_chunk, 64, 1 << 20);
+  get("PKV_DIRECT_MAX_TOKENS", &c->direct_max_tokens, 0, 1 << 20);
+  get("PKV_DIRECT_MAX_WGS", &c->direct_max_wgs, 0, 1 << 30);
 }
 
 }  // namespace
@@ -568,7 +586,7 @@ pkv_status paged_attn_decode_plan_stats(pkv_pool* p, const int64_t* seqs, int32_
   out->logical_tokens = plan.logical_tokens;
   out->unique_blocks = plan.unique_blocks;
   out->segments = plan.segments;
-  out->work_items = static_cast<int32_t>(plan.valu.size() + plan.mfma.size());
+  out->work_items = static_cast<int32_t>(plan.valu.size() + plan.mfma.size() + plan.direct.size());
   out->merged_rows = static_cast<int32_t>(plan.merges.size()) * p->core.shape().num_q_heads;
   return PKV_OK;
 }

@@ -93,13 +93,16 @@ void finish_parts(Plan* plan, const std::vector<int32_t>& n_parts, int32_t hq) {
 }
 
 // Copies every item's block list to a fixed-stride slot (MFMA items first,
-// as the kernel numbers them), padding with the item's last block.
+// as the kernel numbers them, then VALU, then direct items), padding with the
+// item's last block.
 void pack_item_blocks(Plan* plan, int32_t block_size) {
   auto nblk = [&](const WorkItem& it) { return (it.n_tok + block_size - 1) / block_size; };
-  plan->stride_mfma = plan->stride_valu = 0;
+  plan->stride_mfma = plan->stride_valu = plan->stride_direct = 0;
   for (const WorkItem& it : plan->mfma) plan->stride_mfma = std::max(plan->stride_mfma, nblk(it));
   for (const WorkItem& it : plan->valu) plan->stride_valu = std::max(plan->stride_valu, nblk(it));
-  plan->item_blocks.assign(plan->mfma.size() * plan->stride_mfma + plan->valu.size() * plan->stride_valu, 0);
+  for (const WorkItem& it : plan->direct) plan->stride_direct = std::max(plan->stride_direct, nblk(it));
+  plan->item_blocks.assign(plan->mfma.size() * plan->stride_mfma + plan->valu.size() * plan->stride_valu +
+                               plan->direct.size() * plan->stride_direct, 0);
   int32_t* dst = plan->item_blocks.data();
   auto put = [&](const std::vector<WorkItem>& items, int32_t stride) {
     for (const WorkItem& it : items) {
@@ -110,6 +113,7 @@ void pack_item_blocks(Plan* plan, int32_t block_size) {
   };
   put(plan->mfma, plan->stride_mfma);
   put(plan->valu, plan->stride_valu);
+  put(plan->direct, plan->stride_direct);
 }
 
 }  // namespace
@@ -227,6 +231,39 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     for (auto it = kids.rbegin(); it != kids.rend(); ++it) stack.push_back(std::move(*it));
   }
   plan->segments = static_cast<int32_t>(segs.size());
+
+  // ---- direct plan ----
+  // Few, short queries: one item per query over all of its keys.  The
+  // kernel then reads a shared prefix once per query (from L2 after the
+  // first), but the call is one launch with no partial states; for such
+  // calls launch and latency, not bytes, set the time.
+  int32_t max_len = 0, max_blocks = 0;
+  for (int32_t q = 0; q < n_seqs; ++q) {
+    max_len = std::max(max_len, st[q]->len);
+    max_blocks = std::max(max_blocks, nblk(q));
+  }
+  if (cfg.direct_max_tokens > 0 && G <= 16 && max_len <= cfg.direct_max_tokens &&
+      max_blocks <= cfg.max_chunk_blocks &&
+      static_cast<int64_t>(n_seqs) * sh.num_kv_heads <= cfg.direct_max_wgs) {
+    for (int32_t q = 0; q < n_seqs; ++q) {
+      WorkItem it{};
+      it.blk_off = static_cast<int32_t>(plan->blocks.size());
+      it.n_tok = st[q]->len;
+      it.tail_start = INT_MAX;
+      it.tail_node0 = 0;
+      it.grp_off = static_cast<int32_t>(plan->groups.size());
+      it.n_grp = 1;
+      it.part_base = -1;
+      it.q_index[0] = q;
+      plan->groups.push_back(RowGroup{q, -1, 0u, 0u, -1, {0, 0, 0}});
+      plan->blocks.insert(plan->blocks.end(), st[q]->table.begin(), st[q]->table.end());
+      plan->direct.push_back(it);
+    }
+    std::stable_sort(plan->direct.begin(), plan->direct.end(),
+                     [](const WorkItem& a, const WorkItem& b) { return a.n_tok > b.n_tok; });
+    pack_item_blocks(plan, B);
+    return Err::ok;
+  }
 
   // ---- work items ----
   // Segments read by many rows (a shared prefix under many queries) are a

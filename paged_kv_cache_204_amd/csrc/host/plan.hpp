@@ -39,6 +39,10 @@ struct PlanConfig {
   int32_t unshare_max_queries = 4;   // a shared run of at most this many queries ...
   int32_t unshare_max_tokens = 256;  // ... and tokens, too sparse for the MFMA path,
                                      // is read by each query's own item instead
+  int32_t direct_max_tokens = 1024;  // decode calls whose queries all have at most this many
+  int32_t direct_max_wgs = 256;      // keys, over at most this many (query, kv head) pairs,
+                                     // run one workgroup per pair over all of its keys (no
+                                     // partial states, no merge); 0 turns this off
   int32_t tile = 64;             // key tokens per kernel tile; chunks are multiples
   int32_t max_chunk = 4096;      // key tokens per work item at most
   int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)
@@ -50,12 +54,13 @@ inline int32_t mfma_item_rows(int32_t row_tiles, int32_t waves) { return waves *
 struct Plan {
   std::vector<WorkItem> valu;   // items for the VALU kernel
   std::vector<WorkItem> mfma;   // items for the MFMA kernel
+  std::vector<WorkItem> direct; // one item per query for the direct kernel (then the only items)
   std::vector<RowGroup> groups;
   std::vector<int32_t> blocks;
   std::vector<MergeRow> merges;
   std::vector<int32_t> parts;
   std::vector<int32_t> item_blocks;   // per-item block lists, fixed strides
-  int32_t stride_mfma = 0, stride_valu = 0;
+  int32_t stride_mfma = 0, stride_valu = 0, stride_direct = 0;
   int64_t partial_rows = 0;
   int32_t mfma_row_tiles = 1;   // row tiles per wave the MFMA items were cut for
   int32_t mfma_waves = 4;       // waves per MFMA workgroup (8 only without VALU items)
@@ -71,12 +76,13 @@ struct Plan {
   void reset() {
     valu.clear();
     mfma.clear();
+    direct.clear();
     groups.clear();
     blocks.clear();
     merges.clear();
     parts.clear();
     item_blocks.clear();
-    stride_mfma = stride_valu = 0;
+    stride_mfma = stride_valu = stride_direct = 0;
     partial_rows = 0;
     mfma_row_tiles = 1;
     mfma_waves = 4;

@@ -53,6 +53,12 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t row_tiles,
                        int32_t valu_rows, int32_t waves, hipStream_t s);
 
+// Direct decode: one workgroup per (item, kv head), each item one query
+// over all of its keys (n_grp 1, tail_start INT_MAX), written straight to
+// out / lse; items[i]'s block list at blocks + i * stride (<= kMaxItemBlocks).
+hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
+                         hipStream_t s);
+
 // Log-sum-exp merge of the partial states of several work items.
 struct MergeParams {
   const MergeRow* merges;

@@ -74,13 +74,117 @@ struct MfmaSmem {
   uint16_t vt[2][D][kStep + 4];    // V^T, pitch 18 words
 };
 
-// S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q rows
-// in registers): the accumulator gives each lane 4 tokens of ONE query row,
-// so the softmax max / sum need two cross-row swaps only, and the rounded P
-// (bf16) of the lane's 8 tokens is exactly the B operand of O^T += V^T P^T.
-// O^T keeps each lane on the same row, so the online rescale is lane local.
-// The O rescale runs only when some row of the wave outgrows its reference
-// max by more than kSlack (see the softmax step below).
+// One 32-token step of the MFMA path for the RT row tiles of one wave, from
+// K rows (k) and V^T (vt) staged in LDS: S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16 (A = K rows, B = Q rows in registers), the masked
+// online softmax, and O^T += V^T P^T.  The score accumulator gives each lane
+// 4 tokens of ONE query row (row l16, tokens 16 tt + 4 g4 + i), so the
+// softmax max / sum need two cross-row swaps only, and the rounded P (bf16)
+// of the lane's 8 tokens is exactly the B operand of the P V product.  O^T
+// keeps each lane on the same row, so the online rescale is lane local; it
+// runs only when some row of the wave outgrows its reference max by more
+// than kSlack.
+template <int D, int RT>
+__device__ __forceinline__ void mfma_tile(const uint16_t (*k)[D + 8], const uint16_t (*vt)[kStep + 4],
+                                          const bf16x8 (&qf)[RT][D / 32], const uint64_t (&anc)[RT],
+                                          const WorkItem& it, int t0, float scale_log2,
+                                          float (&m_run)[RT], float (&l_run)[RT],
+                                          f32x4 (&o)[RT][D / 16]) {
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+  f32x4 sacc[RT][2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    sacc[rt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sacc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k[16 * tt + l16][32 * kk + 8 * g4]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        sacc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][kk], sacc[rt][tt], 0, 0, 0);
+    }
+  }
+  const bool full = t0 + kStep <= it.n_tok && t0 + kStep <= it.tail_start;
+  bf16x8 pf[RT], pf_lo[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float sv[8];   // raw scores; the scale is applied inside the exponent
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[4 * tt + i] = sacc[rt][tt][i];
+    if (!full) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tok = t0 + 16 * (j >> 2) + 4 * g4 + (j & 3);
+        bool vis = tok < it.n_tok;
+        if (vis && tok >= it.tail_start)
+          vis = (anc[rt] >> (it.tail_node0 + tok - it.tail_start)) & 1ull;
+        if (!vis) sv[j] = -INFINITY;
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+    mx = xor32_max(xor16_max(mx)) * scale_log2;
+    // The reference max m moves only when a row's max passes it by more
+    // than kSlack (then the whole wave rescales, every row to its exact
+    // max), so P <= 2^kSlack and the O rescale is rare after the first
+    // steps.  P enters the PV product as two bf16 terms, hi = bf16(P) and
+    // lo = bf16(P - hi), which carry it to about 2^-17 relative: a single
+    // bf16 P would leave up to 2^-9 relative error on each weight, which
+    // on rows of a few keys reaches 4e-3 in the output.
+    const float m_old = m_run[rt];
+    if (__ballot(mx > m_old + kSlack)) {
+      const float m_new = fmaxf(mx, m_old);
+      const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
+      l_run[rt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) o[rt][dt] *= alpha;
+      m_run[rt] = m_new;
+    }
+    const float m_use = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];
+    float ps = 0.f;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const float p0 = fast_exp2(fmaf(sv[j], scale_log2, -m_use));
+      const float p1 = fast_exp2(fmaf(sv[j + 1], scale_log2, -m_use));
+      ps += p0 + p1;
+      const uint32_t h = pack_bf16x2(p0, p1);
+      ph[j >> 1] = h;
+      pl[j >> 1] = pack_bf16x2(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xFFFF0000u));
+    }
+    l_run[rt] += ps;
+    uint4 hv = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+    uint4 lv = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+    pf[rt] = *reinterpret_cast<bf16x8*>(&hv);
+    pf_lo[rt] = *reinterpret_cast<bf16x8*>(&lv);
+  }
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(&vt[16 * dt + l16][4 * g4]);
+    const uint2 hi = *reinterpret_cast<const uint2*>(&vt[16 * dt + l16][16 + 4 * g4]);
+    uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    const bf16x8 a = *reinterpret_cast<bf16x8*>(&av);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[rt][dt], 0, 0, 0);
+      o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf_lo[rt], o[rt][dt], 0, 0, 0);
+    }
+  }
+}
+
+// One MFMA work item: the W waves share each 32-token K / V^T step staged in
+// LDS (double buffered, loads requested kDepth steps ahead), and each wave
+// runs mfma_tile on its own RT row tiles.
 template <int D, int RT, int W>
 __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& it, int h,
                                           MfmaSmem<D>& sm, const int32_t* blk_s) {
@@ -192,92 +296,7 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
     fetch(slot, (s + kDepth) * kStep);
     if (!active) return;
 
-    const int t0 = s * kStep;
-    f32x4 sacc[RT][2];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      sacc[rt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sacc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][16 * tt + l16][32 * kk + 8 * g4]);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          sacc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][kk], sacc[rt][tt], 0, 0, 0);
-      }
-    }
-    const bool full = t0 + kStep <= it.n_tok && t0 + kStep <= it.tail_start;
-    bf16x8 pf[RT], pf_lo[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float sv[8];   // raw scores; the scale is applied inside the exponent
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[4 * tt + i] = sacc[rt][tt][i];
-      if (!full) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int tok = t0 + 16 * (j >> 2) + 4 * g4 + (j & 3);
-          bool vis = tok < it.n_tok;
-          if (vis && tok >= it.tail_start)
-            vis = (anc[rt] >> (it.tail_node0 + tok - it.tail_start)) & 1ull;
-          if (!vis) sv[j] = -INFINITY;
-        }
-      }
-      float mx = sv[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-      mx = xor32_max(xor16_max(mx)) * p.scale_log2;
-      // The reference max m moves only when a row's max passes it by more
-      // than kSlack (then the whole wave rescales, every row to its exact
-      // max), so P <= 2^kSlack and the O rescale is rare after the first
-      // steps.  P enters the PV product as two bf16 terms, hi = bf16(P) and
-      // lo = bf16(P - hi), which carry it to about 2^-17 relative: a single
-      // bf16 P would leave up to 2^-9 relative error on each weight, which
-      // on rows of a few keys reaches 4e-3 in the output.
-      const float m_old = m_run[rt];
-      if (__ballot(mx > m_old + kSlack)) {
-        const float m_new = fmaxf(mx, m_old);
-        const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
-        l_run[rt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) o[rt][dt] *= alpha;
-        m_run[rt] = m_new;
-      }
-      const float m_use = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];
-      float ps = 0.f;
-      uint32_t ph[4], pl[4];
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const float p0 = fast_exp2(fmaf(sv[j], p.scale_log2, -m_use));
-        const float p1 = fast_exp2(fmaf(sv[j + 1], p.scale_log2, -m_use));
-        ps += p0 + p1;
-        const uint32_t h = pack_bf16x2(p0, p1);
-        ph[j >> 1] = h;
-        pl[j >> 1] = pack_bf16x2(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xFFFF0000u));
-      }
-      l_run[rt] += ps;
-      uint4 hv = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-      uint4 lv = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-      pf[rt] = *reinterpret_cast<bf16x8*>(&hv);
-      pf_lo[rt] = *reinterpret_cast<bf16x8*>(&lv);
-    }
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(&sm.vt[buf][16 * dt + l16][4 * g4]);
-      const uint2 hi = *reinterpret_cast<const uint2*>(&sm.vt[buf][16 * dt + l16][16 + 4 * g4]);
-      uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      const bf16x8 a = *reinterpret_cast<bf16x8*>(&av);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[rt][dt], 0, 0, 0);
-        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf_lo[rt], o[rt][dt], 0, 0, 0);
-      }
-    }
+    mfma_tile<D, RT>(sm.k[buf], sm.vt[buf], qf, anc, it, s * kStep, p.scale_log2, m_run, l_run, o);
   };
 
 #pragma unroll
@@ -703,6 +722,178 @@ __global__ __launch_bounds__(64 * W) void attn_kernel(const WorkItem* __restrict
   }
 }
 
+// ---------------------------------------------------------------- direct path
+// Decode calls of few, short queries: one workgroup per (query, kv head)
+// covers all of the query's keys, so the call writes no partial states and
+// needs no merge launch.  The W waves take the 32-token steps in turn (wave
+// w the steps w, w + W, ...); each stages its own K / V^T tile in its own
+// LDS region, with register loads DEPTH of its steps ahead and only
+// wave-level ordering, and runs mfma_tile on one 16-row tile that holds the
+// query's G <= 16 heads (rows G..15 are zero).  At the end the waves'
+// softmax states (m, l, O) meet in LDS and are merged by log-sum-exp.
+template <int D>
+struct DirectWaveSmem {
+  uint16_t k[kStep][D + 8];
+  uint16_t vt[D][kStep + 4];
+};
+
+template <int D, int W>
+union DirectSmem {
+  DirectWaveSmem<D> w[W];
+  struct {
+    float o[W][16][D + 4];
+    float m[W][16];
+    float l[W][16];
+  } fin;
+};
+
+template <int D, int W, int DEPTH>
+__global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restrict__ items,
+                                                          const int32_t* __restrict__ blocks,
+                                                          const uint16_t* __restrict__ q,
+                                                          int32_t stride, AttnParams p) {
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int KPER = kStep * CPR / 64;   // K chunks per lane per step
+  constexpr int VPER = 16 * CPR / 64;      // (token pair, chunk) V units per lane per step
+  static_assert(KPER * 64 == kStep * CPR && VPER * 64 == 16 * CPR, "a step splits evenly over a wave");
+  __shared__ DirectSmem<D, W> sm;
+  __shared__ int32_t blk_s[kMaxItemBlocks];
+
+  const int item = static_cast<int>(blockIdx.x) / p.Hkv;
+  const int h = static_cast<int>(blockIdx.x) - item * p.Hkv;
+  const int32_t* lst = blocks + static_cast<size_t>(item) * stride;
+  for (int i = threadIdx.x; i < stride; i += 64 * W) blk_s[i] = lst[i];
+  const WorkItem it = items[item];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+  const size_t row0 = static_cast<size_t>(it.q_index[0]) * p.Hq + static_cast<size_t>(h) * p.G;
+
+  bf16x8 qf[1][NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) qf[0][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  if (l16 < p.G) {
+    const uint16_t* qrow = q + (row0 + l16) * D;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qf[0][kk] = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * g4);
+  }
+  const uint64_t anc[1] = {0};
+  float m_run[1] = {-INFINITY}, l_run[1] = {0.f};
+  f32x4 o[1][ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) o[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  lds_barrier();
+
+  // K chunk ci = lane + 64 i is (token ci / CPR, chunk ci % CPR); V unit
+  // u = lane + 64 i is chunk u / 16 of tokens 2 (u % 16) and 2 (u % 16) + 1,
+  // stored transposed as in the shared-tile path.  Tokens past the end
+  // re-read the last token (its lanes are masked in the softmax).
+  DirectWaveSmem<D>& ws = sm.w[wave];
+  const uint4* kb = layer_head_base(p, p.k_pool, h, D);
+  const uint4* vb = layer_head_base(p, p.v_pool, h, D);
+  const uint32_t blk_chunks = static_cast<uint32_t>(p.Hkv * p.B * D / 8);
+  const int t_last = it.n_tok - 1;
+  auto ldg = [&](const uint4* src, int t, int c) {
+    t = min(t, t_last);
+    return src[chunk_index(blk_s[t >> p.log2B], blk_chunks, (t & (p.B - 1)) * CPR + c)];
+  };
+  uint4 rk[DEPTH][KPER], rv[DEPTH][2 * VPER];
+  auto fetch = [&](int slot, int t0) {
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int ci = lane + 64 * i;
+      rk[slot][i] = ldg(kb, t0 + ci / CPR, ci % CPR);
+    }
+#pragma unroll
+    for (int i = 0; i < VPER; ++i) {
+      const int u = lane + 64 * i;
+      rv[slot][2 * i] = ldg(vb, t0 + 2 * (u & 15), u >> 4);
+      rv[slot][2 * i + 1] = ldg(vb, t0 + 2 * (u & 15) + 1, u >> 4);
+    }
+  };
+  auto step = [&](int slot, int s) {
+    // this wave's reads of its previous tile are done before it is replaced
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int ci = lane + 64 * i;
+      *reinterpret_cast<uint4*>(&ws.k[ci / CPR][(ci % CPR) * 8]) = rk[slot][i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPER; ++i) {
+      const int u = lane + 64 * i;
+      const int pair = u & 15;
+      const int c = u >> 4;
+      const uint4 va = rv[slot][2 * i], vb2 = rv[slot][2 * i + 1];
+      const uint32_t a[4] = {va.x, va.y, va.z, va.w};
+      const uint32_t b[4] = {vb2.x, vb2.y, vb2.z, vb2.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<uint32_t*>(&ws.vt[c * 8 + 2 * j][2 * pair]) = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&ws.vt[c * 8 + 2 * j + 1][2 * pair]) = __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
+      }
+    }
+    wave_lds_sync();
+    fetch(slot, (s + DEPTH * W) * kStep);
+    mfma_tile<D, 1>(ws.k, ws.vt, qf, anc, it, s * kStep, p.scale_log2, m_run, l_run, o);
+  };
+
+  const int nsteps = (it.n_tok + kStep - 1) / kStep;
+  const int mine = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;   // steps of this wave
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) fetch(j, (wave + j * W) * kStep);
+  int j0 = 0;
+  for (; j0 + DEPTH <= mine; j0 += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) step(j, wave + (j0 + j) * W);
+  }
+#pragma unroll
+  for (int j = 0; j < DEPTH - 1; ++j)
+    if (j0 + j < mine) step(j, wave + (j0 + j) * W);
+
+  // ---- merge of the W wave states ------------------------------------------
+  const float l_w = xor32_sum(xor16_sum(l_run[0]));
+  __syncthreads();   // every wave is done with its staging region (aliased below)
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+    *reinterpret_cast<float4*>(&sm.fin.o[wave][l16][16 * dt + 4 * g4]) =
+        make_float4(o[0][dt][0], o[0][dt][1], o[0][dt][2], o[0][dt][3]);
+  if (g4 == 0) {
+    sm.fin.m[wave][l16] = m_run[0];
+    sm.fin.l[wave][l16] = l_w;
+  }
+  __syncthreads();
+  for (int e = tid; e < p.G * (D / 4); e += 64 * W) {
+    const int row = e / (D / 4);
+    const int c4 = e - row * (D / 4);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) mx = fmaxf(mx, sm.fin.m[w][row]);
+    // wave 0 holds token 0, so mx is finite and l > 0
+    float l = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = sm.fin.m[w][row];
+      const float a = mw == -INFINITY ? 0.f : fast_exp2(mw - mx);
+      const float4 ow = *reinterpret_cast<const float4*>(&sm.fin.o[w][row][4 * c4]);
+      l = fmaf(a, sm.fin.l[w][row], l);
+      acc.x = fmaf(a, ow.x, acc.x);
+      acc.y = fmaf(a, ow.y, acc.y);
+      acc.z = fmaf(a, ow.z, acc.z);
+      acc.w = fmaf(a, ow.w, acc.w);
+    }
+    const float inv = 1.f / l;
+    *reinterpret_cast<float4*>(p.out + (row0 + row) * D + 4 * c4) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (c4 == 0 && p.lse) p.lse[row0 + row] = (mx + log2f(l)) * kLn2;
+  }
+}
+
 }  // namespace
 
 template <int D, int RT>
@@ -735,6 +926,25 @@ hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, i
   if (head_dim == 128 && row_tiles == 1) return launch_rows<128, 1>(p, grid, valu_rows, waves, s);
   if (head_dim == 128 && row_tiles == 2) return launch_rows<128, 2>(p, grid, valu_rows, waves, s);
   return hipErrorInvalidValue;
+}
+
+
+hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
+                         hipStream_t s) {
+  if (n_items == 0) return hipSuccess;
+  if (stride < 1 || stride > kMaxItemBlocks || p.G > 16) return hipErrorInvalidValue;
+  const int64_t n_wg = static_cast<int64_t>(n_items) * p.Hkv;
+  if (n_wg > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(n_wg));
+  // eight waves at head_dim 64; at 128 a wave's loads in flight need more
+  // registers than eight waves per workgroup leave, so four
+  if (head_dim == 64)
+    hipLaunchKernelGGL((direct_kernel<64, 8, 2>), grid, dim3(512), 0, s, p.items, p.blocks, p.q, stride, p);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((direct_kernel<128, 4, 2>), grid, dim3(256), 0, s, p.items, p.blocks, p.q, stride, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -126,10 +126,28 @@ def reduced():
 
 REDUCED = reduced()
 
+# Decode calls of few, short queries run the direct kernel (one workgroup per
+# query and kv head over all its keys); the same calls can be forced onto the
+# split path (shared-prefix items, partial states, merge) or, past the default
+# limits, onto the direct kernel.  Planner settings are read from the
+# environment when a pool is created.
+PATHS = {
+    "auto": {},
+    "split": {"PKV_DIRECT_MAX_TOKENS": "0"},
+    "direct": {"PKV_DIRECT_MAX_TOKENS": "100000", "PKV_DIRECT_MAX_WGS": "100000"},
+}
 
+
+def set_path(monkeypatch, path):
+    for k, v in PATHS[path].items():
+        monkeypatch.setenv(k, v)
+
+
+@pytest.mark.parametrize("path", ["auto", "split"])
 @pytest.mark.parametrize("name", list(REDUCED))
-def test_reduced_workload_parity(dev, name):
-    parity(REDUCED[name])
+def test_reduced_workload_parity(dev, name, path, monkeypatch):
+    set_path(monkeypatch, path)
+    parity(REDUCED[name], label=f"{name}[{path}]")
 
 
 # Shapes at the edges of what the kernels take: block sizes 1..128, GQA group
@@ -144,30 +162,70 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["auto", "split"])
 @pytest.mark.parametrize("shape,label", SHAPES, ids=[s[1] for s in SHAPES])
-def test_shape_edges(dev, shape, label):
+def test_shape_edges(dev, shape, label, path, monkeypatch):
+    set_path(monkeypatch, path)
     wl = synth.fork_workload(f"edge_{label}", 20 + SHAPES.index((shape, label)), shape,
                              prefix_len=131, n_branches=3, branch_len=67, decode_steps=2,
                              permute=True)
-    parity(wl)
-    tree = synth.verify_workload(f"edge_tree_{label}", 40 + SHAPES.index((shape, label)),
-                                 shape, n_seqs=2, ctx_len=70, n_nodes=9, tree_depth=4)
-    parity(tree)
+    parity(wl, label=f"edge_{label}[{path}]")
+    if path == "auto":
+        tree = synth.verify_workload(f"edge_tree_{label}", 40 + SHAPES.index((shape, label)),
+                                     shape, n_seqs=2, ctx_len=70, n_nodes=9, tree_depth=4)
+        parity(tree)
+
+
+# Direct decode at its edges: fewer 32-token steps than waves (1..9 keys),
+# ragged lengths within one call, lengths around the step size, G 1 / 3 / 16
+# at both head dims (eight- and four-wave kernels).
+DIRECT_CASES = [
+    # shape, prefix, own keys of branch i = base + i * inc, branches
+    (Shape(8, 8, 64, 16, 1, 64), 1, 0, 1, 6),
+    (Shape(24, 8, 64, 4, 1, 256), 31, 1, 16, 5),
+    (Shape(16, 1, 128, 16, 1, 256), 64, 0, 31, 4),
+    (Shape(32, 4, 128, 32, 1, 512), 200, 290, 9, 7),
+]
+
+
+def ragged_fork(name, cfg_id, shape, prefix, base, inc, n, decode_steps=3):
+    ops = [("alloc", 0), ("append", (0,), prefix, 1)]
+    kids = tuple(range(1, n + 1))
+    for c in kids:
+        ops.append(("fork", 0, c))
+    for i, c in enumerate(kids):
+        if base + i * inc:
+            ops.append(("append", (c,), base + i * inc, len(ops)))
+    for _ in range(decode_steps):
+        ops.append(("append", kids, 1, len(ops)))
+        ops.append(("decode", kids, 0, len(ops)))
+    return synth.Workload(name, cfg_id, shape, ops, 1.0 / math.sqrt(shape.head_dim),
+                          permute_free_list=True)
+
+
+@pytest.mark.parametrize("case", range(len(DIRECT_CASES)))
+def test_direct_decode_edges(dev, case, monkeypatch):
+    set_path(monkeypatch, "direct")
+    shape, prefix, base, inc, n = DIRECT_CASES[case]
+    parity(ragged_fork(f"direct_{case}", 70 + case, shape, prefix, base, inc, n), label=f"direct_{case}")
 
 
 # Planner settings (read from the environment when a pool is created) pick
 # different kernel variants for the same call: four- or eight-wave MFMA
 # workgroups, one or two row tiles per wave, few or many key chunks, the
 # VALU path for everything it can take.  Every setting must keep parity.
+# (the split-path settings also turn direct decode plans off)
+_SPLIT = {"PKV_DIRECT_MAX_TOKENS": "0"}
 KNOBS = [
-    {"PKV_MFMA_WAVES": "4", "PKV_MFMA_ROW_TILES": "2"},
-    {"PKV_MFMA_WAVES": "8", "PKV_MFMA_ROW_TILES": "2"},
-    {"PKV_MFMA_ROW_TILES": "1"},
-    {"PKV_TARGET_MFMA_WGS": "16", "PKV_TARGET_WGS": "16"},
-    {"PKV_TARGET_MFMA_WGS": "4096", "PKV_TARGET_WGS": "4096", "PKV_MAX_CHUNK": "64"},
-    {"PKV_MFMA_MIN_ROWS": "0"},
-    {"PKV_UNSHARE_MAX_QUERIES": "0"},
-    {"PKV_UNSHARE_MAX_QUERIES": "64", "PKV_UNSHARE_MAX_TOKENS": "100000"},
+    {"PKV_MFMA_WAVES": "4", "PKV_MFMA_ROW_TILES": "2", **_SPLIT},
+    {"PKV_MFMA_WAVES": "8", "PKV_MFMA_ROW_TILES": "2", **_SPLIT},
+    {"PKV_MFMA_ROW_TILES": "1", **_SPLIT},
+    {"PKV_TARGET_MFMA_WGS": "16", "PKV_TARGET_WGS": "16", **_SPLIT},
+    {"PKV_TARGET_MFMA_WGS": "4096", "PKV_TARGET_WGS": "4096", "PKV_MAX_CHUNK": "64", **_SPLIT},
+    {"PKV_MFMA_MIN_ROWS": "0", **_SPLIT},
+    {"PKV_UNSHARE_MAX_QUERIES": "0", **_SPLIT},
+    {"PKV_UNSHARE_MAX_QUERIES": "64", "PKV_UNSHARE_MAX_TOKENS": "100000", **_SPLIT},
+    PATHS["direct"],
 ]
 
 
@@ -199,16 +257,20 @@ def sample_ops(wl, every):
     return keep
 
 
-@pytest.mark.parametrize("name,every", [
-    ("c1_tiny_fork", 1), ("c2_trellis", 23), ("c3_dendrite", 9),
-    ("c3_dendrite_aligned", 31), ("c4_mcts", 1), ("c4_mcts_folded", 1), ("c5_verify", 1),
+@pytest.mark.parametrize("name,every,path", [
+    ("c1_tiny_fork", 1, "auto"), ("c1_tiny_fork", 1, "split"),
+    ("c2_trellis", 23, "auto"), ("c2_trellis", 23, "split"),
+    ("c3_dendrite", 9, "auto"), ("c3_dendrite", 31, "direct"), ("c3_dendrite_aligned", 31, "auto"),
+    ("c4_mcts", 1, "auto"), ("c4_mcts_folded", 1, "auto"), ("c5_verify", 1, "auto"),
 ])
-def test_full_workload_parity(dev, name, every):
+def test_full_workload_parity(dev, name, every, path, monkeypatch):
     """The five workloads at full size, launched as the benchmark launches
-    them; every call runs on the GPU, the oracle checks a sample of calls
-    (all of them for single-call workloads)."""
+    them (path "auto"), and the small-batch decode ones also on the other
+    decode path; every call runs on the GPU, the oracle checks a sample of
+    calls (all of them for single-call workloads)."""
+    set_path(monkeypatch, path)
     wl = synth.named(name)
-    parity(wl, want=sample_ops(wl, every), check_pool=name != "c2_trellis")
+    parity(wl, want=sample_ops(wl, every), check_pool=name != "c2_trellis", label=f"{name}[{path}]")
 
 
 # ---------------------------------------------------------------- edges

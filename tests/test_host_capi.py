@@ -200,7 +200,7 @@ def test_named_workloads_match_the_oracle_pool(name):
         mir.close()
 
 
-def test_c2_plan_reads_the_shared_prompt_once():
+def c2_first_decode_stats():
     wl = synth.named("c2_trellis")
     s = wl.shape
     pool = host_pool(s.num_blocks, s.block_size, s.num_layers, s.num_q_heads,
@@ -215,15 +215,42 @@ def test_c2_plan_reads_the_shared_prompt_once():
             elif op[0] == "append":
                 pkv.kv_append(pool, [ids[h] for h in op[1]], op[2])
             elif op[0] == "decode":
-                st_ = pkv.paged_attn_decode_plan_stats(pool, [ids[h] for h in op[1]])
-                break
-        # 1 shared segment (8 blocks) + 16 own segments
-        assert st_["segments"] == 17
-        assert st_["unique_blocks"] == 8 + 16 * 9
-        assert st_["unique_tokens"] == 256 + 16 * 257
-        assert st_["logical_tokens"] == 16 * 513
+                return pkv.paged_attn_decode_plan_stats(pool, [ids[h] for h in op[1]])
     finally:
         pkv.kv_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("direct", [True, False])
+def test_c2_plan_reads_the_shared_prompt_once(direct, monkeypatch):
+    if not direct:
+        monkeypatch.setenv("PKV_DIRECT_MAX_TOKENS", "0")
+    st_ = c2_first_decode_stats()
+    # 1 shared segment (8 blocks) + 16 own segments
+    assert st_["segments"] == 17
+    assert st_["unique_blocks"] == 8 + 16 * 9
+    assert st_["unique_tokens"] == 256 + 16 * 257
+    assert st_["logical_tokens"] == 16 * 513
+    if direct:
+        # 16 queries x 4 kv heads with 513 keys each: one item per query, no merge
+        assert st_["work_items"] == 16 and st_["merged_rows"] == 0
+    else:
+        # the shared prompt is its own item(s): every query's heads are merged
+        assert st_["work_items"] > 16 and st_["merged_rows"] == 16 * 32
+
+
+@pytest.mark.parametrize("env,direct", [
+    ({}, True),
+    ({"PKV_DIRECT_MAX_TOKENS": "512"}, False),   # queries hold 513 keys
+    ({"PKV_DIRECT_MAX_WGS": "63"}, False),       # 16 queries x 4 kv heads = 64
+    ({"PKV_DIRECT_MAX_WGS": "64"}, True),
+    ({"PKV_DIRECT_MAX_WGS": "0"}, False),
+])
+def test_direct_plan_limits(env, direct, monkeypatch):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    st_ = c2_first_decode_stats()
+    assert (st_["merged_rows"] == 0) == direct
+    assert (st_["work_items"] == 16) == direct
 
 
 def test_errors_leave_the_pool_unchanged():
