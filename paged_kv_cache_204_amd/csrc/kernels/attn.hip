@@ -74,18 +74,20 @@ struct MfmaSmem {
   uint16_t vt[2][D][kStep + 4];    // V^T, pitch 18 words
 };
 
-// One 32-token step of the MFMA path for the RT row tiles of one wave, from
-// K rows (k) and V^T (vt) staged in LDS: S^T = K Q^T with
-// v_mfma_f32_16x16x32_bf16 (A = K rows, B = Q rows in registers), the masked
-// online softmax, and O^T += V^T P^T.  The score accumulator gives each lane
+// One 32-token step of the MFMA path for the RT row tiles of one wave:
+// S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows, B = Q rows in
+// registers), the masked online softmax, and O^T += V^T P^T.  kop(tt, kk)
+// gives the K operand of tokens 16 tt + l16, dims 32 kk + 8 g4 .. + 7;
+// vop(dt) the V^T operand of dim 16 dt + l16, tokens 4 g4 .. + 3 and
+// 16 + 4 g4 .. + 3; after_qk() runs once the score products are issued.  The score accumulator gives each lane
 // 4 tokens of ONE query row (row l16, tokens 16 tt + 4 g4 + i), so the
 // softmax max / sum need two cross-row swaps only, and the rounded P (bf16)
 // of the lane's 8 tokens is exactly the B operand of the P V product.  O^T
 // keeps each lane on the same row, so the online rescale is lane local; it
 // runs only when some row of the wave outgrows its reference max by more
 // than kSlack.
-template <int D, int RT>
-__device__ __forceinline__ void mfma_tile(const uint16_t (*k)[D + 8], const uint16_t (*vt)[kStep + 4],
+template <int D, int RT, class KOp, class VOp, class AfterQK>
+__device__ __forceinline__ void mfma_tile(KOp kop, VOp vop, AfterQK after_qk,
                                           const bf16x8 (&qf)[RT][D / 32], const uint64_t (&anc)[RT],
                                           const WorkItem& it, int t0, float scale_log2,
                                           float (&m_run)[RT], float (&l_run)[RT],
@@ -105,12 +107,13 @@ __device__ __forceinline__ void mfma_tile(const uint16_t (*k)[D + 8], const uint
   for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k[16 * tt + l16][32 * kk + 8 * g4]);
+      const bf16x8 a = kop(tt, kk);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         sacc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][kk], sacc[rt][tt], 0, 0, 0);
     }
   }
+  after_qk();
   const bool full = t0 + kStep <= it.n_tok && t0 + kStep <= it.tail_start;
   bf16x8 pf[RT], pf_lo[RT];
 #pragma unroll
@@ -170,10 +173,7 @@ __device__ __forceinline__ void mfma_tile(const uint16_t (*k)[D + 8], const uint
   }
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(&vt[16 * dt + l16][4 * g4]);
-    const uint2 hi = *reinterpret_cast<const uint2*>(&vt[16 * dt + l16][16 + 4 * g4]);
-    uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    const bf16x8 a = *reinterpret_cast<bf16x8*>(&av);
+    const bf16x8 a = vop(dt);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[rt][dt], 0, 0, 0);
@@ -296,7 +296,16 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
     fetch(slot, (s + kDepth) * kStep);
     if (!active) return;
 
-    mfma_tile<D, RT>(sm.k[buf], sm.vt[buf], qf, anc, it, s * kStep, p.scale_log2, m_run, l_run, o);
+    const auto kop = [&](int tt, int kk) {
+      return *reinterpret_cast<const bf16x8*>(&sm.k[buf][16 * tt + l16][32 * kk + 8 * g4]);
+    };
+    const auto vop = [&](int dt) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(&sm.vt[buf][16 * dt + l16][4 * g4]);
+      const uint2 hi = *reinterpret_cast<const uint2*>(&sm.vt[buf][16 * dt + l16][16 + 4 * g4]);
+      uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      return *reinterpret_cast<bf16x8*>(&av);
+    };
+    mfma_tile<D, RT>(kop, vop, [] {}, qf, anc, it, s * kStep, p.scale_log2, m_run, l_run, o);
   };
 
 #pragma unroll
@@ -726,20 +735,25 @@ __global__ __launch_bounds__(64 * W) void attn_kernel(const WorkItem* __restrict
 // Decode calls of few, short queries: one workgroup per (query, kv head)
 // covers all of the query's keys, so the call writes no partial states and
 // needs no merge launch.  The W waves take the 32-token steps in turn (wave
-// w the steps w, w + W, ...); each stages its own K / V^T tile in its own
-// LDS region, with register loads DEPTH of its steps ahead and only
-// wave-level ordering, and runs mfma_tile on one 16-row tile that holds the
-// query's G <= 16 heads (rows G..15 are zero).  At the end the waves'
+// w the steps w, w + W, ...) and run mfma_tile on one 16-row tile that holds
+// the query's G <= 16 heads (rows G..15 are zero).  No wave reads another's
+// tile, so K goes from global memory straight into the lane's MFMA operand
+// registers and V is staged untransposed in an LDS region of the wave's own,
+// read back transposed with ds_read_b64_tr_b16; a wave's loads run DEPTH of
+// its steps ahead and need only wave-level ordering.  At the end the waves'
 // softmax states (m, l, O) meet in LDS and are merged by log-sum-exp.
-template <int D>
-struct DirectWaveSmem {
-  uint16_t k[kStep][D + 8];
-  uint16_t vt[D][kStep + 4];
-};
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 4-element rows named by lanes 4k + i / 4, for k = 0..3.
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* at) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(at));
+}
 
 template <int D, int W>
 union DirectSmem {
-  DirectWaveSmem<D> w[W];
+  uint16_t v[W][kStep][D + 8];   // each wave's V rows, padded pitch
   struct {
     float o[W][16][D + 4];
     float m[W][16];
@@ -755,9 +769,8 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
   constexpr int CPR = D / 8;
-  constexpr int KPER = kStep * CPR / 64;   // K chunks per lane per step
-  constexpr int VPER = 16 * CPR / 64;      // (token pair, chunk) V units per lane per step
-  static_assert(KPER * 64 == kStep * CPR && VPER * 64 == 16 * CPR, "a step splits evenly over a wave");
+  constexpr int VPER = kStep * CPR / 64;   // V chunks per lane per step
+  static_assert(VPER * 64 == kStep * CPR, "a step's V splits evenly over a wave");
   __shared__ DirectSmem<D, W> sm;
   __shared__ int32_t blk_s[kMaxItemBlocks];
 
@@ -768,7 +781,7 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
   const WorkItem it = items[item];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
   const size_t row0 = static_cast<size_t>(it.q_index[0]) * p.Hq + static_cast<size_t>(h) * p.G;
@@ -788,11 +801,10 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
   for (int dt = 0; dt < ND; ++dt) o[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   lds_barrier();
 
-  // K chunk ci = lane + 64 i is (token ci / CPR, chunk ci % CPR); V unit
-  // u = lane + 64 i is chunk u / 16 of tokens 2 (u % 16) and 2 (u % 16) + 1,
-  // stored transposed as in the shared-tile path.  Tokens past the end
-  // re-read the last token (its lanes are masked in the softmax).
-  DirectWaveSmem<D>& ws = sm.w[wave];
+  // K of token t0 + 16 tt + l16, chunk 4 kk + g4 is the lane's operand for
+  // (tt, kk); V chunk ci = lane + 64 i is (token ci / CPR, chunk ci % CPR).
+  // Tokens past the end re-read the last token (masked in the softmax).
+  uint16_t (*vs)[D + 8] = sm.v[wave];
   const uint4* kb = layer_head_base(p, p.k_pool, h, D);
   const uint4* vb = layer_head_base(p, p.v_pool, h, D);
   const uint32_t blk_chunks = static_cast<uint32_t>(p.Hkv * p.B * D / 8);
@@ -801,63 +813,64 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
     t = min(t, t_last);
     return src[chunk_index(blk_s[t >> p.log2B], blk_chunks, (t & (p.B - 1)) * CPR + c)];
   };
-  uint4 rk[DEPTH][KPER], rv[DEPTH][2 * VPER];
+  bf16x8 rk[DEPTH][2][NK];
+  uint4 rv[DEPTH][VPER];
   auto fetch = [&](int slot, int t0) {
 #pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int ci = lane + 64 * i;
-      rk[slot][i] = ldg(kb, t0 + ci / CPR, ci % CPR);
-    }
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        rk[slot][tt][kk] = __builtin_bit_cast(bf16x8, ldg(kb, t0 + 16 * tt + l16, 4 * kk + g4));
 #pragma unroll
     for (int i = 0; i < VPER; ++i) {
-      const int u = lane + 64 * i;
-      rv[slot][2 * i] = ldg(vb, t0 + 2 * (u & 15), u >> 4);
-      rv[slot][2 * i + 1] = ldg(vb, t0 + 2 * (u & 15) + 1, u >> 4);
+      const int ci = lane + 64 * i;
+      rv[slot][i] = ldg(vb, t0 + ci / CPR, ci % CPR);
     }
   };
-  auto step = [&](int slot, int s) {
-    // this wave's reads of its previous tile are done before it is replaced
+  auto step = [&](int slot, int s, bool prefetch) {
+    // this wave's reads of its previous V tile are done before it is replaced
     wave_lds_sync();
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int ci = lane + 64 * i;
-      *reinterpret_cast<uint4*>(&ws.k[ci / CPR][(ci % CPR) * 8]) = rk[slot][i];
-    }
 #pragma unroll
     for (int i = 0; i < VPER; ++i) {
-      const int u = lane + 64 * i;
-      const int pair = u & 15;
-      const int c = u >> 4;
-      const uint4 va = rv[slot][2 * i], vb2 = rv[slot][2 * i + 1];
-      const uint32_t a[4] = {va.x, va.y, va.z, va.w};
-      const uint32_t b[4] = {vb2.x, vb2.y, vb2.z, vb2.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<uint32_t*>(&ws.vt[c * 8 + 2 * j][2 * pair]) = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(&ws.vt[c * 8 + 2 * j + 1][2 * pair]) = __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
-      }
+      const int ci = lane + 64 * i;
+      *reinterpret_cast<uint4*>(&vs[ci / CPR][(ci % CPR) * 8]) = rv[slot][i];
     }
     wave_lds_sync();
-    fetch(slot, (s + DEPTH * W) * kStep);
-    mfma_tile<D, 1>(ws.k, ws.vt, qf, anc, it, s * kStep, p.scale_log2, m_run, l_run, o);
+    const auto kop = [&](int tt, int kk) { return rk[slot][tt][kk]; };
+    // lane (l16, g4) of each 16-lane group names 4 dims of one token row; the
+    // transposed read hands lane i of the group dim 16 dt + i of 4 tokens
+    const auto vop = [&](int dt) {
+      const int r = 4 * g4 + (l16 >> 2);
+      const int c = 16 * dt + 4 * (l16 & 3);
+      const v4i16 lo = lds_read_tr16(&vs[r][c]);
+      const v4i16 hi = lds_read_tr16(&vs[16 + r][c]);
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    // the slot's next loads leave once its K operands have been consumed
+    const auto after_qk = [&] {
+      if (prefetch) fetch(slot, (s + DEPTH * W) * kStep);
+    };
+    mfma_tile<D, 1>(kop, vop, after_qk, qf, anc, it, s * kStep, p.scale_log2, m_run, l_run, o);
   };
 
   const int nsteps = (it.n_tok + kStep - 1) / kStep;
   const int mine = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;   // steps of this wave
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) fetch(j, (wave + j * W) * kStep);
+  // whole rounds in which every step fetches the one DEPTH ahead, then the
+  // last steps, of which only those with a step DEPTH ahead fetch
   int j0 = 0;
-  for (; j0 + DEPTH <= mine; j0 += DEPTH) {
+  for (; j0 + 2 * DEPTH <= mine; j0 += DEPTH) {
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) step(j, wave + (j0 + j) * W);
+    for (int j = 0; j < DEPTH; ++j) step(j, wave + (j0 + j) * W, true);
   }
 #pragma unroll
-  for (int j = 0; j < DEPTH - 1; ++j)
-    if (j0 + j < mine) step(j, wave + (j0 + j) * W);
+  for (int j = 0; j < 2 * DEPTH - 1; ++j)
+    if (j0 + j < mine) step(j % DEPTH, wave + (j0 + j) * W, j0 + j + DEPTH < mine);
 
   // ---- merge of the W wave states ------------------------------------------
   const float l_w = xor32_sum(xor16_sum(l_run[0]));
-  __syncthreads();   // every wave is done with its staging region (aliased below)
+  lds_barrier();   // every wave is done with its V region (aliased below)
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
     *reinterpret_cast<float4*>(&sm.fin.o[wave][l16][16 * dt + 4 * g4]) =
@@ -866,7 +879,7 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
     sm.fin.m[wave][l16] = m_run[0];
     sm.fin.l[wave][l16] = l_w;
   }
-  __syncthreads();
+  lds_barrier();
   for (int e = tid; e < p.G * (D / 4); e += 64 * W) {
     const int row = e / (D / 4);
     const int c4 = e - row * (D / 4);
