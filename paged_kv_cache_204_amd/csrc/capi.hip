@@ -588,6 +588,8 @@ pkv_status paged_attn_decode_plan_stats(pkv_pool* p, const int64_t* seqs, int32_
   out->segments = plan.segments;
   out->work_items = static_cast<int32_t>(plan.valu.size() + plan.mfma.size() + plan.direct.size());
   out->merged_rows = static_cast<int32_t>(plan.merges.size()) * p->core.shape().num_q_heads;
+  out->direct = plan.direct.empty() ? 0 : 1;
+  out->pad = 0;
   return PKV_OK;
 }
 

@@ -94,9 +94,7 @@ __device__ __forceinline__ void mfma_tile(KOp kop, VOp vop, AfterQK after_qk,
                                           f32x4 (&o)[RT][D / 16]) {
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
-  const int lane = threadIdx.x & 63;
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
+  const int g4 = (threadIdx.x & 63) >> 4;
   f32x4 sacc[RT][2];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {

@@ -51,3 +51,19 @@ def test_traffic_summary_scales_by_the_copy_and_tracks_the_kernel_source(tmp_pat
     # a second workload is merged into the same table
     bench.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "c5_verify")
     assert set(json.loads(out.read_text())) == {"c2_trellis", "c5_verify"}
+
+
+def test_traffic_summary_takes_the_direct_kernel(tmp_path):
+    calib_kib = bench.CALIB_BYTES / 1024
+    # the library's other kernels must not be taken for the copy
+    for sub, counter in (("f", "FETCH_SIZE"), ("w", "WRITE_SIZE")):
+        _write_counters(tmp_path / sub, counter,
+                        [("void pkv::direct_kernel<64, 8, 2>(...)", 40.0),
+                         ("pkv::merge_kernel(...)", calib_kib * 4),
+                         ("pkv::append_kernel(...)", calib_kib * 8),
+                         ("at::native::copy_kernel", calib_kib)])
+    res = bench.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "t.json"),
+                                "c2_trellis")
+    assert res["kernels"] == ["direct_kernel"]
+    assert res["fetch"]["attn_dispatches"] == 1 and abs(res["fetch"]["scale"] - 1.0) < 1e-12
+    assert abs(res["bytes_per_launch"] - 2 * 40.0 * 1024) < 1e-6

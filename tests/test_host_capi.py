@@ -230,6 +230,7 @@ def test_c2_plan_reads_the_shared_prompt_once(direct, monkeypatch):
     assert st_["unique_blocks"] == 8 + 16 * 9
     assert st_["unique_tokens"] == 256 + 16 * 257
     assert st_["logical_tokens"] == 16 * 513
+    assert st_["direct"] == int(direct)
     if direct:
         # 16 queries x 4 kv heads with 513 keys each: one item per query, no merge
         assert st_["work_items"] == 16 and st_["merged_rows"] == 0
@@ -249,6 +250,7 @@ def test_direct_plan_limits(env, direct, monkeypatch):
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     st_ = c2_first_decode_stats()
+    assert st_["direct"] == int(direct)
     assert (st_["merged_rows"] == 0) == direct
     assert (st_["work_items"] == 16) == direct
 
