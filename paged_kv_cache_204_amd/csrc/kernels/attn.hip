@@ -65,13 +65,51 @@ __device__ __forceinline__ RowOf row_of(const AttnParams& p, int r) {
 
 // ---------------------------------------------------------------- MFMA path
 constexpr int kStep = 32;          // key tokens per step (two 16-token tiles)
-constexpr int kDepth = 2;          // steps of K/V requested ahead
 constexpr float kSlack = 8.f;      // log2 headroom of P above the reference max
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// global_load_lds_dwordx4: lane i copies the 16 bytes at `src` to LDS byte
+// lds + 16 i (lds wave-uniform, through M0).  Issued as inline assembly so
+// the compiler's wait insertion, which would treat the LDS write as aliasing
+// every later LDS read and drain all loads before them, leaves it alone: its
+// completion is awaited explicitly with wait_vmcnt.  (A load the compiler
+// tracks is still awaited correctly: these only add younger entries to the
+// in-order count.)  Nothing else in this file sets or reads M0.
+__device__ __forceinline__ void lds_dma16(const uint4* src, const void* lds) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_ptr)(lds)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 4-element rows named by lanes 4k + i / 4, for k = 0..3.
+__device__ __forceinline__ v4i16 lds_read_tr16(const void* at) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(at));
+}
+
+// s_waitcnt vmcnt(N), the other counters left alone (vmcnt sits in bits
+// 3:0 and 15:14 of the immediate, expcnt in 6:4, lgkmcnt in 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// A step's K or V tile in LDS: 32 token rows of D bf16 without padding.  The
+// 16-byte chunk c of row r sits in chunk slot c ^ tile_swz(r), so the 16 rows
+// that one MFMA operand read touches fall on distinct banks.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int tile_byte(int r, int c) { return r * (2 * D) + ((c ^ tile_swz<D>(r)) << 4); }
+
+constexpr int kBufs = 3;           // tiles in LDS: the step being read, the next two landing
 template <int D>
 struct MfmaSmem {
-  uint16_t k[2][kStep][D + 8];     // K rows, padded pitch
-  uint16_t vt[2][D][kStep + 4];    // V^T, pitch 18 words
+  char k[kBufs][kStep * D * 2];
+  char v[kBufs][kStep * D * 2];
 };
 
 // One 32-token step of the MFMA path for the RT row tiles of one wave:
@@ -180,23 +218,24 @@ __device__ __forceinline__ void mfma_tile(KOp kop, VOp vop, AfterQK after_qk,
   }
 }
 
-// One MFMA work item: the W waves share each 32-token K / V^T step staged in
-// LDS (double buffered, loads requested kDepth steps ahead), and each wave
-// runs mfma_tile on its own RT row tiles.
+// One MFMA work item.  The K and V tiles of each 32-token step go from global
+// memory straight into LDS (global_load_lds_dwordx4: lane i of one
+// instruction fills bytes 16 i .. 16 i + 15 of a 1 KB run), two steps ahead
+// into a ring of three tiles, so no registers hold them and no instructions
+// repack them; every wave then runs mfma_tile on its own RT row tiles, with
+// V^T read through the transposing LDS read.
 template <int D, int RT, int W>
 __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& it, int h,
                                           MfmaSmem<D>& sm, const int32_t* blk_s) {
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
   constexpr int CPR = D / 8;
-  constexpr int NT = 64 * W;                     // threads of the workgroup
-  constexpr int KCH = kStep * CPR;               // K chunks per step
-  constexpr int KPER = KCH >= NT ? KCH / NT : 1; // K chunks per thread per step
-  constexpr int VUNITS = 16 * CPR;               // (token pair, chunk) units per step
-  static_assert(KCH % NT == 0 || NT % KCH == 0, "K chunks split evenly over the threads");
+  constexpr int RUNS = kStep * CPR / 64;    // 1 KB runs per tile
+  constexpr int IPW = 2 * RUNS / W;         // K and V runs each wave loads per step
+  static_assert(IPW * W == 2 * RUNS, "a step's runs split evenly over the waves");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
   const int G = p.G;
@@ -240,85 +279,70 @@ __device__ __forceinline__ void mfma_item(const AttnParams& p, const WorkItem& i
     for (int dt = 0; dt < ND; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Staging: K chunk ci = tid + NT i is (token ci / CPR, 16-byte chunk
-  // ci % CPR; threads past the step's chunks load a duplicate and store
-  // nothing); V unit tid is chunk (tid / 16) of tokens 2q and 2q + 1
-  // (q = tid % 16), written transposed as 32-bit words (one dim, two tokens)
-  // -- with the 18-word V^T pitch the 64 lanes of a store hit 64 banks.
-  const bool v_on = tid < VUNITS;
-  const bool k_on = KCH >= NT || tid < KCH;
-  const int v_pair = tid & 15;
-  const int v_c = (tid >> 4) % CPR;
   const uint4* kb = layer_head_base(p, p.k_pool, h, D);
   const uint4* vb = layer_head_base(p, p.v_pool, h, D);
   const uint32_t blk_chunks = static_cast<uint32_t>(p.Hkv * p.B * D / 8);
   const int t_last = it.n_tok - 1;
-  auto ldg = [&](const uint4* src, int t, int c) {
-    t = min(t, t_last);
-    return src[chunk_index(blk_s[t >> p.log2B], blk_chunks, (t & (p.B - 1)) * (D / 8) + c)];
-  };
-  uint4 rk[kDepth][KPER], rv[kDepth][2];
-  auto fetch = [&](int slot, int t0) {
+  // Run j of a step (K runs first, then V): lane i fills chunk slot
+  // q = 64 (j % RUNS) + i of its tile, i.e. row q / CPR and chunk
+  // (q % CPR) ^ tile_swz(row).  Tokens past the end re-read the last token
+  // (masked in the softmax), so every run stays inside the pool.
+  auto issue = [&](int s) {
+    const int t0 = s * kStep;
+    const int b = s % kBufs;
 #pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int ci = (tid + NT * i) % KCH;
-      rk[slot][i] = ldg(kb, t0 + ci / CPR, ci % CPR);
+    for (int u = 0; u < IPW; ++u) {
+      const int j = wave * IPW + u;
+      const int q = (j % RUNS) * 64 + lane;
+      const int r = q / CPR;
+      const int c = (q % CPR) ^ tile_swz<D>(r);
+      const int t = min(t0 + r, t_last);
+      const uint32_t ci = chunk_index(blk_s[t >> p.log2B], blk_chunks, (t & (p.B - 1)) * CPR + c);
+      char* dst = (j >= RUNS ? sm.v[b] : sm.k[b]) + (j % RUNS) * 1024;
+      lds_dma16((j >= RUNS ? vb : kb) + ci, dst);
     }
-    rv[slot][0] = ldg(vb, t0 + 2 * v_pair, v_c);
-    rv[slot][1] = ldg(vb, t0 + 2 * v_pair + 1, v_c);
   };
   const int nsteps = (it.n_tok + kStep - 1) / kStep;
 
-  auto step = [&](int slot, int s) {
-    const int buf = s & 1;
-    if (k_on) {
+  issue(0);
+  issue(1);
+  // The query operands and masks were loaded first; taking them here makes
+  // the compiler's wait for them (which also drains the first two steps'
+  // runs, younger in the in-order count) land before the loop, not at their
+  // first use inside it, where it would drain every step's runs.
 #pragma unroll
-      for (int i = 0; i < KPER; ++i) {
-        const int ci = tid + NT * i;
-        *reinterpret_cast<uint4*>(&sm.k[buf][ci / CPR][(ci % CPR) * 8]) = rk[slot][i];
-      }
-    }
-    if (v_on) {
-      const uint32_t a[4] = {rv[slot][0].x, rv[slot][0].y, rv[slot][0].z, rv[slot][0].w};
-      const uint32_t b[4] = {rv[slot][1].x, rv[slot][1].y, rv[slot][1].z, rv[slot][1].w};
+  for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // (low halves of a and b), (high halves of a and b)
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][v_c * 8 + 2 * j][2 * v_pair]) =
-            __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][v_c * 8 + 2 * j + 1][2 * v_pair]) =
-            __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
-      }
-    }
+    for (int kk = 0; kk < NK; ++kk) asm volatile("" : "+v"(qf[rt][kk]));
+    asm volatile("" : "+v"(anc[rt]));
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    // this wave's runs of step s have landed (those of step s + 1 may still
+    // be in flight); the barrier shows every wave's runs to all, and orders
+    // the reads of the tile that step s + 2 overwrites before its runs
+    wait_vmcnt<IPW>();
     lds_barrier();
-    fetch(slot, (s + kDepth) * kStep);
-    if (!active) return;
-
+    issue(s + 2);
+    if (!active) continue;
+    const char* kt = sm.k[s % kBufs];
+    const char* vt = sm.v[s % kBufs];
     const auto kop = [&](int tt, int kk) {
-      return *reinterpret_cast<const bf16x8*>(&sm.k[buf][16 * tt + l16][32 * kk + 8 * g4]);
+      return *reinterpret_cast<const bf16x8*>(kt + tile_byte<D>(16 * tt + l16, 4 * kk + g4));
     };
+    // lane (l16, g4) of a 16-lane group names 4 dims of one token row; the
+    // transposed read hands lane i of the group dim 16 dt + i of 4 tokens
     const auto vop = [&](int dt) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(&sm.vt[buf][16 * dt + l16][4 * g4]);
-      const uint2 hi = *reinterpret_cast<const uint2*>(&sm.vt[buf][16 * dt + l16][16 + 4 * g4]);
-      uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      return *reinterpret_cast<bf16x8*>(&av);
+      const int r = 4 * g4 + (l16 >> 2);
+      const int c = 2 * dt + ((l16 & 3) >> 1);
+      const int off = (l16 & 1) * 8;
+      const v4i16 lo = lds_read_tr16(vt + tile_byte<D>(r, c) + off);
+      const v4i16 hi = lds_read_tr16(vt + tile_byte<D>(16 + r, c) + off);
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
     mfma_tile<D, RT>(kop, vop, [] {}, qf, anc, it, s * kStep, p.scale_log2, m_run, l_run, o);
-  };
-
-#pragma unroll
-  for (int j = 0; j < kDepth; ++j) fetch(j, j * kStep);
-  // whole rounds of the ring in the loop, the last partial round peeled, so
-  // the loop body has no load behind a branch and the waits before each
-  // staging store can count the loads still in flight
-  int s0 = 0;
-  for (; s0 + kDepth <= nsteps; s0 += kDepth) {
-#pragma unroll
-    for (int j = 0; j < kDepth; ++j) step(j, s0 + j);
   }
-#pragma unroll
-  for (int j = 0; j < kDepth - 1; ++j)
-    if (s0 + j < nsteps) step(j, s0 + j);
+  // the runs issued past the last step land before the workgroup ends
+  wait_vmcnt<0>();
 
   if (!active) return;
 #pragma unroll
@@ -740,15 +764,6 @@ __global__ __launch_bounds__(64 * W) void attn_kernel(const WorkItem* __restrict
 // read back transposed with ds_read_b64_tr_b16; a wave's loads run DEPTH of
 // its steps ahead and need only wave-level ordering.  At the end the waves'
 // softmax states (m, l, O) meet in LDS and are merged by log-sum-exp.
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
-
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
-// i % 4 of the 4-element rows named by lanes 4k + i / 4, for k = 0..3.
-__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* at) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(at));
-}
-
 template <int D, int W>
 union DirectSmem {
   uint16_t v[W][kStep][D + 8];   // each wave's V rows, padded pitch
