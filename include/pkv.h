@@ -199,7 +199,7 @@ typedef struct pkv_plan_stats {
   int32_t work_items;      /* workgroups per kv head */
   int32_t merged_rows;     /* query rows whose partial states are merged */
   int32_t direct;          /* 1: one workgroup per query and kv head (direct kernel) */
-  int32_t pad;
+  int32_t max_parts;       /* most partial states merged into one query (0: no merge) */
 } pkv_plan_stats;
 
 /* What paged_attn_decode would read and launch for these sequences (host only). */

@@ -65,7 +65,7 @@ class PkvPlanStats(ctypes.Structure):
     _fields_ = [("unique_tokens", ctypes.c_int64), ("logical_tokens", ctypes.c_int64),
                 ("unique_blocks", ctypes.c_int32), ("segments", ctypes.c_int32),
                 ("work_items", ctypes.c_int32), ("merged_rows", ctypes.c_int32),
-                ("direct", ctypes.c_int32), ("pad", ctypes.c_int32)]
+                ("direct", ctypes.c_int32), ("max_parts", ctypes.c_int32)]
 
 
 _lib = None
@@ -284,7 +284,7 @@ def paged_attn_decode_plan_stats(pool, seqs) -> dict:
     p, n = _seq_array(seqs)
     st = PkvPlanStats()
     _check(load().paged_attn_decode_plan_stats(pool, p, n, ctypes.byref(st)))
-    return {f: getattr(st, f) for f, _ in PkvPlanStats._fields_ if f != "pad"}
+    return {f: getattr(st, f) for f, _ in PkvPlanStats._fields_}
 
 
 def pkv_timing_enable(pool, enable=True):

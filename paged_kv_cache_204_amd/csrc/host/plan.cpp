@@ -31,6 +31,27 @@ int64_t chunk_cap(const PlanConfig& cfg, int32_t block_size) {
   return std::min<int64_t>(cfg.max_chunk, static_cast<int64_t>(cfg.max_chunk_blocks) * block_size);
 }
 
+// Lengthens the chunks (by whole multiples of the picked length, in units,
+// within the caps) until parts_of(chunk_m, chunk_v), the most partial states
+// any query gets, is at most cfg.max_parts or both chunks are at their caps:
+// chunks picked for parallelism alone can cut a long shared prefix into so
+// many pieces that merging them costs more than the attention itself.
+template <class PartsOf>
+void limit_parts(const PlanConfig& cfg, int32_t unit, int64_t cap_m, int64_t cap_v, int32_t* chunk_m,
+                 int32_t* chunk_v, PartsOf parts_of) {
+  if (cfg.max_parts <= 0) return;
+  const int32_t m0 = *chunk_m, v0 = *chunk_v;
+  for (int32_t f = 2; parts_of(*chunk_m, *chunk_v) > cfg.max_parts; ++f) {
+    if (*chunk_m >= cap_m && *chunk_v >= cap_v) break;
+    auto grow = [&](int32_t c0, int64_t cap) {
+      const int64_t c = ceil_div(static_cast<int64_t>(c0) * f, unit) * unit;
+      return static_cast<int32_t>(std::min(c, std::max<int64_t>(unit, (cap / unit) * unit)));
+    };
+    *chunk_m = grow(m0, cap_m);
+    *chunk_v = grow(v0, cap_v);
+  }
+}
+
 // Waves per MFMA workgroup: eight (one K/V tile staged for 256 rows) only
 // when the launch has no VALU items and some query tile fills 256 rows.
 int32_t pick_waves(const PlanConfig& cfg, bool any_valu, int32_t row_tiles, int64_t max_rows) {
@@ -292,9 +313,21 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     const int64_t per = std::max(1, (m ? mrows : cfg.valu_rows) / G);
     (m ? work_m : work_v) += static_cast<int64_t>(s.ntok) * ceil_div(static_cast<int64_t>(s.queries.size()), per);
   }
-  const int32_t chunk_v = pick_chunk(work_v, sh.num_kv_heads, unit, cfg.target_wgs, cap_v);
-  const int32_t chunk_m = pick_chunk(work_m, sh.num_kv_heads, unit,
-                                     cfg.target_mfma_wgs * 4 / plan->mfma_waves, cap);
+  int32_t chunk_v = pick_chunk(work_v, sh.num_kv_heads, unit, cfg.target_wgs, cap_v);
+  int32_t chunk_m = pick_chunk(work_m, sh.num_kv_heads, unit,
+                               cfg.target_mfma_wgs * 4 / plan->mfma_waves, cap);
+  {
+    std::vector<int32_t> parts(n_seqs);
+    limit_parts(cfg, unit, cap, cap_v, &chunk_m, &chunk_v, [&](int32_t cm, int32_t cv) {
+      std::fill(parts.begin(), parts.end(), 0);
+      int32_t most = 0;
+      for (const Segment& sg : segs) {
+        const int32_t n = static_cast<int32_t>(ceil_div(sg.ntok, is_mfma(sg) ? cm : cv));
+        for (int32_t q : sg.queries) most = std::max(most, parts[q] += n);
+      }
+      return most;
+    });
+  }
 
   std::vector<int32_t> n_parts(n_seqs, 0);
   for (const Segment& s : segs) {
@@ -380,9 +413,16 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   plan->segments = n_seqs;
   const int64_t cap = mfma ? chunk_cap(cfg, B)
                            : std::min<int64_t>(chunk_cap(cfg, B), cfg.valu_max_tokens);
-  const int32_t chunk = pick_chunk(work, sh.num_kv_heads, std::max(cfg.tile, B),
-                                   mfma ? cfg.target_mfma_wgs * 4 / plan->mfma_waves : cfg.target_wgs,
-                                   cap);
+  int32_t chunk = pick_chunk(work, sh.num_kv_heads, std::max(cfg.tile, B),
+                             mfma ? cfg.target_mfma_wgs * 4 / plan->mfma_waves : cfg.target_wgs,
+                             cap);
+  {
+    int32_t max_len = 0;
+    for (int32_t i = 0; i < n_seqs; ++i) max_len = std::max(max_len, st[i]->len);
+    int32_t unused = chunk;
+    limit_parts(cfg, std::max(cfg.tile, B), cap, cap, &chunk, &unused,
+                [&](int32_t c, int32_t) { return static_cast<int32_t>(ceil_div(max_len, c)); });
+  }
   std::vector<int32_t> n_parts(static_cast<size_t>(n_seqs) * n_nodes, 0);
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t len = st[i]->len;

@@ -45,6 +45,9 @@ struct PlanConfig {
                                      // partial states, no merge); 0 turns this off
   int32_t tile = 64;             // key tokens per kernel tile; chunks are multiples
   int32_t max_chunk = 4096;      // key tokens per work item at most
+  int32_t max_parts = kMergeInline;  // partial states per query at most where the chunk
+                                     // caps allow (beyond the merge row's inline list the
+                                     // merge walks the parts serially); 0 = no limit
   int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)
 };
 

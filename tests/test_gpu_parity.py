@@ -135,6 +135,10 @@ PATHS = {
     "auto": {},
     "split": {"PKV_DIRECT_MAX_TOKENS": "0"},
     "direct": {"PKV_DIRECT_MAX_TOKENS": "100000", "PKV_DIRECT_MAX_WGS": "100000"},
+    # split path with the chunk lengths picked for parallelism alone: long
+    # shared prefixes give queries more partial states than a merge row
+    # carries inline, so the merge walks its part list
+    "manyparts": {"PKV_DIRECT_MAX_TOKENS": "0", "PKV_MAX_PARTS": "0"},
 }
 
 
@@ -221,7 +225,8 @@ KNOBS = [
     {"PKV_MFMA_WAVES": "8", "PKV_MFMA_ROW_TILES": "2", **_SPLIT},
     {"PKV_MFMA_ROW_TILES": "1", **_SPLIT},
     {"PKV_TARGET_MFMA_WGS": "16", "PKV_TARGET_WGS": "16", **_SPLIT},
-    {"PKV_TARGET_MFMA_WGS": "4096", "PKV_TARGET_WGS": "4096", "PKV_MAX_CHUNK": "64", **_SPLIT},
+    {"PKV_TARGET_MFMA_WGS": "4096", "PKV_TARGET_WGS": "4096", "PKV_MAX_CHUNK": "64", "PKV_MAX_PARTS": "0",
+     **_SPLIT},
     {"PKV_MFMA_MIN_ROWS": "0", **_SPLIT},
     {"PKV_UNSHARE_MAX_QUERIES": "0", **_SPLIT},
     {"PKV_UNSHARE_MAX_QUERIES": "64", "PKV_UNSHARE_MAX_TOKENS": "100000", **_SPLIT},
@@ -260,7 +265,8 @@ def sample_ops(wl, every):
 @pytest.mark.parametrize("name,every,path", [
     ("c1_tiny_fork", 1, "auto"), ("c1_tiny_fork", 1, "split"),
     ("c2_trellis", 23, "auto"), ("c2_trellis", 23, "split"),
-    ("c3_dendrite", 9, "auto"), ("c3_dendrite", 31, "direct"), ("c3_dendrite_aligned", 31, "auto"),
+    ("c3_dendrite", 9, "auto"), ("c3_dendrite", 31, "direct"), ("c3_dendrite", 31, "manyparts"),
+    ("c3_dendrite_aligned", 31, "auto"),
     ("c4_mcts", 1, "auto"), ("c4_mcts_folded", 1, "auto"), ("c5_verify", 1, "auto"),
 ])
 def test_full_workload_parity(dev, name, every, path, monkeypatch):

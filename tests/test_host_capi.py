@@ -239,6 +239,49 @@ def test_c2_plan_reads_the_shared_prompt_once(direct, monkeypatch):
         assert st_["work_items"] > 16 and st_["merged_rows"] == 16 * 32
 
 
+def first_decode_stats(name, env, monkeypatch):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    wl = synth.named(name)
+    s = wl.shape
+    desc = dict(num_blocks=s.num_blocks, block_size=s.block_size, num_layers=s.num_layers,
+                num_q_heads=s.num_q_heads, num_kv_heads=s.num_kv_heads, head_dim=s.head_dim)
+    pool = pkv.kv_pool_create(desc, None, None, free_order=wl.free_order())
+    try:
+        hs = {}
+        for op in wl.ops:
+            if op[0] == "alloc":
+                hs[op[1]] = pkv.seq_allocate(pool)
+            elif op[0] == "fork":
+                hs[op[2]] = pkv.seq_fork(pool, hs[op[1]])
+            elif op[0] == "append":
+                pkv.kv_append(pool, [hs[h] for h in op[1]], op[2], None, None, None)
+            elif op[0] == "decode":
+                return pkv.paged_attn_decode_plan_stats(pool, [hs[h] for h in op[1]])
+    finally:
+        pkv.kv_pool_destroy(pool)
+
+
+def test_long_shared_prefix_is_cut_into_few_parts(monkeypatch):
+    """The Dendrite fork (4096 shared tokens under 6 branches): chunks picked
+    for parallelism alone give every query 69 partial states; the planner
+    lengthens them until no query has more than max_parts (the merge row's
+    inline list by default).  What the call reads does not change."""
+    unlimited = first_decode_stats("c3_dendrite", {"PKV_MAX_PARTS": "0"}, monkeypatch)
+    assert unlimited["max_parts"] == 69
+    for limit in (24, 12, 8, 6):
+        st_ = first_decode_stats("c3_dendrite", {"PKV_MAX_PARTS": str(limit)}, monkeypatch)
+        assert 1 < st_["max_parts"] <= limit, limit
+        assert st_["work_items"] < unlimited["work_items"]
+        for k in ("unique_tokens", "unique_blocks", "logical_tokens", "merged_rows", "segments"):
+            assert st_[k] == unlimited[k], k
+    default = first_decode_stats("c3_dendrite", {}, monkeypatch)
+    assert default["max_parts"] <= 12
+    # a limit that the chunk caps cannot reach: the chunks stop at the caps
+    st_ = first_decode_stats("c3_dendrite", {"PKV_MAX_PARTS": "1"}, monkeypatch)
+    assert st_["max_parts"] > 1
+
+
 @pytest.mark.parametrize("env,direct", [
     ({}, True),
     ({"PKV_DIRECT_MAX_TOKENS": "512"}, False),   # queries hold 513 keys
