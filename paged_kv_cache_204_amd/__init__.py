@@ -123,6 +123,8 @@ def _check(code):
 def _addr(x):
     if x is None:
         return None
+    if type(x) is int:
+        return x or None
     dp = getattr(x, "data_ptr", None)
     if dp is not None:
         contiguous = getattr(x, "is_contiguous", None)
