@@ -114,7 +114,8 @@ struct pkv_pool {
   hipEvent_t stage_ev[kStageSlots] = {};
   bool stage_used[kStageSlots] = {};
   int stage_next = 0;
-  // decode plan cache: same sequence list on an unchanged pool -> reuse
+  // decode plan cache: same sequence list on an unchanged pool -> reuse;
+  // after appends that only filled the last blocks -> patch (patch_decode)
   bool dcache_valid = false;
   uint64_t dcache_version = 0;
   std::vector<int64_t> dcache_seqs;
@@ -476,9 +477,22 @@ pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, in
   DeviceGuard g(p->dev);
   PKV_HIP(g.err);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool hit = p->dcache_valid && p->dcache_version == p->core.version() &&
-                   p->dcache_seqs.size() == static_cast<size_t>(n_seqs) &&
-                   std::memcmp(p->dcache_seqs.data(), seqs, n_seqs * sizeof(int64_t)) == 0;
+  const bool same_seqs = p->dcache_valid && p->dcache_seqs.size() == static_cast<size_t>(n_seqs) &&
+                         std::memcmp(p->dcache_seqs.data(), seqs, n_seqs * sizeof(int64_t)) == 0;
+  bool hit = same_seqs && p->dcache_version == p->core.version();
+  if (same_seqs && !hit && pkv::patch_decode(p->core, seqs, n_seqs, p->cfg, &p->dplan)) {
+    // appends only filled the sequences' last blocks: same plan, longer tail items
+    if (!plan_fits_kernels(p->dplan, p->core.shape()))
+      return fail(PKV_ERR_ARG, "paged_attn_decode: internal plan exceeds the kernels' tile limits");
+    pkv_status s = upload(p, p->decode_plan, p->dlayout.total, st,
+                          [&](char* dst) { serialize(p->dplan, p->dlayout, dst); });
+    if (s != PKV_OK) {
+      p->dcache_valid = false;
+      return s;
+    }
+    p->dcache_version = p->core.version();
+    hit = true;
+  }
   if (!hit) {
     p->dcache_valid = false;
     std::string why;

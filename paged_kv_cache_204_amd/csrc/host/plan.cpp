@@ -14,6 +14,7 @@ struct Segment {
   const int32_t* blocks;         // the segment's first block in a member's table
   int32_t nblk;
   int32_t ntok;
+  bool ends;                     // the segment holds its queries' last blocks
 };
 
 // Chunk length in tokens: spread `work_tokens` (token x row-subset units,
@@ -113,6 +114,17 @@ void finish_parts(Plan* plan, const std::vector<int32_t>& n_parts, int32_t hq) {
   for (RowGroup& g : plan->groups) g.merge = merge_of[g.q_index];
 }
 
+// Items (launch order: MFMA, VALU, direct) that end at a query's last key.
+void list_tails(Plan* plan) {
+  plan->tail_items.clear();
+  int32_t k = 0;
+  for (const auto* items : {&plan->mfma, &plan->valu, &plan->direct})
+    for (const WorkItem& it : *items) {
+      if (it.tail_q > 0) plan->tail_items.push_back(k);
+      ++k;
+    }
+}
+
 // Copies every item's block list to a fixed-stride slot (MFMA items first,
 // as the kernel numbers them, then VALU, then direct items), padding with the
 // item's last block.
@@ -167,6 +179,8 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
       return Err::empty;
     }
     plan->logical_tokens += st[i]->len;
+    plan->q_epoch.push_back(st[i]->epoch);
+    plan->q_len.push_back(st[i]->len);
   }
   auto nblk = [&](int32_t q) { return static_cast<int32_t>(st[q]->table.size()); };
   auto fill = [&](int32_t q, int32_t pos) {
@@ -232,6 +246,8 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
         sg.blocks = t0.data() + f.pos;
         sg.nblk = e - f.pos;
         sg.ntok = (sg.nblk - 1) * B + fill(f.qs[0], e - 1);
+        sg.ends = true;
+        for (int32_t q : f.qs) sg.ends = sg.ends && nblk(q) == e;
         segs.push_back(std::move(sg));
       }
     }
@@ -275,6 +291,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
       it.grp_off = static_cast<int32_t>(plan->groups.size());
       it.n_grp = 1;
       it.part_base = -1;
+      it.tail_q = 1 + q;
       it.q_index[0] = q;
       plan->groups.push_back(RowGroup{q, -1, 0u, 0u, -1, {0, 0, 0}});
       plan->blocks.insert(plan->blocks.end(), st[q]->table.begin(), st[q]->table.end());
@@ -283,6 +300,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     std::stable_sort(plan->direct.begin(), plan->direct.end(),
                      [](const WorkItem& a, const WorkItem& b) { return a.n_tok > b.n_tok; });
     pack_item_blocks(plan, B);
+    list_tails(plan);
     return Err::ok;
   }
 
@@ -352,7 +370,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
         it.grp_off = grp_off;
         it.n_grp = ng;
         it.part_base = -1;
-        it.pad = 0;
+        it.tail_q = s.ends && c == nchunk - 1 ? 1 + s.queries[u0] : 0;
         for (int32_t u = 0; u < 8; ++u)
           it.q_index[u] = u < ng ? plan->groups[grp_off + u].q_index : 0;
         (mfma ? plan->mfma : plan->valu).push_back(it);
@@ -361,7 +379,51 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
   }
   finish_parts(plan, n_parts, sh.num_q_heads);
   pack_item_blocks(plan, B);
+  list_tails(plan);
   return Err::ok;
+}
+
+bool patch_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, const PlanConfig& cfg,
+                  Plan* plan) {
+  if (plan->q_epoch.size() != static_cast<size_t>(n_seqs)) return false;
+  std::vector<int32_t> grow(n_seqs);
+  std::vector<int32_t> last_block(n_seqs);
+  for (int32_t q = 0; q < n_seqs; ++q) {
+    const SeqState* st = pool.find(seqs[q]);
+    if (!st || st->epoch != plan->q_epoch[q] || st->len < plan->q_len[q]) return false;
+    if (!plan->direct.empty() && st->len > cfg.direct_max_tokens) return false;
+    grow[q] = st->len - plan->q_len[q];
+    last_block[q] = st->table.back();
+  }
+  auto item_at = [&](int32_t k) -> WorkItem& {
+    if (k < static_cast<int32_t>(plan->mfma.size())) return plan->mfma[k];
+    k -= static_cast<int32_t>(plan->mfma.size());
+    if (k < static_cast<int32_t>(plan->valu.size())) return plan->valu[k];
+    return plan->direct[k - plan->valu.size()];
+  };
+  // every query of a tail item ends in the same (unchanged) last block, so
+  // all of them grew alike; check it before changing anything
+  for (int32_t k : plan->tail_items) {
+    const WorkItem& it = item_at(k);
+    const int32_t d = grow[it.tail_q - 1];
+    for (int32_t u = 0; u < it.n_grp; ++u)
+      if (grow[plan->groups[it.grp_off + u].q_index] != d) return false;
+  }
+  for (int32_t k : plan->tail_items) {
+    WorkItem& it = item_at(k);
+    it.n_tok += grow[it.tail_q - 1];
+  }
+  // what the call reads: the new keys of each distinct last block once
+  std::vector<std::pair<int32_t, int32_t>> fresh;
+  for (int32_t q = 0; q < n_seqs; ++q) {
+    plan->logical_tokens += grow[q];
+    if (grow[q] > 0) fresh.emplace_back(last_block[q], grow[q]);
+    plan->q_len[q] += grow[q];
+  }
+  std::sort(fresh.begin(), fresh.end());
+  fresh.erase(std::unique(fresh.begin(), fresh.end()), fresh.end());
+  for (const auto& f : fresh) plan->unique_tokens += f.second;
+  return true;
 }
 
 Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
@@ -461,7 +523,7 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
         it.grp_off = grp_off;
         it.n_grp = ng;
         it.part_base = -1;
-        it.pad = 0;
+        it.tail_q = 0;
         for (int32_t u = 0; u < 8; ++u)
           it.q_index[u] = u < ng ? plan->groups[grp_off + u].q_index : 0;
         (mfma ? plan->mfma : plan->valu).push_back(it);

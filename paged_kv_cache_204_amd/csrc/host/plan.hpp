@@ -73,6 +73,11 @@ struct Plan {
   int64_t logical_tokens = 0;
   int32_t unique_blocks = 0;
   int32_t segments = 0;
+  // decode plans: each query's table epoch and length when planned, and the
+  // items (launch order: MFMA, VALU, direct) that end at a query's last key
+  std::vector<uint64_t> q_epoch;
+  std::vector<int32_t> q_len;
+  std::vector<int32_t> tail_items;
 
   // Empties the plan for reuse; the vectors keep their capacity, so
   // repeated planning of similar calls does not allocate.
@@ -92,11 +97,22 @@ struct Plan {
     valu_max_rows = 0;
     unique_tokens = logical_tokens = 0;
     unique_blocks = segments = 0;
+    q_epoch.clear();
+    q_len.clear();
+    tail_items.clear();
   }
 };
 
 Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
                 const PlanConfig& cfg, Plan* plan, std::string* why);
+
+// Brings a decode plan for the same sequence list up to date without
+// replanning when no table changed since it was made (same epochs) and the
+// sequences only grew, i.e. appends filled their last blocks: the items that
+// end at a query's last key take the new keys.  False (plan untouched) when
+// that does not hold; the caller then plans afresh.
+bool patch_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, const PlanConfig& cfg,
+                  Plan* plan);
 
 Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
                 int32_t n_nodes, const int32_t* parent, const PlanConfig& cfg,

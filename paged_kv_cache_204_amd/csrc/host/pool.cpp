@@ -30,7 +30,9 @@ BlockPool::BlockPool(const Shape& s, const int32_t* free_order)
 
 int64_t BlockPool::allocate() {
   int64_t id = next_id_++;
-  seqs_.emplace(id, SeqState{});
+  SeqState s;
+  s.epoch = ++epochs_;
+  seqs_.emplace(id, std::move(s));
   ++version_;
   return id;
 }
@@ -47,6 +49,7 @@ Err BlockPool::fork(int64_t parent, int64_t* child, std::string* why) {
     return Err::seq;
   }
   SeqState copy = it->second;  // table pointers only; no K/V moves
+  copy.epoch = ++epochs_;
   for (int32_t b : copy.table) ++rc_[b];
   int64_t id = next_id_++;
   seqs_.emplace(id, std::move(copy));
@@ -124,6 +127,7 @@ Err BlockPool::prepare_append(const int64_t* seqs, int32_t n_seqs, int32_t n_tok
         const int32_t b = fifo_[taken++];
         rcm[b] = 1;
         s.table.push_back(b);
+        s.epoch = 0;   // a new one at commit
       } else if (rc_of(s.table.back()) > 1) {
         if (taken >= fifo_.size()) {
           *why = "kv_append: pool exhausted (" + std::to_string(fifo_.size()) + " free blocks)";
@@ -134,6 +138,7 @@ Err BlockPool::prepare_append(const int64_t* seqs, int32_t n_seqs, int32_t n_tok
         rcm[dst] = 1;
         rcm[src] = rc_of(src) - 1;
         s.table.back() = dst;
+        s.epoch = 0;
         out->result.cow.push_back(CowCopy{src, dst, off});
       }
       out->result.slots[static_cast<size_t>(i) * n_tok + j] = s.table[s.len / B] * B + off;
@@ -150,7 +155,10 @@ Err BlockPool::prepare_append(const int64_t* seqs, int32_t n_seqs, int32_t n_tok
 void BlockPool::commit_append(PendingAppend&& pa) {
   for (size_t k = 0; k < pa.taken; ++k) fifo_.pop_front();
   for (const auto& br : pa.refcounts) rc_[br.first] = br.second;
-  for (auto& ss : pa.states) seqs_[ss.first] = std::move(ss.second);
+  for (auto& ss : pa.states) {
+    if (ss.second.epoch == 0) ss.second.epoch = ++epochs_;
+    seqs_[ss.first] = std::move(ss.second);
+  }
   if (!pa.states.empty()) ++version_;
   last_append_ = std::move(pa.result);
 }

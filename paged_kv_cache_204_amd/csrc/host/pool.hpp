@@ -47,6 +47,10 @@ bool valid_shape(const Shape& s, std::string* why);
 struct SeqState {
   std::vector<int32_t> table;
   int32_t len = 0;
+  // Changes whenever the table does (allocate, fork, an append that adds or
+  // replaces a block), never when an append only fills the last block;
+  // unique over the pool's life, so a reused id never repeats one.
+  uint64_t epoch = 0;
 };
 
 struct CowCopy {
@@ -104,6 +108,7 @@ class BlockPool {
   std::unordered_map<int64_t, SeqState> seqs_;
   int64_t next_id_ = 0;
   uint64_t version_ = 0;
+  uint64_t epochs_ = 0;
   AppendResult last_append_;
 };
 

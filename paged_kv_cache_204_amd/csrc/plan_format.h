@@ -31,7 +31,7 @@ struct WorkItem {
   int32_t grp_off;
   int32_t n_grp;
   int32_t part_base;
-  int32_t pad;
+  int32_t tail_q;    // host side: 1 + the query whose last key ends this item, else 0
   // query vectors of the first min(n_grp, 8) row groups, so the query loads
   // need only the item itself
   int32_t q_index[8];
