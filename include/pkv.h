@@ -209,10 +209,12 @@ pkv_status paged_attn_decode_plan_stats(pkv_pool* pool, const int64_t* seqs,
 /* ---- kernel timing (benchmarks) --------------------------------------- */
 
 /* enable = n > 0: every n-th paged_attn_decode / paged_attn_tree_verify call
- * records a pair of HIP events on its stream around its attention kernel (the
- * plan upload and the partial-state merge kernel stay outside); sampling
- * keeps the event records from slowing the calls they measure.  enable = 0
- * turns timing off and drops pending pairs; negative values are an error. */
+ * times its attention kernel with a pair of HIP events attached to that
+ * kernel's own dispatch (hipExtLaunchKernel: they take the kernel's start and
+ * end, not the time of separate markers; the plan upload and the
+ * partial-state merge kernel stay outside); sampling keeps the timing from
+ * slowing the calls it measures.  enable = 0 turns timing off and drops
+ * pending pairs; negative values are an error. */
 pkv_status pkv_timing_enable(pkv_pool* pool, int32_t enable);
 
 /* Synchronise the recorded events and return the summed kernel time in ms

@@ -209,8 +209,9 @@ bool plan_fits_kernels(const pkv::Plan& plan, const pkv::Shape& sh) {
 }
 
 // The attention kernel of one call (the direct kernel for direct plans)
-// and, when some queries have several partial states, the merge kernel.  With timing enabled, a pair of events
-// brackets the attention kernel alone.
+// and, when some queries have several partial states, the merge kernel.
+// With timing enabled, a pair of events takes the attention kernel's own
+// start and end.
 pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
                           const DevBuf& buf, int32_t layer, const void* q, float sm_scale,
                           float* out, float* lse, hipStream_t stream) {
@@ -254,18 +255,15 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
     s = take_event(p, &ev_a);
     if (s == PKV_OK) s = take_event(p, &ev_b);
     if (s != PKV_OK) return s;
-    PKV_HIP(hipEventRecord(ev_a, stream));
   }
+  // the events ride on the kernel's own dispatch: they take its start and end
   if (plan.direct.empty())
     PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles,
-                              plan.valu_max_rows * ap.G, plan.mfma_waves, stream));
+                              plan.valu_max_rows * ap.G, plan.mfma_waves, stream, ev_a, ev_b));
   else
     PKV_HIP(pkv::launch_direct(ap, static_cast<int32_t>(plan.direct.size()), sh.head_dim,
-                                plan.stride_direct, stream));
-  if (timed) {
-    PKV_HIP(hipEventRecord(ev_b, stream));
-    p->ev_pending.emplace_back(ev_a, ev_b);
-  }
+                                plan.stride_direct, stream, ev_a, ev_b));
+  if (timed) p->ev_pending.emplace_back(ev_a, ev_b);
   if (!plan.merges.empty()) {
     pkv::MergeParams mp{};
     mp.merges = reinterpret_cast<const pkv::MergeRow*>(base + lay.merges);

@@ -49,15 +49,17 @@ struct AttnParams {
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 // valu_rows: the most rows any VALU item of the launch holds (<= 8);
-// waves: 4, or 8 for launches of MFMA items only (row_tiles 2).
+// waves: 4, or 8 for launches of MFMA items only (row_tiles 2).  Non-null
+// events take the start and end times of the kernel's own dispatch.
 hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t row_tiles,
-                       int32_t valu_rows, int32_t waves, hipStream_t s);
+                       int32_t valu_rows, int32_t waves, hipStream_t s, hipEvent_t ev_start = nullptr,
+                       hipEvent_t ev_stop = nullptr);
 
 // Direct decode: one workgroup per (item, kv head), each item one query
 // over all of its keys (n_grp 1, tail_start INT_MAX), written straight to
 // out / lse; items[i]'s block list at blocks + i * stride (<= kMaxItemBlocks).
 hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
-                         hipStream_t s);
+                         hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Log-sum-exp merge of the partial states of several work items.
 struct MergeParams {

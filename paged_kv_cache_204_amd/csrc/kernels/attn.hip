@@ -22,6 +22,7 @@
 // this launch would need device-scope release/acquire fences per workgroup;
 // on this GPU those write back and invalidate the whole L2 of an XCD, which
 // costs far more than a second launch and evicts shared blocks.)
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "../kernels.hpp"
@@ -77,10 +78,16 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // every later LDS read and drain all loads before them, leaves it alone: its
 // completion is awaited explicitly with wait_vmcnt.  (A load the compiler
 // tracks is still awaited correctly: these only add younger entries to the
-// in-order count.)  Nothing else in this file sets or reads M0.
+// in-order count.)
 __device__ __forceinline__ void lds_dma16(const uint4* src, const void* lds) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_ptr)(lds)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+  uint32_t saved;
+  // M0 is put back as it was, so the compiler's own use of it is undisturbed
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(m0)
+      : "memory");
 }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
@@ -923,40 +930,42 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
 }  // namespace
 
 template <int D, int RT>
-hipError_t launch_rows(const AttnParams& p, dim3 grid, int32_t valu_rows, int32_t waves, hipStream_t s) {
+hipError_t launch_rows(const AttnParams& p, dim3 grid, int32_t valu_rows, int32_t waves, hipStream_t s,
+                       hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (waves == 8) {
     if constexpr (RT == 2)
-      hipLaunchKernelGGL((attn_kernel<D, RT, 4, 8>), grid, dim3(512), 0, s, p.items, p.blocks, p.groups,
+      hipExtLaunchKernelGGL((attn_kernel<D, RT, 4, 8>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.groups,
                          p.q, p.n_mfma, p.stride_mfma, p.stride_valu, p);
     else
       return hipErrorInvalidValue;
   } else if (valu_rows <= 4) {
-    hipLaunchKernelGGL((attn_kernel<D, RT, 4, 4>), grid, dim3(kThreads), 0, s, p.items, p.blocks, p.groups,
+    hipExtLaunchKernelGGL((attn_kernel<D, RT, 4, 4>), grid, dim3(kThreads), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.groups,
                        p.q, p.n_mfma, p.stride_mfma, p.stride_valu, p);
   } else {
-    hipLaunchKernelGGL((attn_kernel<D, RT, 8, 4>), grid, dim3(kThreads), 0, s, p.items, p.blocks, p.groups,
+    hipExtLaunchKernelGGL((attn_kernel<D, RT, 8, 4>), grid, dim3(kThreads), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.groups,
                        p.q, p.n_mfma, p.stride_mfma, p.stride_valu, p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t row_tiles,
-                       int32_t valu_rows, int32_t waves, hipStream_t s) {
+                       int32_t valu_rows, int32_t waves, hipStream_t s, hipEvent_t ev_start,
+                       hipEvent_t ev_stop) {
   if (n_items == 0) return hipSuccess;
   if (waves == 8 && n_items != p.n_mfma) return hipErrorInvalidValue;
   const int64_t n_wg = static_cast<int64_t>(n_items) * p.Hkv;
   if (n_wg > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(n_wg));
-  if (head_dim == 64 && row_tiles == 1) return launch_rows<64, 1>(p, grid, valu_rows, waves, s);
-  if (head_dim == 64 && row_tiles == 2) return launch_rows<64, 2>(p, grid, valu_rows, waves, s);
-  if (head_dim == 128 && row_tiles == 1) return launch_rows<128, 1>(p, grid, valu_rows, waves, s);
-  if (head_dim == 128 && row_tiles == 2) return launch_rows<128, 2>(p, grid, valu_rows, waves, s);
+  if (head_dim == 64 && row_tiles == 1) return launch_rows<64, 1>(p, grid, valu_rows, waves, s, ev_start, ev_stop);
+  if (head_dim == 64 && row_tiles == 2) return launch_rows<64, 2>(p, grid, valu_rows, waves, s, ev_start, ev_stop);
+  if (head_dim == 128 && row_tiles == 1) return launch_rows<128, 1>(p, grid, valu_rows, waves, s, ev_start, ev_stop);
+  if (head_dim == 128 && row_tiles == 2) return launch_rows<128, 2>(p, grid, valu_rows, waves, s, ev_start, ev_stop);
   return hipErrorInvalidValue;
 }
 
 
 hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
-                         hipStream_t s) {
+                         hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (n_items == 0) return hipSuccess;
   if (stride < 1 || stride > kMaxItemBlocks || p.G > 16) return hipErrorInvalidValue;
   const int64_t n_wg = static_cast<int64_t>(n_items) * p.Hkv;
@@ -965,9 +974,9 @@ hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim,
   // eight waves at head_dim 64; at 128 a wave's loads in flight need more
   // registers than eight waves per workgroup leave, so four
   if (head_dim == 64)
-    hipLaunchKernelGGL((direct_kernel<64, 8, 2>), grid, dim3(512), 0, s, p.items, p.blocks, p.q, stride, p);
+    hipExtLaunchKernelGGL((direct_kernel<64, 8, 2>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.q, stride, p);
   else if (head_dim == 128)
-    hipLaunchKernelGGL((direct_kernel<128, 4, 2>), grid, dim3(256), 0, s, p.items, p.blocks, p.q, stride, p);
+    hipExtLaunchKernelGGL((direct_kernel<128, 4, 2>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.q, stride, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
