@@ -13,8 +13,9 @@ Contents:
   free.  It also keeps its own copy of every block's K/V bits.
 * :mod:`oracle.attention` -- textbook softmax attention in float64 over each
   sequence's keys, gathered token by token through its block table; decode
-  (one query per sequence) and draft-tree verify (context plus tree
-  ancestors and the node itself).
+  (one query per sequence), draft-tree verify (context plus tree
+  ancestors and the node itself) and causal prefill of a sequence's newest
+  tokens over its whole cache.
 * :mod:`oracle.run` -- runs a ``synth`` op program through the two.
 
 Every function here is pinned by the ``-m "not gpu"`` tests against facts the
@@ -24,7 +25,7 @@ invariants, a library attention routine, numbers the pages print); none is
 """
 
 from .pool import PoolModel, PoolError, OOMError, SeqError, ArgError, EmptyError
-from .attention import bf16_bits_to_f64, attend, decode, tree_verify, tree_key_positions
+from .attention import bf16_bits_to_f64, attend, decode, prefill, tree_verify, tree_key_positions
 from .run import run_program
 
 __all__ = [
@@ -37,6 +38,7 @@ __all__ = [
     "bf16_bits_to_f64",
     "attend",
     "decode",
+    "prefill",
     "tree_verify",
     "tree_key_positions",
     "run_program",

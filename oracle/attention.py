@@ -131,3 +131,49 @@ def tree_verify(pool, layer, seqs, parents, q_bits, sm_scale):
                 out[i, j, rows], lse[i, j, rows] = attend(
                     q[i, j, rows], k[pos, kvh], v[pos, kvh], sm_scale)
     return out, lse
+
+
+def prefill(pool, layer, seqs, n_new, q_bits, sm_scale):
+    """Causal attention of each sequence's newest tokens over its whole cache.
+
+    After a prefix match only the unmatched part of a prompt is computed
+    (SGLang RadixAttention page, "Three core operations", prefix matching:
+    the forward pass runs over the n - k tokens that missed); those tokens
+    are appended first, and token ``t`` attends to tokens ``0..t`` -- the
+    causal rule of the Trellis page's section "LLM prefill and KV cache".
+
+    ``n_new[i]`` tokens of sequence ``i`` are new: they are its last
+    ``n_new[i]`` tokens, at positions ``len - n_new[i] .. len - 1``.  ``q_bits``
+    uint16 ``[sum(n_new)][Hq][D]`` holds their queries, sequence after
+    sequence.  Query ``j`` of sequence ``i`` attends to positions
+    ``0 .. len - n_new[i] + j``.
+    Returns float64 ``out [sum(n_new)][Hq][D]`` and ``lse [sum(n_new)][Hq]``.
+    """
+    q = bf16_bits_to_f64(q_bits)
+    n_new = [int(x) for x in n_new]
+    if len(n_new) != len(seqs):
+        raise ArgError("one new-token count per sequence")
+    total = sum(n_new)
+    if q.shape[0] != total:
+        raise ArgError("q must hold sum(n_new) query vectors")
+    _, hq, d = q.shape
+    g = _group(hq, pool.Hkv)
+    out = np.empty((total, hq, d))
+    lse = np.empty((total, hq))
+    row = 0
+    for sid, n in zip(seqs, n_new):
+        kb, vb = pool.gather_bits(sid, layer)
+        length = kb.shape[0]
+        if n < 0 or n > length:
+            raise ArgError("more new tokens than the sequence holds")
+        k = bf16_bits_to_f64(kb)
+        v = bf16_bits_to_f64(vb)
+        ctx = length - n
+        for j in range(n):
+            visible = ctx + j + 1            # keys 0 .. ctx + j
+            for kvh in range(pool.Hkv):
+                rows = slice(kvh * g, (kvh + 1) * g)
+                out[row, rows], lse[row, rows] = attend(
+                    q[row, rows], k[:visible, kvh], v[:visible, kvh], sm_scale)
+            row += 1
+    return out, lse

@@ -2,7 +2,7 @@
 
 from __future__ import annotations
 
-from .attention import decode, tree_verify
+from .attention import decode, prefill, tree_verify
 from .pool import PoolModel
 
 
@@ -13,7 +13,7 @@ def run_program(workload, store_data=True, want=None, free_order=_DEFAULT):
     """Execute ``workload.ops`` on a fresh :class:`PoolModel`.
 
     Yields ``(index, op, pool, handles, result)`` after every op, where
-    ``result`` is ``(out, lse)`` for decode/verify ops whose index is in
+    ``result`` is ``(out, lse)`` for decode/verify/prefill ops whose index is in
     ``want`` (all of them when ``want`` is None) and None otherwise.
     ``free_order`` overrides the workload's initial free-list order.
     """
@@ -51,6 +51,12 @@ def run_program(workload, store_data=True, want=None, free_order=_DEFAULT):
                 q = workload.verify_query(key, len(hs), n_nodes)
                 result = tree_verify(pool, layer, [handles[h] for h in hs],
                                      parents, q, workload.sm_scale)
+        elif kind == "prefill":
+            hs, layer, n_new, key = op[1], op[2], op[3], op[4]
+            if store_data and (want is None or idx in want):
+                q = workload.prefill_query(key, sum(n_new))
+                result = prefill(pool, layer, [handles[h] for h in hs], n_new, q,
+                                 workload.sm_scale)
         else:
             raise ValueError(f"unknown op {kind}")
         yield idx, op, pool, handles, result

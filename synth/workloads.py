@@ -16,6 +16,9 @@ Ops (tuples):
   ``n_nodes`` tokens of every sequence in ``hs`` are the tree's nodes (in node
   order); parents from :meth:`Workload.tree_parents`, Q from
   :meth:`Workload.verify_query`
+* ``("prefill", hs, layer, n_new, key)``    causal attention of the newest
+  ``n_new[i]`` tokens of sequence ``hs[i]`` (already appended) over its whole
+  cache; Q from :meth:`Workload.prefill_query`
 
 Random draws use ``numpy.random.default_rng([cfg_id, stream, key])`` so every
 tensor depends on the logical op that consumes it, never on where a pool puts
@@ -95,6 +98,13 @@ class Workload:
         s = self.shape
         q = self._rng(STREAM_Q, key).standard_normal(
             (n_seqs, n_nodes, s.num_q_heads, s.head_dim), dtype=np.float32)
+        return f32_to_bf16_bits(q)
+
+    def prefill_query(self, key: int, n_queries: int):
+        """bf16 bits of Q, ``[n_queries][Hq][D]`` (uint16), sequence after sequence."""
+        s = self.shape
+        q = self._rng(STREAM_Q, key).standard_normal(
+            (n_queries, s.num_q_heads, s.head_dim), dtype=np.float32)
         return f32_to_bf16_bits(q)
 
     def tree_parents(self, key: int, n_seqs: int, n_nodes: int):
@@ -256,6 +266,35 @@ def verify_workload(name, cfg_id, shape, n_seqs, ctx_len, n_nodes, tree_depth,
                               tree_depth=tree_depth))
 
 
+def prefill_workload(name, cfg_id, shape, shared_len, own_lens, sm_scale=None,
+                     description=""):
+    """Prompts whose first ``shared_len`` tokens hit a cached prefix.
+
+    sys = alloc + append ``shared_len`` tokens (the cached prefix, kept
+    alive); session ``i`` forks sys, appends its ``own_lens[i]`` unmatched
+    prompt tokens, and one prefill call per layer computes causal attention
+    of all sessions' new tokens over their whole caches.
+    """
+    ops = [("alloc", 0)]
+    if shared_len:
+        ops.append(("append", (0,), shared_len, len(ops)))
+    sessions = tuple(range(1, len(own_lens) + 1))
+    for h in sessions:
+        ops.append(("fork", 0, h))
+    by_len = {}
+    for h, n in zip(sessions, own_lens):
+        by_len.setdefault(n, []).append(h)
+    for n, hs in sorted(by_len.items()):
+        if n:
+            ops.append(("append", tuple(hs), n, len(ops)))
+    for layer in range(shape.num_layers):
+        ops.append(("prefill", sessions, layer, tuple(own_lens), len(ops)))
+    return Workload(name, cfg_id, shape, ops,
+                    _default_scale(shape) if sm_scale is None else sm_scale,
+                    description=description,
+                    meta=dict(shared_len=shared_len, own_lens=tuple(own_lens)))
+
+
 # ---------------------------------------------------------------------------
 # the five named workloads
 # ---------------------------------------------------------------------------
@@ -314,6 +353,17 @@ def _c5():
                     "2048-token context and a 64-node depth-6 draft tree each")
 
 
+def _c2_prefill():
+    # The Trellis-shaped prompts' prefill: 256 of each 512-token prompt hit
+    # the cached shared prefix, the other 256 are computed (one layer).
+    shape = Shape(32, 4, 64, 32, 1, 256)
+    return prefill_workload(
+        "c2_trellis_prefill", 6, shape, shared_len=256, own_lens=[256] * 16,
+        description="32 q / 4 kv heads, D 64, B 32; 16 prompts of 512 tokens "
+                    "whose first 256 hit a cached shared prefix; causal prefill "
+                    "of the other 256 tokens of every prompt (4096 queries)")
+
+
 _NAMED = {
     "c1_tiny_fork": _c1,
     "c2_trellis": _c2,
@@ -322,6 +372,7 @@ _NAMED = {
     "c4_mcts": _c4,
     "c4_mcts_folded": lambda: _c4(True),
     "c5_verify": _c5,
+    "c2_trellis_prefill": _c2_prefill,
 }
 NAMES = tuple(_NAMED)
 

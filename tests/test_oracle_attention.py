@@ -22,8 +22,8 @@ import torch
 import torch.nn.functional as F
 
 import synth
-from oracle import (PoolModel, attend, bf16_bits_to_f64, decode, tree_verify,
-                    tree_key_positions, run_program, EmptyError)
+from oracle import (PoolModel, attend, bf16_bits_to_f64, decode, prefill, tree_verify,
+                    tree_key_positions, run_program, ArgError, EmptyError)
 
 
 def rand_bits(rng, shape, scale=1.0):
@@ -375,3 +375,119 @@ def test_brute_force_tiny_pools(B):
                     ro, rl = sdpa(q[i:i + 1], kk, vv, 0.5)
                     assert np.allclose(ok[0][0][i], ro[0], rtol=0, atol=1e-13)
                     assert np.allclose(ok[0][1][i], rl[0], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------ causal prefill
+
+def sdpa_causal(q_bits, k_bits, v_bits, scale):
+    """Library causal attention over a whole sequence: q/k/v [n][H][D], query
+    i sees keys 0..i (``is_causal``); lse by ``torch.logsumexp`` over a
+    ``tril`` of ones."""
+    q = t64(q_bits).permute(1, 0, 2)[None]
+    k = t64(k_bits).permute(1, 0, 2)[None]
+    v = t64(v_bits).permute(1, 0, 2)[None]
+    out = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale,
+                                         enable_gqa=True)[0].permute(1, 0, 2)
+    g = q.shape[1] // k.shape[1]
+    z = scale * (q @ k.repeat_interleave(g, dim=1).transpose(-1, -2))
+    n = z.shape[-1]
+    keep = torch.ones(n, n, dtype=torch.bool).tril()
+    lse = torch.logsumexp(z.masked_fill(~keep, float("-inf")), dim=-1)[0].permute(1, 0)
+    return out.numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("hq,hkv,d,B", [(8, 2, 64, 16), (32, 4, 64, 32), (6, 1, 8, 1),
+                                        (4, 4, 16, 4)])
+def test_prefill_matches_library_causal_attention(hq, hkv, d, B):
+    """The new tokens' rows equal the last rows of the library's causal
+    attention over the whole sequence (the earlier rows get queries of their
+    own, which the prefill does not compute).  Covers a shared prefix, ragged
+    counts, a count of 0 and a whole sequence new."""
+    rng = np.random.default_rng(hq * 100 + d + B)
+    tp = Tracked(256, B, 2, hkv, d, free_order=rng.permutation(256))
+    root = tp.alloc()
+    tp.append([root], 29, rng)
+    kids = [tp.fork(root) for _ in range(3)]
+    tp.append(kids, 7, rng)
+    tp.append([kids[0]], 66, rng)
+    tp.append([kids[2]], 1, rng)
+    seqs = kids + [root]
+    n_new = [66 + 7, 0, 8, 29]       # kids[0]: 73 new; root: all of it new
+    lens = [29 + 7 + 66, 29 + 7, 29 + 7 + 1, 29]
+    for layer in range(2):
+        q_new = rand_bits(rng, (sum(n_new), hq, d))
+        out, lse = prefill(tp.pool, layer, seqs, n_new, q_new, 1 / math.sqrt(d))
+        row = 0
+        for s_, n, ln in zip(seqs, n_new, lens):
+            k, v = tp.data[s_]
+            assert k.shape[1] == ln
+            q_all = np.concatenate([rand_bits(rng, (ln - n, hq, d)), q_new[row:row + n]])
+            ro, rl = sdpa_causal(q_all, k[layer], v[layer], 1 / math.sqrt(d))
+            assert np.allclose(out[row:row + n], ro[ln - n:], rtol=0, atol=1e-12)
+            assert np.allclose(lse[row:row + n], rl[ln - n:], rtol=0, atol=1e-12)
+            row += n
+
+
+def test_prefill_query_equals_decode_on_the_prefix_it_sees():
+    """Query j of the new tokens reads what a decode reads on a sequence
+    holding only the first len - n + j + 1 tokens (built by appending exactly
+    those tokens to a fresh pool)."""
+    rng = np.random.default_rng(21)
+    B, hkv, d, hq = 4, 2, 16, 4
+    tp = Tracked(64, B, 1, hkv, d)
+    s = tp.alloc()
+    tp.append([s], 13, rng)
+    tp.append([s], 9, rng)
+    k, v = tp.data[s]
+    q = rand_bits(rng, (9, hq, d))
+    out, lse = prefill(tp.pool, 0, [s], [9], q, 0.4)
+    for j in range(9):
+        solo = PoolModel(64, B, 1, hkv, d)
+        t = solo.allocate()
+        n = 13 + j + 1
+        solo.append([t], n, k[:, None, :n], v[:, None, :n])
+        od, ld = decode(solo, 0, [t], q[j:j + 1], 0.4)
+        assert np.array_equal(out[j], od[0]) and np.array_equal(lse[j], ld[0])
+
+
+def test_prefill_equals_chain_tree_verify():
+    """A chain-shaped draft tree is causal attention over its tokens."""
+    rng = np.random.default_rng(22)
+    tp = Tracked(64, 8, 1, 2, 32)
+    seqs = [tp.alloc() for _ in range(2)]
+    tp.append(seqs, 19, rng)
+    tp.append(seqs, 11, rng)
+    q = rand_bits(rng, (2, 11, 8, 32))
+    chain = np.tile(np.arange(-1, 10, dtype=np.int32), (2, 1))
+    out_t, lse_t = tree_verify(tp.pool, 0, seqs, chain, q, 0.3)
+    out_p, lse_p = prefill(tp.pool, 0, seqs, [11, 11], q.reshape(22, 8, 32), 0.3)
+    assert np.array_equal(out_t.reshape(22, 8, 32), out_p)
+    assert np.array_equal(lse_t.reshape(22, 8), lse_p)
+
+
+def test_prefill_zero_query_gives_running_means():
+    """q = 0: every visible key weighs the same, so query j's output is the
+    mean of V over tokens 0..ctx+j and its lse is ln(ctx + j + 1)."""
+    rng = np.random.default_rng(23)
+    tp = Tracked(32, 4, 1, 1, 8)
+    s = tp.alloc()
+    tp.append([s], 10, rng)
+    out, lse = prefill(tp.pool, 0, [s], [6], np.zeros((6, 2, 8), np.uint16), 0.7)
+    v = bf16_bits_to_f64(tp.data[s][1][0, :, 0])    # [10][8]
+    for j in range(6):
+        seen = 4 + j + 1
+        assert np.allclose(out[j, 0], v[:seen].mean(axis=0), rtol=0, atol=1e-15)
+        assert math.isclose(lse[j, 1], math.log(seen), abs_tol=1e-15)
+
+
+def test_prefill_argument_errors():
+    rng = np.random.default_rng(24)
+    tp = Tracked(16, 4, 1, 1, 8)
+    s = tp.alloc()
+    tp.append([s], 5, rng)
+    with pytest.raises(ArgError):
+        prefill(tp.pool, 0, [s], [6], np.zeros((6, 1, 8), np.uint16), 1.0)
+    with pytest.raises(ArgError):
+        prefill(tp.pool, 0, [s], [2], np.zeros((3, 1, 8), np.uint16), 1.0)
+    out, lse = prefill(tp.pool, 0, [s], [0], np.zeros((0, 1, 8), np.uint16), 1.0)
+    assert out.shape == (0, 1, 8) and lse.shape == (0, 1)

@@ -240,6 +240,7 @@ def test_dendrite_memory_figure():
     ("c3_dendrite_aligned", 4096 // 16 + 6 * 24, 0),
     ("c4_mcts", 2048 // 16 + 4 * 4 + 16 * 4 + 64 * 4 + 256 * 4, 0),
     ("c5_verify", 8 * (2048 // 16 + 64 // 16), 0),
+    ("c2_trellis_prefill", 256 // 32 + 16 * (256 // 32), 0),
 ])
 def test_workload_block_counts(name, unique, cows):
     """Closed-form block counts of each workload's construction.  The
