@@ -171,6 +171,31 @@ pkv_status paged_attn_tree_verify(pkv_pool* pool, int32_t layer,
                                   const void* q, float sm_scale, float* out,
                                   float* lse, void* stream);
 
+/*
+ * Causal prefill at one layer: attention of each sequence's newest tokens
+ * over its whole cache.  After a prefix-cache hit only the prompt's
+ * unmatched tokens are computed (SGLang RadixAttention page, the radix
+ * tree's core operations, prefix matching: the forward pass covers the
+ * n - k tokens that missed); they are appended with kv_append first, and
+ * token t attends to tokens 0..t, the causal rule (Trellis page, section
+ * "LLM prefill and KV cache").
+ * n_new: host int32 [n_seqs]; the last n_new[i] tokens of seqs[i] are new
+ *        (0 <= n_new[i] <= len; 0 contributes no queries).
+ * q:   device bf16 [sum n_new][num_q_heads][head_dim], sequence after
+ *      sequence, tokens in order.
+ * out: device fp32 [sum n_new][num_q_heads][head_dim];
+ * lse: device fp32 [sum n_new][num_q_heads] (natural log), or NULL.
+ * Query j of sequence i (at position len - n_new[i] + j) attends to tokens
+ * 0 .. len - n_new[i] + j.  At most 65536 queries per call (PKV_ERR_ARG
+ * beyond).  A call whose n_new are all 0 is a no-op (q and out may then be
+ * NULL).  Sequences may repeat.  A call with the same sequences and counts
+ * as the previous prefill call, on a pool no call has changed since (the
+ * next layer of the same step), reuses that call's plan.
+ */
+pkv_status paged_attn_prefill(pkv_pool* pool, int32_t layer, const int64_t* seqs,
+                              int32_t n_seqs, const int32_t* n_new, const void* q,
+                              float sm_scale, float* out, float* lse, void* stream);
+
 /* ---- introspection (host only) ---------------------------------------- */
 
 /* Block table (up to cap entries copied to out; out may be NULL when cap is 0),

@@ -22,7 +22,7 @@ __all__ = [
     "PkvError", "PkvDesc", "load", "library_path",
     "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy",
     "seq_allocate", "seq_fork", "seq_free", "kv_append",
-    "paged_attn_decode", "paged_attn_tree_verify",
+    "paged_attn_decode", "paged_attn_tree_verify", "paged_attn_prefill",
     "seq_block_table", "block_refcount", "free_list", "kv_last_append",
     "paged_attn_decode_plan_stats", "pkv_timing_enable", "pkv_timing_read", "pkv_last_error",
     "seq_ids",
@@ -98,6 +98,8 @@ def load():
         "paged_attn_decode": (_I32, [_P, _I32, _PI64, _I32, _P, ctypes.c_float, _P, _P, _P]),
         "paged_attn_tree_verify": (_I32, [_P, _I32, _PI64, _I32, _I32, _PI32, _P,
                                           ctypes.c_float, _P, _P, _P]),
+        "paged_attn_prefill": (_I32, [_P, _I32, _PI64, _I32, _PI32, _P, ctypes.c_float, _P, _P,
+                                      _P]),
         "seq_block_table": (_I32, [_P, _I64, _PI32, _I32, _PI32, _PI32]),
         "block_refcount": (_I32, [_P, _I32, _PI32]),
         "free_list": (_I32, [_P, _PI32, _I32, _PI32]),
@@ -245,6 +247,15 @@ def paged_attn_tree_verify(pool, layer, seqs, n_nodes, parent, q, sm_scale, out,
     _check(load().paged_attn_tree_verify(pool, int(layer), p, n, int(n_nodes),
                                          par.ctypes.data_as(_PI32), _addr(q), float(sm_scale),
                                          _addr(out), _addr(lse), _stream(stream)))
+
+
+def paged_attn_prefill(pool, layer, seqs, n_new, q, sm_scale, out, lse=None, stream=None):
+    p, n = _seq_array(seqs)
+    nn = np.ascontiguousarray(np.asarray(n_new, dtype=np.int32).reshape(-1))
+    if nn.size != n:
+        raise ValueError("n_new must hold one count per sequence")
+    _check(load().paged_attn_prefill(pool, int(layer), p, n, nn.ctypes.data_as(_PI32), _addr(q),
+                                     float(sm_scale), _addr(out), _addr(lse), _stream(stream)))
 
 
 def seq_block_table(pool, seq):

@@ -108,7 +108,7 @@ struct pkv_pool {
   int dev = -1;
   uint16_t* k_pool = nullptr;
   uint16_t* v_pool = nullptr;
-  DevBuf append_plan, decode_plan, verify_plan, partials;
+  DevBuf append_plan, decode_plan, verify_plan, prefill_plan, partials;
   void* stage[kStageSlots] = {};
   size_t stage_cap[kStageSlots] = {};
   hipEvent_t stage_ev[kStageSlots] = {};
@@ -123,6 +123,14 @@ struct pkv_pool {
   PlanLayout dlayout;
   pkv::Plan vplan;
   PlanLayout vlayout;
+  // prefill plan cache: the same call repeated at every layer of a step
+  // (same sequences and counts, pool unchanged) reuses the uploaded plan
+  bool pcache_valid = false;
+  uint64_t pcache_version = 0;
+  std::vector<int64_t> pcache_seqs;
+  std::vector<int32_t> pcache_new;
+  pkv::Plan pplan;
+  PlanLayout playout;
   // kernel timing: event pairs recorded around every timing_every-th
   // attention kernel
   bool timing = false;
@@ -371,7 +379,7 @@ void kv_pool_destroy(pkv_pool* p) {
   if (p->device) {
     DeviceGuard g(p->dev);
     (void)hipDeviceSynchronize();
-    for (DevBuf* b : {&p->append_plan, &p->decode_plan, &p->verify_plan, &p->partials})
+    for (DevBuf* b : {&p->append_plan, &p->decode_plan, &p->verify_plan, &p->prefill_plan, &p->partials})
       if (b->ptr) (void)hipFree(b->ptr);
     for (int i = 0; i < kStageSlots; ++i) {
       if (p->stage[i]) (void)hipHostFree(p->stage[i]);
@@ -535,6 +543,48 @@ pkv_status paged_attn_tree_verify(pkv_pool* p, int32_t layer, const int64_t* seq
                         [&](char* dst) { serialize(p->vplan, p->vlayout, dst); });
   if (s != PKV_OK) return s;
   return launch_plan(p, p->vplan, p->vlayout, p->verify_plan, layer, q, sm_scale, out, lse, st);
+}
+
+pkv_status paged_attn_prefill(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs,
+                              const int32_t* n_new, const void* q, float sm_scale, float* out,
+                              float* lse, void* stream) {
+  if (!p) return fail(PKV_ERR_ARG, "paged_attn_prefill: NULL pool");
+  if (!p->device) return fail(PKV_ERR_ARG, "paged_attn_prefill: the pool has no device storage");
+  if (n_seqs < 0) return fail(PKV_ERR_ARG, "paged_attn_prefill: negative n_seqs");
+  if (n_seqs == 0) return PKV_OK;
+  if (!seqs || !n_new) return fail(PKV_ERR_ARG, "paged_attn_prefill: NULL seqs or n_new");
+  if (layer < 0 || layer >= p->core.shape().num_layers)
+    return fail(PKV_ERR_ARG, "paged_attn_prefill: layer out of range");
+  const bool hit = p->pcache_valid && p->pcache_version == p->core.version() &&
+                   p->pcache_seqs.size() == static_cast<size_t>(n_seqs) &&
+                   std::memcmp(p->pcache_seqs.data(), seqs, n_seqs * sizeof(int64_t)) == 0 &&
+                   std::memcmp(p->pcache_new.data(), n_new, n_seqs * sizeof(int32_t)) == 0;
+  if (!hit) {
+    p->pcache_valid = false;
+    std::string why;
+    pkv::Err e = pkv::plan_prefill(p->core, seqs, n_seqs, n_new, p->cfg, &p->pplan, &why);
+    if (e != pkv::Err::ok) return fail(to_status(e), why);
+  }
+  if (p->pplan.mfma.empty() && p->pplan.valu.empty()) return PKV_OK;   // no new tokens
+  if (!q || !out) return fail(PKV_ERR_ARG, "paged_attn_prefill: NULL q or out");
+  if (!aligned16(q) || !aligned16(out))
+    return fail(PKV_ERR_ARG, "paged_attn_prefill: q and out must be 16-byte aligned");
+  DeviceGuard g(p->dev);
+  PKV_HIP(g.err);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!hit) {
+    if (!plan_fits_kernels(p->pplan, p->core.shape()))
+      return fail(PKV_ERR_ARG, "paged_attn_prefill: internal plan exceeds the kernels' tile limits");
+    p->playout = layout_of(p->pplan);
+    pkv_status s = upload(p, p->prefill_plan, p->playout.total, st,
+                          [&](char* dst) { serialize(p->pplan, p->playout, dst); });
+    if (s != PKV_OK) return s;
+    p->pcache_seqs.assign(seqs, seqs + n_seqs);
+    p->pcache_new.assign(n_new, n_new + n_seqs);
+    p->pcache_version = p->core.version();
+    p->pcache_valid = true;
+  }
+  return launch_plan(p, p->pplan, p->playout, p->prefill_plan, layer, q, sm_scale, out, lse, st);
 }
 
 pkv_status seq_block_table(const pkv_pool* p, int64_t seq, int32_t* out, int32_t cap,

@@ -536,3 +536,130 @@ Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
 }
 
 }  // namespace pkv
+
+namespace pkv {
+
+// Causal prefill as chain-shaped key tails: the new tokens of a sequence are
+// cut into windows of `per` consecutive queries (at most 64, one item's row
+// subset).  A window's key range runs from token 0 to its last query's own
+// token; its own tokens are the item's masked tail, node k of the window
+// seeing nodes 0..k (the ancestor-or-self mask of a chain), everything before
+// the window is unmasked context.  So the kernels' tree-tail masking serves
+// the causal mask unchanged, and no window reads keys past its last query.
+Err plan_prefill(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, const int32_t* n_new,
+                 const PlanConfig& cfg, Plan* plan, std::string* why) {
+  plan->reset();
+  const Shape& sh = pool.shape();
+  const int32_t B = sh.block_size;
+  const int32_t G = sh.num_q_heads / sh.num_kv_heads;
+  std::vector<const SeqState*> st(n_seqs);
+  std::vector<int32_t> q_off(static_cast<size_t>(n_seqs) + 1, 0);
+  int32_t max_new = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    st[i] = pool.find(seqs[i]);
+    if (!st[i]) {
+      *why = "paged_attn_prefill: unknown sequence " + std::to_string(seqs[i]);
+      return Err::seq;
+    }
+    if (n_new[i] < 0 || n_new[i] > st[i]->len) {
+      *why = "paged_attn_prefill: sequence " + std::to_string(seqs[i]) + " holds " +
+             std::to_string(st[i]->len) + " tokens, fewer than its " + std::to_string(n_new[i]) +
+             " new ones (or the count is negative)";
+      return Err::arg;
+    }
+    if (static_cast<int64_t>(q_off[i]) + n_new[i] > kMaxPrefillQueries) {
+      *why = "paged_attn_prefill: more than " + std::to_string(kMaxPrefillQueries) + " queries in one call";
+      return Err::arg;
+    }
+    q_off[i + 1] = q_off[i] + n_new[i];
+    max_new = std::max(max_new, n_new[i]);
+  }
+  const int32_t nq = q_off[n_seqs];
+  if (nq == 0) return Err::ok;
+  const int64_t win_rows = static_cast<int64_t>(std::min(max_new, 64)) * G;
+  const bool mfma = G > cfg.valu_rows || (cfg.mfma_min_rows > 0 && win_rows >= cfg.mfma_min_rows);
+  plan->mfma_row_tiles = cfg.mfma_row_tiles > 0 ? cfg.mfma_row_tiles : 2;
+  plan->mfma_waves = mfma ? pick_waves(cfg, false, plan->mfma_row_tiles, win_rows) : 4;
+  const int32_t per = std::min(
+      64, std::max(1, (mfma ? mfma_item_rows(plan->mfma_row_tiles, plan->mfma_waves) : cfg.valu_rows) / G));
+  // work (tokens x windows, per kv head) and what the call reads: the
+  // distinct blocks of the sequences with new tokens, at their filled slots
+  int64_t work = 0;
+  int32_t max_len = 0;
+  std::vector<int32_t> filled(static_cast<size_t>(sh.num_blocks), 0);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t n = n_new[i];
+    if (n == 0) continue;
+    const int32_t len = st[i]->len;
+    const int32_t ctx = len - n;
+    max_len = std::max(max_len, len);
+    for (int32_t w0 = 0; w0 < n; w0 += per) work += ctx + std::min(n, w0 + per);
+    for (int32_t j = 0; j < n; ++j) plan->logical_tokens += ctx + j + 1;
+    const auto& t = st[i]->table;
+    for (size_t b = 0; b < t.size(); ++b)
+      filled[t[b]] = std::max(filled[t[b]], std::min<int32_t>(B, len - static_cast<int32_t>(b) * B));
+  }
+  for (int32_t f : filled) {
+    plan->unique_tokens += f;
+    plan->unique_blocks += f > 0;
+  }
+  const int64_t cap = mfma ? chunk_cap(cfg, B) : std::min<int64_t>(chunk_cap(cfg, B), cfg.valu_max_tokens);
+  const int32_t unit = std::max(cfg.tile, B);
+  int32_t chunk = pick_chunk(work, sh.num_kv_heads, unit,
+                             mfma ? cfg.target_mfma_wgs * 4 / plan->mfma_waves : cfg.target_wgs, cap);
+  {
+    int32_t unused = chunk;
+    limit_parts(cfg, unit, cap, cap, &chunk, &unused,
+                [&](int32_t c, int32_t) { return static_cast<int32_t>(ceil_div(max_len, c)); });
+  }
+  std::vector<int32_t> n_parts(static_cast<size_t>(nq), 0);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t n = n_new[i];
+    if (n == 0) continue;
+    const int32_t len = st[i]->len;
+    const int32_t ctx = len - n;
+    const int32_t blk_base = static_cast<int32_t>(plan->blocks.size());
+    plan->blocks.insert(plan->blocks.end(), st[i]->table.begin(), st[i]->table.end());
+    for (int32_t w0 = 0; w0 < n; w0 += per) {
+      const int32_t nw = std::min(per, n - w0);
+      const int32_t tail = ctx + w0;         // the window's first own token
+      const int32_t end = tail + nw;         // keys of the window: 0 .. end - 1
+      const int32_t nchunk = static_cast<int32_t>(ceil_div(end, chunk));
+      const int32_t grp_off = static_cast<int32_t>(plan->groups.size());
+      for (int32_t k = 0; k < nw; ++k) {
+        const uint64_t m = k == 63 ? ~0ull : (2ull << k) - 1;   // nodes 0..k of the window
+        plan->groups.push_back(RowGroup{q_off[i] + w0 + k, k, static_cast<uint32_t>(m),
+                                        static_cast<uint32_t>(m >> 32), -1, {0, 0, 0}});
+        n_parts[q_off[i] + w0 + k] = nchunk;
+      }
+      for (int32_t c = 0; c < nchunk; ++c) {
+        const int32_t start = c * chunk;
+        WorkItem it{};
+        it.blk_off = blk_base + start / B;
+        it.n_tok = std::min(chunk, end - start);
+        if (tail - start >= it.n_tok) {
+          it.tail_start = INT_MAX;
+          it.tail_node0 = 0;
+        } else if (start >= tail) {
+          it.tail_start = 0;
+          it.tail_node0 = start - tail;
+        } else {
+          it.tail_start = tail - start;
+          it.tail_node0 = 0;
+        }
+        it.grp_off = grp_off;
+        it.n_grp = nw;
+        it.part_base = -1;
+        it.tail_q = 0;
+        for (int32_t u = 0; u < 8; ++u) it.q_index[u] = u < nw ? plan->groups[grp_off + u].q_index : 0;
+        (mfma ? plan->mfma : plan->valu).push_back(it);
+      }
+    }
+  }
+  plan->segments = n_seqs;
+  finish_parts(plan, n_parts, sh.num_q_heads);
+  pack_item_blocks(plan, B);
+  return Err::ok;
+}
+
+}  // namespace pkv

@@ -13,6 +13,9 @@
 // Tree verify: one key range per sequence (context + draft-tree tail),
 // split into chunks; the row groups are the tree nodes with their
 // ancestor-or-self masks.
+//
+// Prefill: causal attention of a sequence's newest tokens, planned as
+// windows of consecutive queries whose own tokens form a chain-shaped tail.
 #pragma once
 
 #include <string>
@@ -117,6 +120,17 @@ bool patch_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, co
 Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
                 int32_t n_nodes, const int32_t* parent, const PlanConfig& cfg,
                 Plan* plan, std::string* why);
+
+// Most queries one prefill call takes (keeps query and partial-row indices
+// in 32 bits).
+constexpr int32_t kMaxPrefillQueries = 1 << 16;
+
+// Causal attention of each sequence's newest tokens (a prompt's part that
+// missed the prefix cache, appended already): the last n_new[i] tokens of
+// sequence i are queries q_off[i] + j (q_off = running sum of n_new), and
+// query j sees keys 0 .. len - n_new[i] + j.  n_new[i] may be 0.
+Err plan_prefill(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, const int32_t* n_new,
+                 const PlanConfig& cfg, Plan* plan, std::string* why);
 
 // Ancestor-or-self masks of one draft tree: anc[0] = 1,
 // anc[i] = anc[parent[i]] | 1 << i.  False if parent[] is not a tree in node

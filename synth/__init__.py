@@ -5,7 +5,8 @@ consume.  It produces *inputs* only:
 
 * workload shapes (head counts, head dim, block size, layers, pool size),
 * op programs: which pool calls happen in which order (allocate, fork,
-  append, free, decode, tree-verify), referring to sequences by handle,
+  append, free, decode, tree-verify, prefill), referring to sequences by
+  handle,
 * bf16 sample tensors (fp32 N(0,1) draws rounded to nearest-even), keyed by
   the op that consumes them, never by a physical block,
 * the block free-list order (identity or a seeded permutation),
@@ -31,6 +32,7 @@ from .workloads import (
     shared_prompt_workload,
     mcts_workload,
     verify_workload,
+    prefill_workload,
     draw_tree,
 )
 
@@ -49,5 +51,6 @@ __all__ = [
     "shared_prompt_workload",
     "mcts_workload",
     "verify_workload",
+    "prefill_workload",
     "draw_tree",
 ]

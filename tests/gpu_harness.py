@@ -95,6 +95,16 @@ def run_gpu(workload, want=None, free_order="default", on_result=None, pool_cb=N
                                            parents, q, workload.sm_scale, out, lse, gp.stream)
                 if want is None or idx in want:
                     results[idx] = (out.cpu().numpy(), lse.cpu().numpy())
+            elif kind == "prefill":
+                hs, layer, n_new, key = op[1], op[2], op[3], op[4]
+                total = sum(n_new)
+                q = to_dev(workload.prefill_query(key, total))
+                out = torch.empty((total, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+                lse = torch.empty((total, s.num_q_heads), dtype=torch.float32, device="cuda")
+                pkv.paged_attn_prefill(gp.pool, layer, [handles[h] for h in hs], n_new, q,
+                                       workload.sm_scale, out, lse, gp.stream)
+                if want is None or idx in want:
+                    results[idx] = (out.cpu().numpy(), lse.cpu().numpy())
         torch.cuda.synchronize()
         if pool_cb is not None:
             pool_cb(gp, handles)

@@ -121,6 +121,27 @@ def reduced():
             "verify_one_node", 17, Shape(8, 8, 64, 16, 1, 64), n_seqs=4, ctx_len=100,
             n_nodes=1, tree_depth=1),
         "c1_tiny_fork": synth.named("c1_tiny_fork"),
+        # causal prefill after a cached prefix: ragged counts (one window,
+        # exactly one, just over one, several), a count of 0
+        "prefill_small": synth.prefill_workload(
+            "prefill_small", 18, Shape(32, 8, 128, 16, 1, 256), shared_len=77,
+            own_lens=[1, 63, 64, 65, 130, 0, 200]),
+        # whole prompts new (no cached prefix), G 4 at D 64, 32-token blocks
+        "prefill_ctx0": synth.prefill_workload(
+            "prefill_ctx0", 19, Shape(32, 4, 64, 32, 2, 128), shared_len=0,
+            own_lens=[300, 5, 64]),
+        # repeated prefill calls: the same call at the next layer (plan reused),
+        # the same arguments after an append (pool changed: planned afresh),
+        # other counts
+        "prefill_repeat": synth.Workload(
+            "prefill_repeat", 20, Shape(32, 8, 128, 16, 2, 128),
+            [("alloc", 0), ("append", (0,), 40, 1), ("fork", 0, 1), ("fork", 0, 2), ("fork", 0, 3),
+             ("append", (1, 2, 3), 20, 5),
+             ("prefill", (1, 2, 3), 0, (20, 20, 20), 6), ("prefill", (1, 2, 3), 1, (20, 20, 20), 7),
+             ("append", (1, 2, 3), 5, 8),
+             ("prefill", (1, 2, 3), 0, (20, 20, 20), 9), ("prefill", (1, 2, 3), 1, (25, 5, 0), 10),
+             ("prefill", (3, 1), 1, (45, 1), 11)],
+            1.0 / math.sqrt(128)),
     }
 
 
@@ -178,6 +199,9 @@ def test_shape_edges(dev, shape, label, path, monkeypatch):
         tree = synth.verify_workload(f"edge_tree_{label}", 40 + SHAPES.index((shape, label)),
                                      shape, n_seqs=2, ctx_len=70, n_nodes=9, tree_depth=4)
         parity(tree)
+        pre = synth.prefill_workload(f"edge_prefill_{label}", 50 + SHAPES.index((shape, label)),
+                                     shape, shared_len=70, own_lens=[9, 70, 1])
+        parity(pre)
 
 
 # Direct decode at its edges: fewer 32-token steps than waves (1..9 keys),
@@ -251,12 +275,15 @@ def test_planner_settings_keep_parity(dev, knobs, monkeypatch):
     parity(synth.fork_workload(f"knob_mixed_{tag}", 62, Shape(32, 8, 64, 16, 1, 256),
                                prefix_len=260, n_branches=12, branch_len=41, decode_steps=2),
            check_pool=False)
+    # causal prefill of ragged prompts after a shared prefix
+    parity(synth.prefill_workload(f"knob_prefill_{tag}", 63, Shape(32, 4, 64, 16, 1, 256),
+                                  shared_len=150, own_lens=[100, 7, 64, 260]), check_pool=False)
 
 
 # ------------------------------------------------------- full-size workloads
 
 def sample_ops(wl, every):
-    idx = [i for i, op in enumerate(wl.ops) if op[0] in ("decode", "verify")]
+    idx = [i for i, op in enumerate(wl.ops) if op[0] in ("decode", "verify", "prefill")]
     keep = set(idx[::every])
     keep.add(idx[-1])
     return keep
@@ -268,6 +295,7 @@ def sample_ops(wl, every):
     ("c3_dendrite", 9, "auto"), ("c3_dendrite", 31, "direct"), ("c3_dendrite", 31, "manyparts"),
     ("c3_dendrite_aligned", 31, "auto"),
     ("c4_mcts", 1, "auto"), ("c4_mcts_folded", 1, "auto"), ("c5_verify", 1, "auto"),
+    ("c2_trellis_prefill", 1, "auto"),
 ])
 def test_full_workload_parity(dev, name, every, path, monkeypatch):
     """The five workloads at full size, launched as the benchmark launches
