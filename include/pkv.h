@@ -196,6 +196,76 @@ pkv_status paged_attn_prefill(pkv_pool* pool, int32_t layer, const int64_t* seqs
                               int32_t n_seqs, const int32_t* n_new, const void* q,
                               float sm_scale, float* out, float* lse, void* stream);
 
+/* ---- radix prefix cache (host only) ------------------------------------ */
+
+/*
+ * A block-granular radix tree from token-id sequences to the pool blocks
+ * holding their K/V (SGLang RadixAttention page: node and edge structure,
+ * the core operations match / split / insert, reference counting and
+ * leaf-first LRU eviction; block-paged as on the Trellis page, section
+ * "RadixAttention in Trellis": a session sharing a prefix acquires the
+ * existing blocks, refcount + 1).  Edges hold whole blocks; a prompt matches
+ * whole blocks only, so a prompt differing inside a block shares the blocks
+ * before it (Trellis page, hit rate at most (L/B - 1)/(L/B) when the probe
+ * differs in the last block).  The cache holds one reference on every block
+ * it caches; blocks leave the pool only when their refcount reaches zero.
+ * A cache borrows its pool: destroy the cache first.  Not thread-safe.
+ * Access order for eviction is a counter bumped per touched node.
+ * None of these calls enqueues device work.
+ */
+typedef struct pkv_radix pkv_radix;
+
+pkv_status radix_create(pkv_pool* pool, pkv_radix** out);
+
+/* Drops the cache's block references; NULL is a no-op. */
+void radix_destroy(pkv_radix* cache);
+
+/*
+ * Longest cached whole-block prefix of tokens[0..n_tokens): a new sequence
+ * (*out_seq) holds those blocks (refcount + 1 each) with length
+ * *out_matched (a multiple of block_size, possibly 0).  The caller appends
+ * the other n_tokens - *out_matched tokens with kv_append and computes only
+ * them (paged_attn_prefill).  Every tree node on the matched path is locked
+ * (protected from eviction) until radix_release(out_seq).
+ */
+pkv_status radix_match(pkv_radix* cache, const int32_t* tokens, int32_t n_tokens,
+                       int64_t* out_seq, int32_t* out_matched);
+
+/*
+ * Cache the whole blocks of `seq` (its first n_tokens / block_size blocks)
+ * under tokens[0..n_tokens), 0 <= n_tokens <= the sequence's length; the
+ * caller vouches that those blocks hold the K/V of these tokens.  An edge
+ * that diverges part-way is split at the block boundary (block ids are
+ * re-sliced, no data moves); blocks under tokens already cached are left as
+ * the tree has them; the rest become a new leaf (cache reference + 1 each).
+ */
+pkv_status radix_insert(pkv_radix* cache, int64_t seq, const int32_t* tokens, int32_t n_tokens);
+
+/* The request that radix_match made `seq` for is done: unlock its path.
+ * The sequence itself is untouched (seq_free it separately).
+ * PKV_ERR_SEQ if `seq` holds no unreleased match of this cache. */
+pkv_status radix_release(pkv_radix* cache, int64_t seq);
+
+/*
+ * Evict until the pool's free list holds at least want_free blocks: the
+ * unlocked leaf touched longest ago goes first (its blocks lose the cache's
+ * reference); a parent left without children becomes a leaf candidate.
+ * *n_free (may be NULL) receives the free-list length afterwards.
+ * PKV_ERR_OOM when only locked nodes remain and the target is not reached
+ * (what could be evicted has been).
+ */
+pkv_status radix_evict(pkv_radix* cache, int32_t want_free, int32_t* n_free);
+
+/* Tree nodes (root excluded), blocks referenced by the tree, locked nodes. */
+pkv_status radix_stats(const pkv_radix* cache, int32_t* nodes, int32_t* cached_blocks,
+                       int32_t* locked_nodes);
+
+/* The tree in preorder (children ordered by their first block's tokens,
+ * root excluded), per node: depth, token count t, lock count, t tokens,
+ * t / block_size block ids.  Up to cap entries are copied; *n receives the
+ * full length. */
+pkv_status radix_dump(const pkv_radix* cache, int32_t* out, int32_t cap, int32_t* n);
+
 /* ---- introspection (host only) ---------------------------------------- */
 
 /* Block table (up to cap entries copied to out; out may be NULL when cap is 0),

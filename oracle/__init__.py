@@ -16,6 +16,8 @@ Contents:
   (one query per sequence), draft-tree verify (context plus tree
   ancestors and the node itself) and causal prefill of a sequence's newest
   tokens over its whole cache.
+* :mod:`oracle.radix` -- a block-paged radix-tree prefix cache over the pool
+  model: match, split-on-insert, release, leaf-first LRU eviction.
 * :mod:`oracle.run` -- runs a ``synth`` op program through the two.
 
 Every function here is pinned by the ``-m "not gpu"`` tests against facts the
@@ -26,6 +28,7 @@ invariants, a library attention routine, numbers the pages print); none is
 
 from .pool import PoolModel, PoolError, OOMError, SeqError, ArgError, EmptyError
 from .attention import bf16_bits_to_f64, attend, decode, prefill, tree_verify, tree_key_positions
+from .radix import RadixModel
 from .run import run_program
 
 __all__ = [
@@ -42,4 +45,5 @@ __all__ = [
     "tree_verify",
     "tree_key_positions",
     "run_program",
+    "RadixModel",
 ]

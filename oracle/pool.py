@@ -118,6 +118,41 @@ class PoolModel:
         del self.tables[sid]
         del self.lens[sid]
 
+    def adopt(self, blocks, length: int) -> int:
+        """New sequence over blocks someone already holds (a prefix-cache
+        hit): the table is ``blocks``, the length ``length``, and each block
+        gains a reference ("Introducing RadixAttention into Trellis",
+        section "RadixAttention in Trellis": a session sharing a prefix
+        acquires the existing blocks, refcount + 1)."""
+        blocks = [int(b) for b in blocks]
+        if blocks and not (len(blocks) - 1) * self.B < length <= len(blocks) * self.B:
+            raise ArgError("length does not fit the block count")
+        if not blocks and length != 0:
+            raise ArgError("length does not fit the block count")
+        for b in blocks:
+            if self.rc[b] < 1:
+                raise ArgError(f"block {b} is not held")
+        sid = self.next_id
+        self.next_id += 1
+        self.tables[sid] = list(blocks)
+        self.lens[sid] = length
+        for b in blocks:
+            self.rc[b] += 1
+        return sid
+
+    def hold(self, block: int) -> None:
+        """One more reference held outside any sequence (a cache's own)."""
+        if self.rc[block] < 1:
+            raise ArgError(f"block {block} is not held")
+        self.rc[block] += 1
+
+    def unhold(self, block: int) -> None:
+        """Drop a reference taken by :meth:`hold`; zero -> tail of the free list."""
+        self.rc[block] -= 1
+        if self.rc[block] == 0:
+            self.fifo.append(block)
+            self.filled[block] = 0
+
     def append(self, seqs, n_tok, k_bits=None, v_bits=None):
         """Append ``n_tok`` tokens to each sequence in ``seqs``.
 

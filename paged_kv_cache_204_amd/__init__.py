@@ -26,6 +26,8 @@ __all__ = [
     "seq_block_table", "block_refcount", "free_list", "kv_last_append",
     "paged_attn_decode_plan_stats", "pkv_timing_enable", "pkv_timing_read", "pkv_last_error",
     "seq_ids",
+    "radix_create", "radix_destroy", "radix_match", "radix_insert", "radix_release",
+    "radix_evict", "radix_stats", "radix_dump",
     "PKV_OK", "PKV_ERR_ARG", "PKV_ERR_OOM", "PKV_ERR_SEQ", "PKV_ERR_HIP",
     "PKV_ERR_EMPTY", "PKV_ERR_UNSUPPORTED",
 ]
@@ -108,6 +110,14 @@ def load():
         "pkv_timing_enable": (_I32, [_P, _I32]),
         "pkv_timing_read": (_I32, [_P, ctypes.POINTER(ctypes.c_double), _PI64, _I32]),
         "pkv_last_error": (ctypes.c_char_p, []),
+        "radix_create": (_I32, [_P, ctypes.POINTER(_P)]),
+        "radix_destroy": (None, [_P]),
+        "radix_match": (_I32, [_P, _PI32, _I32, _PI64, _PI32]),
+        "radix_insert": (_I32, [_P, _I64, _PI32, _I32]),
+        "radix_release": (_I32, [_P, _I64]),
+        "radix_evict": (_I32, [_P, _I32, _PI32]),
+        "radix_stats": (_I32, [_P, _PI32, _PI32, _PI32]),
+        "radix_dump": (_I32, [_P, _PI32, _I32, _PI32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -317,3 +327,71 @@ def pkv_timing_read(pool, reset=True):
 
 def pkv_last_error() -> str:
     return load().pkv_last_error().decode()
+
+
+# ---- radix prefix cache ---------------------------------------------------
+
+def _tokens(tokens):
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+    return t, t.ctypes.data_as(_PI32), t.size
+
+
+def radix_create(pool):
+    out = _P()
+    _check(load().radix_create(pool, ctypes.byref(out)))
+    return out.value
+
+
+def radix_destroy(cache):
+    if cache:
+        load().radix_destroy(cache)
+
+
+def radix_match(cache, tokens):
+    """(new sequence id, matched token count)."""
+    t, p, n = _tokens(tokens)
+    seq = _I64()
+    m = _I32()
+    _check(load().radix_match(cache, p, n, ctypes.byref(seq), ctypes.byref(m)))
+    return seq.value, m.value
+
+
+def radix_insert(cache, seq, tokens):
+    t, p, n = _tokens(tokens)
+    _check(load().radix_insert(cache, int(seq), p, n))
+
+
+def radix_release(cache, seq):
+    _check(load().radix_release(cache, int(seq)))
+
+
+def radix_evict(cache, want_free):
+    """Free-list length afterwards; raises PkvError (PKV_ERR_OOM) when the
+    target cannot be reached."""
+    n = _I32()
+    _check(load().radix_evict(cache, int(want_free), ctypes.byref(n)))
+    return n.value
+
+
+def radix_stats(cache):
+    a, b, c = _I32(), _I32(), _I32()
+    _check(load().radix_stats(cache, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return {"nodes": a.value, "cached_blocks": b.value, "locked_nodes": c.value}
+
+
+def radix_dump(cache, block_size):
+    """The tree as a list of (depth, tokens, lock, blocks) in preorder."""
+    n = _I32()
+    _check(load().radix_dump(cache, None, 0, ctypes.byref(n)))
+    buf = (ctypes.c_int32 * max(1, n.value))()
+    _check(load().radix_dump(cache, buf, n.value, ctypes.byref(n)))
+    flat = list(buf[:n.value])
+    out = []
+    i = 0
+    while i < len(flat):
+        depth, t, lock = flat[i], flat[i + 1], flat[i + 2]
+        toks = flat[i + 3:i + 3 + t]
+        blocks = flat[i + 3 + t:i + 3 + t + t // block_size]
+        out.append((depth, toks, lock, blocks))
+        i += 3 + t + t // block_size
+    return out

@@ -20,6 +20,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = [
     "host/pool.cpp",
     "host/plan.cpp",
+    "host/radix.cpp",
     "capi.hip",
     "kernels/append.hip",
     "kernels/attn.hip",

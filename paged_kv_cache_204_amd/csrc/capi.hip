@@ -15,6 +15,7 @@
 
 #include "pkv.h"
 #include "host/plan.hpp"
+#include "host/radix.hpp"
 #include "host/pool.hpp"
 #include "kernels.hpp"
 
@@ -585,6 +586,71 @@ pkv_status paged_attn_prefill(pkv_pool* p, int32_t layer, const int64_t* seqs, i
     p->pcache_valid = true;
   }
   return launch_plan(p, p->pplan, p->playout, p->prefill_plan, layer, q, sm_scale, out, lse, st);
+}
+
+// ---- radix prefix cache --------------------------------------------------
+
+struct pkv_radix {
+  explicit pkv_radix(pkv_pool* p) : pool(p), cache(&p->core) {}
+  pkv_pool* pool;
+  pkv::RadixCache cache;
+};
+
+pkv_status radix_create(pkv_pool* p, pkv_radix** out) {
+  if (!p || !out) return fail(PKV_ERR_ARG, "radix_create: NULL argument");
+  *out = new (std::nothrow) pkv_radix(p);
+  return *out ? PKV_OK : fail(PKV_ERR_OOM, "radix_create: out of host memory");
+}
+
+void radix_destroy(pkv_radix* r) { delete r; }
+
+pkv_status radix_match(pkv_radix* r, const int32_t* tokens, int32_t n_tokens, int64_t* out_seq,
+                       int32_t* out_matched) {
+  if (!r || !out_seq || !out_matched) return fail(PKV_ERR_ARG, "radix_match: NULL argument");
+  std::string why;
+  pkv::Err e = r->cache.match(tokens, n_tokens, out_seq, out_matched, &why);
+  return e == pkv::Err::ok ? PKV_OK : fail(to_status(e), why);
+}
+
+pkv_status radix_insert(pkv_radix* r, int64_t seq, const int32_t* tokens, int32_t n_tokens) {
+  if (!r) return fail(PKV_ERR_ARG, "radix_insert: NULL cache");
+  std::string why;
+  pkv::Err e = r->cache.insert(seq, tokens, n_tokens, &why);
+  return e == pkv::Err::ok ? PKV_OK : fail(to_status(e), why);
+}
+
+pkv_status radix_release(pkv_radix* r, int64_t seq) {
+  if (!r) return fail(PKV_ERR_ARG, "radix_release: NULL cache");
+  std::string why;
+  pkv::Err e = r->cache.release(seq, &why);
+  return e == pkv::Err::ok ? PKV_OK : fail(to_status(e), why);
+}
+
+pkv_status radix_evict(pkv_radix* r, int32_t want_free, int32_t* n_free) {
+  if (!r) return fail(PKV_ERR_ARG, "radix_evict: NULL cache");
+  const bool ok = r->cache.evict(want_free);
+  if (n_free) *n_free = static_cast<int32_t>(r->pool->core.free_list().size());
+  return ok ? PKV_OK
+            : fail(PKV_ERR_OOM, "radix_evict: every remaining cached block is under a live match");
+}
+
+pkv_status radix_stats(const pkv_radix* r, int32_t* nodes, int32_t* cached_blocks,
+                       int32_t* locked_nodes) {
+  if (!r) return fail(PKV_ERR_ARG, "radix_stats: NULL cache");
+  if (nodes) *nodes = r->cache.nodes();
+  if (cached_blocks) *cached_blocks = r->cache.cached_blocks();
+  if (locked_nodes) *locked_nodes = r->cache.locked_nodes();
+  return PKV_OK;
+}
+
+pkv_status radix_dump(const pkv_radix* r, int32_t* out, int32_t cap, int32_t* n) {
+  if (!r || !n) return fail(PKV_ERR_ARG, "radix_dump: NULL argument");
+  if (cap > 0 && !out) return fail(PKV_ERR_ARG, "radix_dump: NULL out with cap > 0");
+  std::vector<int32_t> d;
+  r->cache.dump(&d);
+  for (int32_t i = 0; i < static_cast<int32_t>(d.size()) && i < cap; ++i) out[i] = d[i];
+  *n = static_cast<int32_t>(d.size());
+  return PKV_OK;
 }
 
 pkv_status seq_block_table(const pkv_pool* p, int64_t seq, int32_t* out, int32_t cap,

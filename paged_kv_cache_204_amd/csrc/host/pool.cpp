@@ -37,6 +37,41 @@ int64_t BlockPool::allocate() {
   return id;
 }
 
+Err BlockPool::adopt(const int32_t* blocks, int32_t n_blocks, int32_t len, int64_t* seq,
+                     std::string* why) {
+  const int32_t B = shape_.block_size;
+  if (n_blocks < 0 || (n_blocks > 0 && !blocks) ||
+      (n_blocks == 0 ? len != 0 : (len <= (n_blocks - 1) * B || len > n_blocks * B))) {
+    *why = "adopt: length does not match the block count";
+    return Err::arg;
+  }
+  for (int32_t i = 0; i < n_blocks; ++i)
+    if (blocks[i] < 0 || blocks[i] >= shape_.num_blocks || rc_[blocks[i]] < 1) {
+      *why = "adopt: block " + std::to_string(blocks[i]) + " is not held";
+      return Err::arg;
+    }
+  SeqState s;
+  s.table.assign(blocks, blocks + n_blocks);
+  s.len = len;
+  s.epoch = ++epochs_;
+  for (int32_t b : s.table) ++rc_[b];
+  const int64_t id = next_id_++;
+  seqs_.emplace(id, std::move(s));
+  *seq = id;
+  ++version_;
+  return Err::ok;
+}
+
+void BlockPool::retain(int32_t block) {
+  ++rc_[block];
+  ++version_;
+}
+
+void BlockPool::drop(int32_t block) {
+  if (--rc_[block] == 0) fifo_.push_back(block);
+  ++version_;
+}
+
 const SeqState* BlockPool::find(int64_t seq) const {
   auto it = seqs_.find(seq);
   return it == seqs_.end() ? nullptr : &it->second;

@@ -91,6 +91,16 @@ class BlockPool {
   // Apply a prepared append (must be the next change to the pool).
   void commit_append(PendingAppend&& pa);
 
+  // A new sequence over existing blocks (a prefix-cache hit): its table is
+  // `blocks`, its length `len`, and every block gains a reference.  `len`
+  // must lie in ((n_blocks - 1) * B, n_blocks * B] (0 with no blocks) and
+  // every block must be held already.
+  Err adopt(const int32_t* blocks, int32_t n_blocks, int32_t len, int64_t* seq, std::string* why);
+  // A reference held outside any sequence (the prefix cache's own), taken
+  // on a held block / dropped (zero -> tail of the free list).
+  void retain(int32_t block);
+  void drop(int32_t block);
+
   const SeqState* find(int64_t seq) const;
   int32_t refcount(int32_t block) const { return rc_[block]; }
   const std::deque<int32_t>& free_list() const { return fifo_; }
