@@ -130,6 +130,31 @@ pkv_status kv_append(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
                      void* stream);
 
 /*
+ * Draft-tree commit: keep the accepted path of each sequence's draft tree
+ * and drop the other nodes (CAST page: the target model checks the draft
+ * tree in one pass and keeps the tokens it accepts -- lay summary part 2
+ * and the technical summary's accept length).  The tree is the sequence's
+ * last n_nodes tokens in node order, as for paged_attn_tree_verify.
+ * parent:   host int32 [n_seqs][n_nodes], parent[0] = -1, 0 <= parent[i] < i;
+ * path_len: host int32 [n_seqs], 0..n_nodes accepted nodes;
+ * paths:    host int32 [n_seqs][n_nodes], row i starting with path_len[i]
+ *           nodes: the root first, each node the parent of the next.
+ * Afterwards sequence i has length ctx + path_len[i] (ctx = len - n_nodes):
+ * its context, then the accepted nodes' K/V (all layers) in path order.
+ * Per sequence in call order, blocks past the new length lose a reference
+ * (table order; freed blocks go to the free-list tail), then each shared
+ * block that receives a moved token is copied first (copy-on-write, table
+ * order), taking only blocks that were free before the call.
+ * All-or-nothing (PKV_ERR_OOM / PKV_ERR_ARG / PKV_ERR_SEQ change nothing).
+ * Device work (device pools): one launch on `stream` (one per sequence
+ * when a block one sequence writes in place is read by another).
+ * 1 <= n_nodes <= 64; sequences must be distinct.
+ */
+pkv_status kv_tree_commit(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs, int32_t n_nodes,
+                          const int32_t* parent, const int32_t* path_len, const int32_t* paths,
+                          void* stream);
+
+/*
  * Decode attention at one layer: one query per sequence, GQA.
  * q:   device bf16 [n_seqs][num_q_heads][head_dim]
  * out: device fp32 [n_seqs][num_q_heads][head_dim]

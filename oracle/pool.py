@@ -223,6 +223,104 @@ class PoolModel:
                 self.filled[b] = max(self.filled[b], off + 1)
         return slots, cow
 
+    def tree_commit(self, seqs, n_nodes, parents, paths):
+        """Keep the accepted path of each sequence's draft tree, drop the rest.
+
+        The target model checks a draft tree in one pass and keeps the tokens
+        it accepts (CAST page: lay summary part 2, the target approves the
+        draft's guesses and the tree keeps other branches alive; technical
+        summary, the accept length).  Reading: the tree is the last
+        ``n_nodes`` tokens of the sequence in node order (as in verify);
+        ``paths[i]`` lists the accepted nodes root first, each the parent of
+        the next (possibly empty).  Afterwards the sequence is its context
+        followed by the accepted nodes' tokens, in path order, and blocks
+        past the new length are released in table order.
+
+        Per sequence in call order: (1) release the blocks past the new
+        length; (2) each block that receives a moved token (position
+        ``ctx + k`` with ``path[k] != k``) and is shared is copied first
+        (copy-on-write of its slots below the new length, fresh block from
+        the free-list head, the old block loses a reference), in table
+        order; copies take only blocks that were free before the call,
+        since a block this call releases may still hold a kept token.
+        All-or-nothing.  Returns the copies ``(src, dst, n_slots)``.
+        """
+        seqs = [int(s) for s in seqs]
+        if len(set(seqs)) != len(seqs):
+            raise ArgError("a sequence appears twice in one commit")
+        if len(parents) != len(seqs) or len(paths) != len(seqs):
+            raise ArgError("one tree and one path per sequence")
+        for s, par, path in zip(seqs, parents, paths):
+            self._check(s)
+            if not 1 <= n_nodes <= self.lens[s]:
+                raise ArgError("tree larger than the sequence")
+            par = [int(x) for x in par]
+            if len(par) != n_nodes or par[0] != -1 or any(not 0 <= par[i] < i for i in range(1, n_nodes)):
+                raise ArgError("parents must form a tree in node order")
+            path = [int(x) for x in path]
+            if path and (path[0] != 0 or any(par[path[k]] != path[k - 1] for k in range(1, len(path)))
+                         or any(not 0 <= x < n_nodes for x in path)):
+                raise ArgError("path must run from the root along parent links")
+        rc = list(self.rc)
+        fifo = deque(self.fifo)
+        free_before = len(self.fifo)    # copies take only blocks free before the call
+        taken = 0
+        tables = {s: list(self.tables[s]) for s in seqs}
+        lens = {s: self.lens[s] for s in seqs}
+        cow = []
+        for s, path in zip(seqs, paths):
+            t = tables[s]
+            ctx = lens[s] - n_nodes
+            new_len = ctx + len(path)
+            keep = -(-new_len // self.B)
+            for b in t[keep:]:
+                rc[b] -= 1
+                if rc[b] == 0:
+                    fifo.append(b)
+            del t[keep:]
+            written = sorted({(ctx + k) // self.B for k in range(len(path)) if path[k] != k})
+            for i in written:
+                if rc[t[i]] > 1:
+                    if taken >= free_before:
+                        raise OOMError("pool exhausted")
+                    src = t[i]
+                    dst = fifo.popleft()
+                    taken += 1
+                    rc[dst] = 1
+                    rc[src] -= 1
+                    t[i] = dst
+                    cow.append((s, src, dst, min(self.B, new_len - i * self.B)))
+            lens[s] = new_len
+        # data: every kept token's bits are read from the old layout first
+        moves = []
+        if self.store_data:
+            for s, path in zip(seqs, paths):
+                ctx = self.lens[s] - n_nodes
+                old = self.tables[s]
+                for k in range(len(path)):
+                    if path[k] != k:
+                        p = ctx + path[k]
+                        b, off = old[p // self.B], p % self.B
+                        moves.append((s, ctx + k, self.kbits[b, off].copy(), self.vbits[b, off].copy()))
+        self.rc = rc
+        self.fifo = fifo
+        for s in seqs:
+            self.tables[s] = tables[s]
+            self.lens[s] = lens[s]
+        for _, src, dst, n in cow:
+            if self.store_data:
+                self.kbits[dst, :n] = self.kbits[src, :n]
+                self.vbits[dst, :n] = self.vbits[src, :n]
+            self.filled[dst] = n
+        for s, pos, kb, vb in moves:
+            b, off = self.tables[s][pos // self.B], pos % self.B
+            self.kbits[b, off] = kb
+            self.vbits[b, off] = vb
+        for b in range(self.N):
+            if self.rc[b] == 0:
+                self.filled[b] = 0
+        return [(src, dst, n) for _, src, dst, n in cow]
+
     # --------------------------------------------------------- inspection
     def table(self, sid):
         self._check(sid)

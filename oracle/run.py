@@ -51,6 +51,11 @@ def run_program(workload, store_data=True, want=None, free_order=_DEFAULT):
                 q = workload.verify_query(key, len(hs), n_nodes)
                 result = tree_verify(pool, layer, [handles[h] for h in hs],
                                      parents, q, workload.sm_scale)
+        elif kind == "commit":
+            hs, n_nodes, tree_key, path_key = op[1], op[2], op[3], op[4]
+            parents = workload.tree_parents(tree_key, len(hs), n_nodes)
+            paths = workload.accept_paths(path_key, parents)
+            pool.tree_commit([handles[h] for h in hs], n_nodes, parents, paths)
         elif kind == "prefill":
             hs, layer, n_new, key = op[1], op[2], op[3], op[4]
             if store_data and (want is None or idx in want):

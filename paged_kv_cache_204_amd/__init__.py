@@ -22,7 +22,7 @@ __all__ = [
     "PkvError", "PkvDesc", "load", "library_path",
     "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy",
     "seq_allocate", "seq_fork", "seq_free", "kv_append",
-    "paged_attn_decode", "paged_attn_tree_verify", "paged_attn_prefill",
+    "paged_attn_decode", "paged_attn_tree_verify", "paged_attn_prefill", "kv_tree_commit",
     "seq_block_table", "block_refcount", "free_list", "kv_last_append",
     "paged_attn_decode_plan_stats", "pkv_timing_enable", "pkv_timing_read", "pkv_last_error",
     "seq_ids",
@@ -102,6 +102,7 @@ def load():
                                           ctypes.c_float, _P, _P, _P]),
         "paged_attn_prefill": (_I32, [_P, _I32, _PI64, _I32, _PI32, _P, ctypes.c_float, _P, _P,
                                       _P]),
+        "kv_tree_commit": (_I32, [_P, _PI64, _I32, _I32, _PI32, _PI32, _PI32, _P]),
         "seq_block_table": (_I32, [_P, _I64, _PI32, _I32, _PI32, _PI32]),
         "block_refcount": (_I32, [_P, _I32, _PI32]),
         "free_list": (_I32, [_P, _PI32, _I32, _PI32]),
@@ -266,6 +267,25 @@ def paged_attn_prefill(pool, layer, seqs, n_new, q, sm_scale, out, lse=None, str
         raise ValueError("n_new must hold one count per sequence")
     _check(load().paged_attn_prefill(pool, int(layer), p, n, nn.ctypes.data_as(_PI32), _addr(q),
                                      float(sm_scale), _addr(out), _addr(lse), _stream(stream)))
+
+
+def kv_tree_commit(pool, seqs, n_nodes, parent, paths, stream=None):
+    """paths: one list of accepted nodes (root first) per sequence."""
+    p, n = _seq_array(seqs)
+    par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32).reshape(-1))
+    if par.size != n * int(n_nodes):
+        raise ValueError("parent must hold n_seqs * n_nodes entries")
+    if len(paths) != n:
+        raise ValueError("one path per sequence")
+    plen = np.asarray([len(x) for x in paths], dtype=np.int32)
+    pad = np.zeros((max(n, 1), int(n_nodes)), dtype=np.int32)
+    for i, x in enumerate(paths):
+        if len(x) > n_nodes:
+            raise ValueError("a path longer than the tree")
+        pad[i, :len(x)] = x
+    _check(load().kv_tree_commit(pool, p, n, int(n_nodes), par.ctypes.data_as(_PI32),
+                                 plen.ctypes.data_as(_PI32), pad.ctypes.data_as(_PI32),
+                                 _stream(stream)))
 
 
 def seq_block_table(pool, seq):

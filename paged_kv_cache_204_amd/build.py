@@ -23,6 +23,7 @@ SOURCES = [
     "host/radix.cpp",
     "capi.hip",
     "kernels/append.hip",
+    "kernels/commit.hip",
     "kernels/attn.hip",
     "kernels/merge.hip",
 ]

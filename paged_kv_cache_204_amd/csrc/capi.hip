@@ -109,7 +109,7 @@ struct pkv_pool {
   int dev = -1;
   uint16_t* k_pool = nullptr;
   uint16_t* v_pool = nullptr;
-  DevBuf append_plan, decode_plan, verify_plan, prefill_plan, partials;
+  DevBuf append_plan, commit_plan, decode_plan, verify_plan, prefill_plan, partials;
   void* stage[kStageSlots] = {};
   size_t stage_cap[kStageSlots] = {};
   hipEvent_t stage_ev[kStageSlots] = {};
@@ -380,7 +380,7 @@ void kv_pool_destroy(pkv_pool* p) {
   if (p->device) {
     DeviceGuard g(p->dev);
     (void)hipDeviceSynchronize();
-    for (DevBuf* b : {&p->append_plan, &p->decode_plan, &p->verify_plan, &p->prefill_plan, &p->partials})
+    for (DevBuf* b : {&p->append_plan, &p->commit_plan, &p->decode_plan, &p->verify_plan, &p->prefill_plan, &p->partials})
       if (b->ptr) (void)hipFree(b->ptr);
     for (int i = 0; i < kStageSlots; ++i) {
       if (p->stage[i]) (void)hipHostFree(p->stage[i]);
@@ -467,6 +467,69 @@ pkv_status kv_append(pkv_pool* p, const int64_t* seqs, int32_t n_seqs, int32_t n
     PKV_HIP(pkv::launch_append(ap, st));
   }
   p->core.commit_append(std::move(pa));
+  return PKV_OK;
+}
+
+pkv_status kv_tree_commit(pkv_pool* p, const int64_t* seqs, int32_t n_seqs, int32_t n_nodes,
+                          const int32_t* parent, const int32_t* path_len, const int32_t* paths,
+                          void* stream) {
+  if (!p) return fail(PKV_ERR_ARG, "kv_tree_commit: NULL pool");
+  if (n_seqs == 0) return PKV_OK;
+  pkv::PendingCommit pc;
+  std::string why;
+  pkv::Err e = p->core.prepare_commit(seqs, n_seqs, n_nodes, parent, path_len, paths, &pc, &why);
+  if (e != pkv::Err::ok) return fail(to_status(e), why);
+  if (p->device && (!pc.cow.empty() || !pc.move_src.empty())) {
+    DeviceGuard g(p->dev);
+    PKV_HIP(g.err);
+    const pkv::Shape& sh = p->core.shape();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t n_mv = pc.move_src.size();
+    const size_t off_src = align16((pc.seq_cow.size() + pc.seq_move.size()) * sizeof(int32_t));
+    const size_t off_dst = off_src + align16(n_mv * sizeof(int32_t));
+    const size_t off_cow = off_dst + align16(n_mv * sizeof(int32_t));
+    const size_t bytes = off_cow + pc.cow.size() * 3 * sizeof(int32_t);
+    pkv_status s = upload(p, p->commit_plan, bytes, st, [&](char* dst) {
+      std::memcpy(dst, pc.seq_cow.data(), pc.seq_cow.size() * sizeof(int32_t));
+      std::memcpy(dst + pc.seq_cow.size() * sizeof(int32_t), pc.seq_move.data(),
+                  pc.seq_move.size() * sizeof(int32_t));
+      std::memcpy(dst + off_src, pc.move_src.data(), n_mv * sizeof(int32_t));
+      std::memcpy(dst + off_dst, pc.move_dst.data(), n_mv * sizeof(int32_t));
+      int32_t* c = reinterpret_cast<int32_t*>(dst + off_cow);
+      for (size_t k = 0; k < pc.cow.size(); ++k) {
+        c[3 * k + 0] = pc.cow[k].src;
+        c[3 * k + 1] = pc.cow[k].dst;
+        c[3 * k + 2] = pc.cow[k].n_slots;
+      }
+    });
+    if (s != PKV_OK) return s;
+    const char* base = static_cast<const char*>(p->commit_plan.ptr);
+    pkv::CommitParams cp{};
+    cp.k_pool = p->k_pool;
+    cp.v_pool = p->v_pool;
+    cp.seq_cow = reinterpret_cast<const int32_t*>(base);
+    cp.seq_move = cp.seq_cow + pc.seq_cow.size();
+    cp.move_src = reinterpret_cast<const int32_t*>(base + off_src);
+    cp.move_dst = reinterpret_cast<const int32_t*>(base + off_dst);
+    cp.cow = reinterpret_cast<const int32_t*>(base + off_cow);
+    cp.L = sh.num_layers;
+    cp.N = sh.num_blocks;
+    cp.Hkv = sh.num_kv_heads;
+    cp.B = sh.block_size;
+    cp.log2B = p->core.log2_block();
+    cp.D = sh.head_dim;
+    if (!pc.conflict) {
+      cp.seq0 = 0;
+      PKV_HIP(pkv::launch_commit(cp, n_seqs, st));
+    } else {
+      // a block written in place by one sequence is read by another: in order
+      for (int32_t i = 0; i < n_seqs; ++i) {
+        cp.seq0 = i;
+        PKV_HIP(pkv::launch_commit(cp, 1, st));
+      }
+    }
+  }
+  p->core.commit_commit(std::move(pc));
   return PKV_OK;
 }
 

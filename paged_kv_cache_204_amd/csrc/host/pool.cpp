@@ -198,4 +198,140 @@ void BlockPool::commit_append(PendingAppend&& pa) {
   last_append_ = std::move(pa.result);
 }
 
+Err BlockPool::prepare_commit(const int64_t* seqs, int32_t n_seqs, int32_t n_nodes,
+                              const int32_t* parent, const int32_t* path_len, const int32_t* paths,
+                              PendingCommit* out, std::string* why) const {
+  if (n_seqs < 0 || (n_seqs > 0 && (!seqs || !parent || !path_len || !paths))) {
+    *why = "kv_tree_commit: bad arguments";
+    return Err::arg;
+  }
+  if (n_seqs > 0 && (n_nodes < 1 || n_nodes > 64)) {
+    *why = "kv_tree_commit: n_nodes must be in 1..64";
+    return Err::arg;
+  }
+  const int32_t B = shape_.block_size;
+  std::vector<const SeqState*> st(n_seqs);
+  {
+    std::unordered_set<int64_t> seen;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      auto it = seqs_.find(seqs[i]);
+      if (it == seqs_.end()) {
+        *why = "kv_tree_commit: unknown sequence " + std::to_string(seqs[i]);
+        return Err::seq;
+      }
+      if (!seen.insert(seqs[i]).second) {
+        *why = "kv_tree_commit: sequence " + std::to_string(seqs[i]) + " appears twice";
+        return Err::arg;
+      }
+      if (it->second.len < n_nodes) {
+        *why = "kv_tree_commit: sequence " + std::to_string(seqs[i]) + " is shorter than its tree";
+        return Err::arg;
+      }
+      const int32_t* par = parent + static_cast<size_t>(i) * n_nodes;
+      bool tree = par[0] == -1;
+      for (int32_t j = 1; j < n_nodes && tree; ++j) tree = par[j] >= 0 && par[j] < j;
+      const int32_t np = path_len[i];
+      const int32_t* pa = paths + static_cast<size_t>(i) * n_nodes;
+      bool ok = tree && np >= 0 && np <= n_nodes && (np == 0 || pa[0] == 0);
+      for (int32_t k = 1; k < np && ok; ++k) ok = pa[k] > 0 && pa[k] < n_nodes && par[pa[k]] == pa[k - 1];
+      if (!ok) {
+        *why = "kv_tree_commit: sequence " + std::to_string(seqs[i]) +
+               ": parent[] is not a tree in node order or the path does not run from the root "
+               "along parent links";
+        return Err::arg;
+      }
+      st[i] = &it->second;
+    }
+  }
+  std::unordered_map<int32_t, int32_t> rcm;
+  auto rc_of = [&](int32_t b) {
+    auto it = rcm.find(b);
+    return it == rcm.end() ? rc_[b] : it->second;
+  };
+  out->states.clear();
+  out->pushed.clear();
+  out->cow.clear();
+  out->move_src.clear();
+  out->move_dst.clear();
+  out->seq_cow.assign(1, 0);
+  out->seq_move.assign(1, 0);
+  out->taken = 0;
+  out->conflict = false;
+  // old tree block -> the sequence reading it (-2: more than one)
+  std::unordered_map<int32_t, int32_t> reader;
+  std::vector<std::pair<int32_t, int32_t>> in_place;   // (block, sequence) written without a copy
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    SeqState s = *st[i];
+    const int32_t np = path_len[i];
+    const int32_t* pa = paths + static_cast<size_t>(i) * n_nodes;
+    const int32_t ctx = s.len - n_nodes;
+    const int32_t new_len = ctx + np;
+    const int32_t keep = (new_len + B - 1) / B;
+    for (size_t b = keep; b < s.table.size(); ++b) {
+      const int32_t blk = s.table[b];
+      const int32_t r = rc_of(blk) - 1;
+      rcm[blk] = r;
+      if (r == 0) out->pushed.push_back(blk);
+    }
+    const std::vector<int32_t> old = s.table;
+    s.table.resize(keep);
+    int32_t last_written = -1;
+    for (int32_t k = 0; k < np; ++k) {
+      if (pa[k] == k) continue;
+      const int32_t bi = (ctx + k) / B;
+      if (bi != last_written) {
+        last_written = bi;
+        if (rc_of(s.table[bi]) > 1) {
+          // copies take blocks that were free before the call, never one this
+          // call releases (its old tokens may still be read by a move)
+          if (out->taken >= fifo_.size()) {
+            *why = "kv_tree_commit: pool exhausted (copy-on-write of a shared tree block)";
+            return Err::oom;
+          }
+          const int32_t dst = fifo_[out->taken];
+          ++out->taken;
+          const int32_t src = s.table[bi];
+          rcm[dst] = 1;
+          rcm[src] = rc_of(src) - 1;
+          s.table[bi] = dst;
+          out->cow.push_back(CowCopy{src, dst, std::min(B, new_len - bi * B)});
+        } else {
+          in_place.emplace_back(s.table[bi], i);
+        }
+      }
+      const int32_t sp = ctx + pa[k];
+      const int32_t sb = old[sp / B];
+      auto rd = reader.emplace(sb, i);
+      if (!rd.second && rd.first->second != i) rd.first->second = -2;
+      out->move_src.push_back(sb * B + sp % B);
+      out->move_dst.push_back(s.table[bi] * B + (ctx + k) % B);
+    }
+    s.len = new_len;
+    s.epoch = 0;
+    out->states.emplace_back(seqs[i], std::move(s));
+    out->seq_cow.push_back(static_cast<int32_t>(out->cow.size()));
+    out->seq_move.push_back(static_cast<int32_t>(out->move_src.size()));
+  }
+  // every sequence's moves read its old blocks; a block written in place by
+  // one sequence and read by another needs the sequences in order
+  for (const auto& w : in_place) {
+    auto it = reader.find(w.first);
+    if (it != reader.end() && it->second != w.second) out->conflict = true;   // -2 included
+  }
+  out->refcounts.assign(rcm.begin(), rcm.end());
+  out->version = version_;
+  return Err::ok;
+}
+
+void BlockPool::commit_commit(PendingCommit&& pc) {
+  for (int32_t b : pc.pushed) fifo_.push_back(b);
+  for (size_t k = 0; k < pc.taken; ++k) fifo_.pop_front();
+  for (const auto& br : pc.refcounts) rc_[br.first] = br.second;
+  for (auto& ss : pc.states) {
+    ss.second.epoch = ++epochs_;
+    seqs_[ss.first] = std::move(ss.second);
+  }
+  if (!pc.states.empty()) ++version_;
+}
+
 }  // namespace pkv

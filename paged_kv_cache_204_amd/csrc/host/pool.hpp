@@ -73,6 +73,23 @@ struct PendingAppend {
   uint64_t version = 0;                                 // pool version it was computed on
 };
 
+// A draft-tree commit worked out against the current state (see
+// BlockPool::prepare_commit).  Token moves are physical slots
+// (block * B + offset): the source in the sequence's old table, the
+// destination in its new one.
+struct PendingCommit {
+  std::vector<std::pair<int64_t, SeqState>> states;
+  std::vector<std::pair<int32_t, int32_t>> refcounts;  // final refcount of each touched block
+  std::vector<int32_t> pushed;   // blocks released to the free-list tail, in order
+  size_t taken = 0;              // taken from the head (blocks free before the call)
+  std::vector<CowCopy> cow;      // all sequences' copies, in order
+  std::vector<int32_t> move_src, move_dst;
+  std::vector<int32_t> seq_cow;  // per sequence: first copy, one past the last at [i + 1]
+  std::vector<int32_t> seq_move; // per sequence: first move, likewise
+  bool conflict = false;         // a sequence writes in place a block another one reads
+  uint64_t version = 0;
+};
+
 class BlockPool {
  public:
   BlockPool(const Shape& s, const int32_t* free_order);
@@ -90,6 +107,18 @@ class BlockPool {
                      PendingAppend* out, std::string* why) const;
   // Apply a prepared append (must be the next change to the pool).
   void commit_append(PendingAppend&& pa);
+
+  // Keep the accepted path of each sequence's draft tree (its last n_nodes
+  // tokens, node order; parent [n_seqs][n_nodes]; path i = paths[i *
+  // n_nodes ...], path_len[i] nodes, root first along parent links) and drop
+  // the rest.  Per sequence in call order: blocks past the new length go
+  // back (table order), then every shared block that receives a moved
+  // token is copied first (copy-on-write, table order).  Nothing changes
+  // until commit_commit; errors leave no trace.
+  Err prepare_commit(const int64_t* seqs, int32_t n_seqs, int32_t n_nodes, const int32_t* parent,
+                     const int32_t* path_len, const int32_t* paths, PendingCommit* out,
+                     std::string* why) const;
+  void commit_commit(PendingCommit&& pc);
 
   // A new sequence over existing blocks (a prefix-cache hit): its table is
   // `blocks`, its length `len`, and every block gains a reference.  `len`

@@ -48,6 +48,23 @@ struct AttnParams {
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+
+// Draft-tree commit: per sequence, copy-on-write copies then token moves
+// (physical slots block * B + offset), one thread per pool column.
+struct CommitParams {
+  uint16_t* k_pool;          // [L][N][Hkv][B][D]
+  uint16_t* v_pool;
+  const int32_t* cow;        // [n_cow][3] (src, dst, slots copied)
+  const int32_t* move_src;   // [n_move] old slot of the kept token
+  const int32_t* move_dst;   // [n_move] its new slot
+  const int32_t* seq_cow;    // [n_seqs + 1] copies of sequence i: [seq_cow[i], seq_cow[i + 1])
+  const int32_t* seq_move;   // [n_seqs + 1] likewise for moves
+  int32_t seq0;              // first sequence of this launch
+  int32_t L, N, Hkv, B, log2B, D;
+};
+
+// Sequences seq0 .. seq0 + n_seqs - 1 of the plan, side by side.
+hipError_t launch_commit(const CommitParams& p, int32_t n_seqs, hipStream_t s);
 // valu_rows: the most rows any VALU item of the launch holds (<= 8);
 // waves: 4, or 8 for launches of MFMA items only (row_tiles 2).  Non-null
 // events take the start and end times of the kernel's own dispatch.

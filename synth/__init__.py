@@ -33,6 +33,7 @@ from .workloads import (
     mcts_workload,
     verify_workload,
     prefill_workload,
+    verify_commit_workload,
     draw_tree,
 )
 
@@ -52,5 +53,6 @@ __all__ = [
     "mcts_workload",
     "verify_workload",
     "prefill_workload",
+    "verify_commit_workload",
     "draw_tree",
 ]

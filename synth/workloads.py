@@ -16,6 +16,10 @@ Ops (tuples):
   ``n_nodes`` tokens of every sequence in ``hs`` are the tree's nodes (in node
   order); parents from :meth:`Workload.tree_parents`, Q from
   :meth:`Workload.verify_query`
+* ``("commit", hs, n_nodes, tree_key, path_key)``  keep the accepted path of
+  each sequence's draft tree (parents from :meth:`Workload.tree_parents`
+  with ``tree_key``, paths from :meth:`Workload.accept_paths`) and drop the
+  other nodes
 * ``("prefill", hs, layer, n_new, key)``    causal attention of the newest
   ``n_new[i]`` tokens of sequence ``hs[i]`` (already appended) over its whole
   cache; Q from :meth:`Workload.prefill_query`
@@ -106,6 +110,26 @@ class Workload:
         q = self._rng(STREAM_Q, key).standard_normal(
             (n_queries, s.num_q_heads, s.head_dim), dtype=np.float32)
         return f32_to_bf16_bits(q)
+
+    def accept_paths(self, key: int, parents):
+        """One accepted path per tree (root first along parent links): from
+        the root, step to a uniformly drawn child with probability 0.8, else
+        stop; with probability 0.1 nothing is accepted."""
+        rng = self._rng(STREAM_TREE + 1, key)
+        out = []
+        for par in np.asarray(parents):
+            kids = {}
+            for i in range(1, len(par)):
+                kids.setdefault(int(par[i]), []).append(i)
+            if rng.random() < 0.1:
+                out.append([])
+                continue
+            path = [0]
+            while kids.get(path[-1]) and rng.random() < 0.8:
+                ch = kids[path[-1]]
+                path.append(ch[int(rng.integers(len(ch)))])
+            out.append(path)
+        return out
 
     def tree_parents(self, key: int, n_seqs: int, n_nodes: int):
         """int32 ``[n_seqs][n_nodes]`` parent pointers, one draft tree per sequence."""
@@ -266,6 +290,40 @@ def verify_workload(name, cfg_id, shape, n_seqs, ctx_len, n_nodes, tree_depth,
                               tree_depth=tree_depth))
 
 
+def verify_commit_workload(name, cfg_id, shape, n_seqs, ctx_len, n_nodes, tree_depth, rounds=1,
+                           fork_after=False, sm_scale=None, permute=False, description=""):
+    """Speculative rounds: every sequence appends a draft tree, every layer
+    verifies it, the accepted paths are committed, then one more token is
+    appended and decoded.  ``fork_after``: each sequence is forked after its
+    first tree is appended (the fork shares the tree blocks and issues no
+    queries), so commits copy the shared blocks they write.
+    """
+    hs = tuple(range(n_seqs))
+    ops = [("alloc", h) for h in hs]
+    if ctx_len:
+        ops.append(("append", hs, ctx_len, len(ops)))
+    nxt = n_seqs
+    for r in range(rounds):
+        ops.append(("append", hs, n_nodes, len(ops)))
+        tree_key = len(ops)
+        if fork_after and r == 0:
+            for h in hs:
+                ops.append(("fork", h, nxt))
+                nxt += 1
+        for layer in range(shape.num_layers):
+            ops.append(("verify", hs, layer, n_nodes, tree_key))
+        ops.append(("commit", hs, n_nodes, tree_key, len(ops)))
+        ops.append(("append", hs, 1, len(ops)))
+        for layer in range(shape.num_layers):
+            ops.append(("decode", hs, layer, len(ops)))
+    return Workload(name, cfg_id, shape, ops,
+                    _default_scale(shape) if sm_scale is None else sm_scale,
+                    permute_free_list=permute, tree_depth=tree_depth,
+                    description=description,
+                    meta=dict(n_seqs=n_seqs, ctx_len=ctx_len, n_nodes=n_nodes,
+                              tree_depth=tree_depth, rounds=rounds))
+
+
 def prefill_workload(name, cfg_id, shape, shared_len, own_lens, sm_scale=None,
                      description=""):
     """Prompts whose first ``shared_len`` tokens hit a cached prefix.
@@ -364,6 +422,15 @@ def _c2_prefill():
                     "of the other 256 tokens of every prompt (4096 queries)")
 
 
+def _c5_commit():
+    shape = Shape(32, 8, 128, 16, 1, 1536)
+    return verify_commit_workload(
+        "c5_verify_commit", 5, shape, n_seqs=8, ctx_len=2048, n_nodes=64, tree_depth=6,
+        description="32 q / 8 kv heads, D 128, B 16; 8 sequences with 2048-token "
+                    "context; append a 64-node depth-6 draft tree, verify, commit the "
+                    "accepted paths, append and decode one token")
+
+
 _NAMED = {
     "c1_tiny_fork": _c1,
     "c2_trellis": _c2,
@@ -373,6 +440,7 @@ _NAMED = {
     "c4_mcts_folded": lambda: _c4(True),
     "c5_verify": _c5,
     "c2_trellis_prefill": _c2_prefill,
+    "c5_verify_commit": _c5_commit,
 }
 NAMES = tuple(_NAMED)
 

@@ -95,6 +95,12 @@ def run_gpu(workload, want=None, free_order="default", on_result=None, pool_cb=N
                                            parents, q, workload.sm_scale, out, lse, gp.stream)
                 if want is None or idx in want:
                     results[idx] = (out.cpu().numpy(), lse.cpu().numpy())
+            elif kind == "commit":
+                hs, n_nodes, tree_key, path_key = op[1], op[2], op[3], op[4]
+                parents = workload.tree_parents(tree_key, len(hs), n_nodes)
+                paths = workload.accept_paths(path_key, parents)
+                pkv.kv_tree_commit(gp.pool, [handles[h] for h in hs], n_nodes, parents, paths,
+                                   gp.stream)
             elif kind == "prefill":
                 hs, layer, n_new, key = op[1], op[2], op[3], op[4]
                 total = sum(n_new)

@@ -130,6 +130,24 @@ def reduced():
         "prefill_ctx0": synth.prefill_workload(
             "prefill_ctx0", 19, Shape(32, 4, 64, 32, 2, 128), shared_len=0,
             own_lens=[300, 5, 64]),
+        # speculative rounds: verify a draft tree, commit the accepted paths
+        # (pool contents checked bit for bit), decode after the commit
+        "commit_small": synth.verify_commit_workload(
+            "commit_small", 21, Shape(32, 8, 128, 16, 2, 256), n_seqs=3, ctx_len=77, n_nodes=20,
+            tree_depth=5, rounds=2, permute=True),
+        # forks share the tree blocks: commits copy the blocks they write
+        "commit_forked": synth.verify_commit_workload(
+            "commit_forked", 22, Shape(32, 4, 64, 8, 1, 256), n_seqs=4, ctx_len=45, n_nodes=33,
+            tree_depth=7, rounds=2, fork_after=True),
+        # a sequence and its fork commit different paths of the tree they
+        # share in one call: the second writes in place blocks the first
+        # reads, so the commit runs the sequences one after the other
+        "commit_shared": synth.Workload(
+            "commit_shared", 23, Shape(16, 4, 64, 4, 1, 128),
+            [("alloc", 0), ("append", (0,), 50, 1), ("append", (0,), 16, 2), ("fork", 0, 1),
+             ("verify", (0, 1), 0, 16, 2), ("commit", (0, 1), 16, 2, 10), ("append", (0, 1), 1, 6),
+             ("decode", (0, 1), 0, 7)],
+            1.0 / math.sqrt(64), tree_depth=6),
         # repeated prefill calls: the same call at the next layer (plan reused),
         # the same arguments after an append (pool changed: planned afresh),
         # other counts
@@ -295,7 +313,7 @@ def sample_ops(wl, every):
     ("c3_dendrite", 9, "auto"), ("c3_dendrite", 31, "direct"), ("c3_dendrite", 31, "manyparts"),
     ("c3_dendrite_aligned", 31, "auto"),
     ("c4_mcts", 1, "auto"), ("c4_mcts_folded", 1, "auto"), ("c5_verify", 1, "auto"),
-    ("c2_trellis_prefill", 1, "auto"),
+    ("c2_trellis_prefill", 1, "auto"), ("c5_verify_commit", 1, "auto"),
 ])
 def test_full_workload_parity(dev, name, every, path, monkeypatch):
     """The five workloads at full size, launched as the benchmark launches
