@@ -234,7 +234,9 @@ pkv_status paged_attn_prefill(pkv_pool* pool, int32_t layer, const int64_t* seqs
  * before it (Trellis page, hit rate at most (L/B - 1)/(L/B) when the probe
  * differs in the last block).  The cache holds one reference on every block
  * it caches; blocks leave the pool only when their refcount reaches zero.
- * A cache borrows its pool: destroy the cache first.  Not thread-safe.
+ * A cache borrows its pool.  Destroying the pool first detaches its caches:
+ * their calls then fail with PKV_ERR_ARG and radix_destroy only frees the
+ * cache.  Not thread-safe.
  * Access order for eviction is a counter bumped per touched node.
  * None of these calls enqueues device work.
  */

@@ -6,6 +6,7 @@
 // buffers for plan uploads, and the kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdlib>
 #include <cstring>
@@ -101,8 +102,11 @@ struct DeviceGuard {
 
 }  // namespace
 
+struct pkv_radix;
+
 struct pkv_pool {
   explicit pkv_pool(const pkv::Shape& s, const int32_t* order) : core(s, order) {}
+  std::vector<pkv_radix*> radixes;   // live prefix caches over this pool
   pkv::BlockPool core;
   pkv::PlanConfig cfg;
   bool device = false;
@@ -142,6 +146,25 @@ struct pkv_pool {
   double timed_ms = 0.0;
   int64_t timed_calls = 0;
 };
+
+struct pkv_radix {
+  explicit pkv_radix(pkv_pool* p) : pool(p), cache(&p->core) {}
+  pkv_pool* pool;          // null once the pool was destroyed first
+  pkv::RadixCache cache;
+};
+
+namespace {
+// A pool destroyed before its caches: they forget it (their later calls
+// fail, radix_destroy frees only the cache itself).
+void detach_radixes(pkv_pool* p) {
+  for (pkv_radix* r : p->radixes) {
+    r->cache.detach();
+    r->pool = nullptr;
+  }
+  p->radixes.clear();
+}
+}  // namespace
+
 
 namespace {
 
@@ -377,6 +400,7 @@ pkv_status kv_pool_create(const pkv_desc* d, void* k_pool, void* v_pool,
 
 void kv_pool_destroy(pkv_pool* p) {
   if (!p) return;
+  detach_radixes(p);
   if (p->device) {
     DeviceGuard g(p->dev);
     (void)hipDeviceSynchronize();
@@ -653,23 +677,27 @@ pkv_status paged_attn_prefill(pkv_pool* p, int32_t layer, const int64_t* seqs, i
 
 // ---- radix prefix cache --------------------------------------------------
 
-struct pkv_radix {
-  explicit pkv_radix(pkv_pool* p) : pool(p), cache(&p->core) {}
-  pkv_pool* pool;
-  pkv::RadixCache cache;
-};
-
 pkv_status radix_create(pkv_pool* p, pkv_radix** out) {
   if (!p || !out) return fail(PKV_ERR_ARG, "radix_create: NULL argument");
   *out = new (std::nothrow) pkv_radix(p);
-  return *out ? PKV_OK : fail(PKV_ERR_OOM, "radix_create: out of host memory");
+  if (!*out) return fail(PKV_ERR_OOM, "radix_create: out of host memory");
+  p->radixes.push_back(*out);
+  return PKV_OK;
 }
 
-void radix_destroy(pkv_radix* r) { delete r; }
+void radix_destroy(pkv_radix* r) {
+  if (!r) return;
+  if (r->pool) {
+    auto& v = r->pool->radixes;
+    v.erase(std::remove(v.begin(), v.end(), r), v.end());
+  }
+  delete r;
+}
 
 pkv_status radix_match(pkv_radix* r, const int32_t* tokens, int32_t n_tokens, int64_t* out_seq,
                        int32_t* out_matched) {
   if (!r || !out_seq || !out_matched) return fail(PKV_ERR_ARG, "radix_match: NULL argument");
+  if (!r->pool) return fail(PKV_ERR_ARG, "radix_match: the cache's pool was destroyed");
   std::string why;
   pkv::Err e = r->cache.match(tokens, n_tokens, out_seq, out_matched, &why);
   return e == pkv::Err::ok ? PKV_OK : fail(to_status(e), why);
@@ -677,6 +705,7 @@ pkv_status radix_match(pkv_radix* r, const int32_t* tokens, int32_t n_tokens, in
 
 pkv_status radix_insert(pkv_radix* r, int64_t seq, const int32_t* tokens, int32_t n_tokens) {
   if (!r) return fail(PKV_ERR_ARG, "radix_insert: NULL cache");
+  if (!r->pool) return fail(PKV_ERR_ARG, "radix_insert: the cache's pool was destroyed");
   std::string why;
   pkv::Err e = r->cache.insert(seq, tokens, n_tokens, &why);
   return e == pkv::Err::ok ? PKV_OK : fail(to_status(e), why);
@@ -684,6 +713,7 @@ pkv_status radix_insert(pkv_radix* r, int64_t seq, const int32_t* tokens, int32_
 
 pkv_status radix_release(pkv_radix* r, int64_t seq) {
   if (!r) return fail(PKV_ERR_ARG, "radix_release: NULL cache");
+  if (!r->pool) return fail(PKV_ERR_ARG, "radix_release: the cache's pool was destroyed");
   std::string why;
   pkv::Err e = r->cache.release(seq, &why);
   return e == pkv::Err::ok ? PKV_OK : fail(to_status(e), why);
@@ -691,6 +721,7 @@ pkv_status radix_release(pkv_radix* r, int64_t seq) {
 
 pkv_status radix_evict(pkv_radix* r, int32_t want_free, int32_t* n_free) {
   if (!r) return fail(PKV_ERR_ARG, "radix_evict: NULL cache");
+  if (!r->pool) return fail(PKV_ERR_ARG, "radix_evict: the cache's pool was destroyed");
   const bool ok = r->cache.evict(want_free);
   if (n_free) *n_free = static_cast<int32_t>(r->pool->core.free_list().size());
   return ok ? PKV_OK
@@ -700,6 +731,7 @@ pkv_status radix_evict(pkv_radix* r, int32_t want_free, int32_t* n_free) {
 pkv_status radix_stats(const pkv_radix* r, int32_t* nodes, int32_t* cached_blocks,
                        int32_t* locked_nodes) {
   if (!r) return fail(PKV_ERR_ARG, "radix_stats: NULL cache");
+  if (!r->pool) return fail(PKV_ERR_ARG, "radix_stats: the cache's pool was destroyed");
   if (nodes) *nodes = r->cache.nodes();
   if (cached_blocks) *cached_blocks = r->cache.cached_blocks();
   if (locked_nodes) *locked_nodes = r->cache.locked_nodes();
@@ -708,6 +740,7 @@ pkv_status radix_stats(const pkv_radix* r, int32_t* nodes, int32_t* cached_block
 
 pkv_status radix_dump(const pkv_radix* r, int32_t* out, int32_t cap, int32_t* n) {
   if (!r || !n) return fail(PKV_ERR_ARG, "radix_dump: NULL argument");
+  if (!r->pool) return fail(PKV_ERR_ARG, "radix_dump: the cache's pool was destroyed");
   if (cap > 0 && !out) return fail(PKV_ERR_ARG, "radix_dump: NULL out with cap > 0");
   std::vector<int32_t> d;
   r->cache.dump(&d);

@@ -7,6 +7,7 @@ namespace pkv {
 RadixCache::RadixCache(BlockPool* pool) : pool_(pool) {}
 
 RadixCache::~RadixCache() {
+  if (!pool_) return;
   // preorder, children in key order, each edge's blocks in order
   std::vector<RadixNode*> stack{&root_};
   while (!stack.empty()) {

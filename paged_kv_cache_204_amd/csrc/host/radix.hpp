@@ -60,7 +60,10 @@ struct RadixNode {
 class RadixCache {
  public:
   explicit RadixCache(BlockPool* pool);
-  ~RadixCache();   // drops the cache's block references
+  ~RadixCache();   // drops the cache's block references (unless detached)
+  // The pool goes away first: forget it; the destructor then drops nothing.
+  void detach() { pool_ = nullptr; }
+  bool attached() const { return pool_ != nullptr; }
   RadixCache(const RadixCache&) = delete;
   RadixCache& operator=(const RadixCache&) = delete;
 

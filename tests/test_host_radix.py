@@ -189,3 +189,16 @@ def test_random_programs_match_the_oracle(B, N, seed):
         random_program(p, rng, 300, vocab=3)
     finally:
         p.close()
+
+
+def test_pool_destroyed_before_its_cache():
+    c = host_pool(8, 2)
+    r = pkv.radix_create(c)
+    s, _ = pkv.radix_match(r, [1, 2, 3])
+    pkv.kv_append(c, [s], 3, None, None, None)
+    pkv.radix_insert(r, s, [1, 2, 3])
+    pkv.kv_pool_destroy(c)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.radix_match(r, [1, 2])
+    assert e.value.code == pkv.PKV_ERR_ARG
+    pkv.radix_destroy(r)          # frees the cache only; must not touch the dead pool
