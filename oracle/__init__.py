@@ -16,6 +16,8 @@ Contents:
   (one query per sequence), draft-tree verify (context plus tree
   ancestors and the node itself) and causal prefill of a sequence's newest
   tokens over its whole cache.
+* :mod:`oracle.quant` -- 4-bit K/V codes (rotation, Lloyd-Max levels, fp16
+  norm) and decode attention over them.
 * :mod:`oracle.radix` -- a block-paged radix-tree prefix cache over the pool
   model: match, split-on-insert, release, leaf-first LRU eviction.
 * :mod:`oracle.run` -- runs a ``synth`` op program through the two.

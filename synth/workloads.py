@@ -44,6 +44,7 @@ STREAM_V = 2
 STREAM_Q = 3
 STREAM_PERM = 4
 STREAM_TREE = 5
+STREAM_SIGNS = 7
 
 
 @dataclass(frozen=True)
@@ -89,6 +90,11 @@ class Workload:
             k = k * np.float32(self.k_scale)
         v = self._rng(STREAM_V, key).standard_normal(size, dtype=np.float32)
         return f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+    def rotation_signs(self):
+        """int8 [head_dim] of +-1: the random signs of a 4-bit pool's rotation."""
+        rng = self._rng(STREAM_SIGNS, 0)
+        return np.where(rng.random(self.shape.head_dim) < 0.5, -1, 1).astype(np.int8)
 
     def decode_query(self, key: int, n_seqs: int):
         """bf16 bits of Q, ``[n_seqs][Hq][D]`` (uint16)."""
