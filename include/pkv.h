@@ -90,6 +90,42 @@ size_t kv_pool_bytes(const pkv_desc* desc);
 pkv_status kv_pool_create(const pkv_desc* desc, void* k_pool, void* v_pool,
                           const int32_t* free_order, pkv_pool** out);
 
+/*
+ * 4-bit pools.  The Dendrite page keeps the KV cache in 4 bits (TurboQuant)
+ * for 3.88x less memory and computes from the quantized indices instead of
+ * dequantizing the cache on every call (Dendrite page: summary and the
+ * TurboQuant integration line).  Format of one token's K (or V) vector x of
+ * one kv head: its norm in fp16 and head_dim 4-bit codes of the rotated
+ * direction R x / |x|, R = H diag(signs) / sqrt(head_dim) (H the Sylvester
+ * Hadamard matrix), each coordinate times sqrt(head_dim) quantized to the
+ * 16-level Lloyd-Max levels of the unit normal (Max 1960).  2 + head_dim / 2
+ * bytes per vector: 66 against 256 bf16 bytes at head_dim 128.
+ * Device arrays (caller-owned, 16-byte aligned), for K and for V:
+ *   codes u8   [num_layers][num_blocks][num_kv_heads][block_size][head_dim / 2]
+ *              (byte j: dim 2j in the low nibble, dim 2j + 1 in the high one;
+ *              code c names the c-th level in ascending order),
+ *   norms fp16 [num_layers][num_blocks][num_kv_heads][block_size].
+ * kv_pool_q4_bytes returns the bytes of one codes array and writes those of
+ * one norms array to *norm_bytes (0 if desc is invalid).
+ */
+size_t kv_pool_q4_bytes(const pkv_desc* desc, size_t* norm_bytes);
+
+/*
+ * Create a 4-bit pool: same allocator and calls as kv_pool_create, but
+ * kv_append quantizes the new bf16 K/V into codes and norms (copy-on-write
+ * copies codes and norms), and paged_attn_decode computes attention from the
+ * codes: a key's score is norm * sum_d T[d][code_d] with per-query tables
+ * T built from the rotated query, and V is summed in the rotated space and
+ * rotated back once.  The result is attention over the dequantized K/V.
+ * signs: host int8 [head_dim] of +1 / -1 (the rotation's random signs).
+ * head_dim 64 or 128, (num_q_heads / num_kv_heads) * head_dim <= 512, else
+ * PKV_ERR_UNSUPPORTED.  paged_attn_tree_verify, paged_attn_prefill and
+ * kv_tree_commit return PKV_ERR_UNSUPPORTED on a 4-bit pool.
+ */
+pkv_status kv_pool_create_q4(const pkv_desc* desc, void* k_codes, void* v_codes, void* k_norms,
+                             void* v_norms, const int8_t* signs, const int32_t* free_order,
+                             pkv_pool** out);
+
 /* Synchronise the pool's device, then free its scratch and metadata. NULL is a no-op. */
 void kv_pool_destroy(pkv_pool* pool);
 

@@ -27,7 +27,9 @@ head_dim 128:
   S = sum x^2, b_k the positive decision levels -- all in float64, where
   y, y^2 and S are exact for bf16 inputs of ordinary range, so both sides
   take the same decision;
-* the norm is stored as fp16(fp32(sqrt(S))).
+* the norm is stored as the fp16 value nearest to sqrt(S), ties to even
+  (decided exactly: S and the squares of fp16 midpoints are exact in
+  float64).
 
 Dequantized vector: x_hat = n * R^T (LEVELS[code] / sqrt(D))
                           = n * s * (H LEVELS[code]) / D.
@@ -78,8 +80,26 @@ def quantize(bits, signs):
     for b in DECISION_POS:
         level += y2 > (b * b) * S
     codes = np.where(y >= 0, 8 + level, 7 - level).astype(np.uint8)
-    norm = np.sqrt(S[..., 0]).astype(np.float32).astype(np.float16)
-    return codes, norm.view(np.uint16)
+    return codes, fp16_nearest_sqrt(S[..., 0])
+
+
+def fp16_nearest_sqrt(S):
+    """Bits of the fp16 nearest to sqrt(S) (ties to even), for exact S >= 0.
+
+    Start from float16(float64 sqrt) and step to a neighbour while S lies
+    beyond the squared midpoint towards it.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    h = np.sqrt(S).astype(np.float16).view(np.uint16).astype(np.int64)
+    val = lambda b: np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float64)
+    for _ in range(2):
+        v = val(h)
+        lo = 0.5 * (v + val(np.maximum(h - 1, 0)))
+        hi = 0.5 * (v + val(np.minimum(h + 1, 0x7BFF)))
+        down = (h > 0) & ((S < lo * lo) | ((S == lo * lo) & (h % 2 == 1)))
+        up = ~down & (h < 0x7BFF) & ((S > hi * hi) | ((S == hi * hi) & (h % 2 == 1)))
+        h = h - down + up
+    return h.astype(np.uint16)
 
 
 def dequantize(codes, norm_bits, signs):

@@ -20,7 +20,7 @@ import numpy as np
 
 __all__ = [
     "PkvError", "PkvDesc", "load", "library_path",
-    "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy",
+    "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_q4_bytes", "kv_pool_create_q4",
     "seq_allocate", "seq_fork", "seq_free", "kv_append",
     "paged_attn_decode", "paged_attn_tree_verify", "paged_attn_prefill", "kv_tree_commit",
     "seq_block_table", "block_refcount", "free_list", "kv_last_append",
@@ -93,6 +93,9 @@ def load():
         "kv_pool_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvDesc)]),
         "kv_pool_create": (_I32, [ctypes.POINTER(PkvDesc), _P, _P, _PI32, ctypes.POINTER(_P)]),
         "kv_pool_destroy": (None, [_P]),
+        "kv_pool_q4_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvDesc), ctypes.POINTER(ctypes.c_size_t)]),
+        "kv_pool_create_q4": (_I32, [ctypes.POINTER(PkvDesc), _P, _P, _P, _P,
+                                     ctypes.POINTER(ctypes.c_int8), _PI32, ctypes.POINTER(_P)]),
         "seq_allocate": (_I32, [_P, _PI64]),
         "seq_fork": (_I32, [_P, _I64, _PI64]),
         "seq_free": (_I32, [_P, _I64]),
@@ -212,6 +215,30 @@ def kv_pool_create(desc, k_pool=None, v_pool=None, free_order=None):
     out = _P()
     _check(load().kv_pool_create(ctypes.byref(d), _addr(k_pool), _addr(v_pool), fo,
                                  ctypes.byref(out)))
+    return out
+
+
+def kv_pool_q4_bytes(desc):
+    """(bytes of one codes array, bytes of one norms array) of a 4-bit pool."""
+    nb = ctypes.c_size_t()
+    codes = load().kv_pool_q4_bytes(ctypes.byref(_desc(desc)), ctypes.byref(nb))
+    return codes, nb.value
+
+
+def kv_pool_create_q4(desc, k_codes, v_codes, k_norms, v_norms, signs, free_order=None):
+    d = _desc(desc)
+    sg = np.ascontiguousarray(np.asarray(signs, dtype=np.int8).reshape(-1))
+    if sg.size != d.head_dim:
+        raise ValueError("one sign per head dimension")
+    fo = None
+    keep = None
+    if free_order is not None:
+        keep = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+        fo = keep.ctypes.data_as(_PI32)
+    out = _P()
+    _check(load().kv_pool_create_q4(ctypes.byref(d), _addr(k_codes), _addr(v_codes), _addr(k_norms),
+                                    _addr(v_norms), sg.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)),
+                                    fo, ctypes.byref(out)))
     return out
 
 

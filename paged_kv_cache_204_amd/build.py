@@ -26,6 +26,7 @@ SOURCES = [
     "kernels/commit.hip",
     "kernels/attn.hip",
     "kernels/merge.hip",
+    "kernels/quant.hip",
 ]
 
 ARCH = "gfx950"

@@ -114,6 +114,15 @@ struct pkv_pool {
   uint16_t* k_pool = nullptr;
   uint16_t* v_pool = nullptr;
   DevBuf append_plan, commit_plan, decode_plan, verify_plan, prefill_plan, partials;
+  // 4-bit pools: codes and norms instead of bf16 K/V (k_pool / v_pool unused)
+  bool q4 = false;
+  uint8_t* k_codes = nullptr;
+  uint8_t* v_codes = nullptr;
+  uint16_t* k_norms = nullptr;
+  uint16_t* v_norms = nullptr;
+  DevBuf signs;   // float [head_dim], +-1
+  std::vector<pkv::Q4Item> q4_items;
+  std::vector<int32_t> q4_blocks;
   void* stage[kStageSlots] = {};
   size_t stage_cap[kStageSlots] = {};
   hipEvent_t stage_ev[kStageSlots] = {};
@@ -398,13 +407,65 @@ pkv_status kv_pool_create(const pkv_desc* d, void* k_pool, void* v_pool,
   return PKV_OK;
 }
 
+size_t kv_pool_q4_bytes(const pkv_desc* d, size_t* norm_bytes) {
+  if (norm_bytes) *norm_bytes = 0;
+  if (!d) return 0;
+  pkv::Shape s{d->num_blocks, d->block_size, d->num_layers, d->num_q_heads, d->num_kv_heads, d->head_dim};
+  if (!pkv::valid_shape(s, nullptr)) return 0;
+  const size_t vecs = static_cast<size_t>(s.num_layers) * s.num_blocks * s.num_kv_heads * s.block_size;
+  if (norm_bytes) *norm_bytes = vecs * sizeof(uint16_t);
+  return vecs * static_cast<size_t>(s.head_dim / 2);
+}
+
+pkv_status kv_pool_create_q4(const pkv_desc* d, void* k_codes, void* v_codes, void* k_norms,
+                             void* v_norms, const int8_t* signs, const int32_t* free_order,
+                             pkv_pool** out) {
+  if (!d || !out) return fail(PKV_ERR_ARG, "kv_pool_create_q4: desc and out must not be NULL");
+  *out = nullptr;
+  if (!k_codes || !v_codes || !k_norms || !v_norms || !signs)
+    return fail(PKV_ERR_ARG, "kv_pool_create_q4: codes, norms and signs are required");
+  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_norms) || !aligned16(v_norms))
+    return fail(PKV_ERR_ARG, "kv_pool_create_q4: device arrays must be 16-byte aligned");
+  pkv::Shape s{d->num_blocks, d->block_size, d->num_layers, d->num_q_heads, d->num_kv_heads, d->head_dim};
+  std::string why;
+  if (!pkv::valid_shape(s, &why)) return fail(PKV_ERR_ARG, "kv_pool_create_q4: " + why);
+  if (s.head_dim != 64 && s.head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_pool_create_q4: head_dim must be 64 or 128");
+  if (static_cast<int64_t>(s.num_q_heads / s.num_kv_heads) * s.head_dim > pkv::kQ4MaxRowDims)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_pool_create_q4: (q heads per kv head) x head_dim must be <= 512");
+  for (int32_t i = 0; i < s.head_dim; ++i)
+    if (signs[i] != 1 && signs[i] != -1) return fail(PKV_ERR_ARG, "kv_pool_create_q4: signs must be +1 or -1");
+  // a placeholder bf16 pair keeps the device path of kv_pool_create; never read
+  pkv_status st = kv_pool_create(d, k_codes, v_codes, free_order, out);
+  if (st != PKV_OK) return st;
+  pkv_pool* p = *out;
+  p->q4 = true;
+  p->k_pool = p->v_pool = nullptr;
+  p->k_codes = static_cast<uint8_t*>(k_codes);
+  p->v_codes = static_cast<uint8_t*>(v_codes);
+  p->k_norms = static_cast<uint16_t*>(k_norms);
+  p->v_norms = static_cast<uint16_t*>(v_norms);
+  std::vector<float> sf(signs, signs + s.head_dim);
+  for (float& f : sf) f = f > 0 ? 1.f : -1.f;
+  DeviceGuard g(p->dev);
+  st = ensure(p->signs, sf.size() * sizeof(float));
+  hipError_t e = st == PKV_OK ? hipMemcpy(p->signs.ptr, sf.data(), sf.size() * sizeof(float), hipMemcpyHostToDevice)
+                              : hipErrorOutOfMemory;
+  if (e != hipSuccess) {
+    kv_pool_destroy(p);
+    *out = nullptr;
+    return fail(PKV_ERR_HIP, std::string("kv_pool_create_q4: ") + hipGetErrorString(e));
+  }
+  return PKV_OK;
+}
+
 void kv_pool_destroy(pkv_pool* p) {
   if (!p) return;
   detach_radixes(p);
   if (p->device) {
     DeviceGuard g(p->dev);
     (void)hipDeviceSynchronize();
-    for (DevBuf* b : {&p->append_plan, &p->commit_plan, &p->decode_plan, &p->verify_plan, &p->prefill_plan, &p->partials})
+    for (DevBuf* b : {&p->append_plan, &p->commit_plan, &p->decode_plan, &p->verify_plan, &p->prefill_plan, &p->partials, &p->signs})
       if (b->ptr) (void)hipFree(b->ptr);
     for (int i = 0; i < kStageSlots; ++i) {
       if (p->stage[i]) (void)hipHostFree(p->stage[i]);
@@ -473,6 +534,29 @@ pkv_status kv_append(pkv_pool* p, const int64_t* seqs, int32_t n_seqs, int32_t n
       }
     });
     if (s != PKV_OK) return s;
+    if (p->q4) {
+      pkv::Q4AppendParams qp{};
+      qp.k_new = static_cast<const uint16_t*>(k_new);
+      qp.v_new = static_cast<const uint16_t*>(v_new);
+      qp.k_codes = p->k_codes;
+      qp.v_codes = p->v_codes;
+      qp.k_norms = p->k_norms;
+      qp.v_norms = p->v_norms;
+      qp.signs = static_cast<const float*>(p->signs.ptr);
+      qp.slots = static_cast<const int32_t*>(p->append_plan.ptr);
+      qp.cow = reinterpret_cast<const int32_t*>(static_cast<const char*>(p->append_plan.ptr) + cow_off);
+      qp.n_rows = n_seqs * n_tok;
+      qp.n_cow = static_cast<int32_t>(pa.result.cow.size());
+      qp.L = sh.num_layers;
+      qp.N = sh.num_blocks;
+      qp.Hkv = sh.num_kv_heads;
+      qp.B = sh.block_size;
+      qp.log2B = p->core.log2_block();
+      qp.D = sh.head_dim;
+      PKV_HIP(pkv::launch_q4_append(qp, st));
+      p->core.commit_append(std::move(pa));
+      return PKV_OK;
+    }
     pkv::AppendParams ap{};
     ap.k_new = static_cast<const uint16_t*>(k_new);
     ap.v_new = static_cast<const uint16_t*>(v_new);
@@ -498,6 +582,7 @@ pkv_status kv_tree_commit(pkv_pool* p, const int64_t* seqs, int32_t n_seqs, int3
                           const int32_t* parent, const int32_t* path_len, const int32_t* paths,
                           void* stream) {
   if (!p) return fail(PKV_ERR_ARG, "kv_tree_commit: NULL pool");
+  if (p->q4) return fail(PKV_ERR_UNSUPPORTED, "kv_tree_commit: 4-bit pools support decode only");
   if (n_seqs == 0) return PKV_OK;
   pkv::PendingCommit pc;
   std::string why;
@@ -557,6 +642,68 @@ pkv_status kv_tree_commit(pkv_pool* p, const int64_t* seqs, int32_t n_seqs, int3
   return PKV_OK;
 }
 
+namespace {
+
+// Decode over a 4-bit pool: one workgroup per (query, kv head) over all of
+// the query's keys, straight from the codes.
+pkv_status decode_q4(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs, const void* q,
+                     float sm_scale, float* out, float* lse, void* stream) {
+  const pkv::Shape& sh = p->core.shape();
+  p->q4_items.clear();
+  p->q4_blocks.clear();
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const pkv::SeqState* st = p->core.find(seqs[i]);
+    if (!st) return fail(PKV_ERR_SEQ, "paged_attn_decode: unknown sequence " + std::to_string(seqs[i]));
+    if (st->len == 0) return fail(PKV_ERR_EMPTY, "paged_attn_decode: empty sequence " + std::to_string(seqs[i]));
+    p->q4_items.push_back(pkv::Q4Item{static_cast<int32_t>(p->q4_blocks.size()), st->len, i, 0});
+    p->q4_blocks.insert(p->q4_blocks.end(), st->table.begin(), st->table.end());
+  }
+  DeviceGuard g(p->dev);
+  PKV_HIP(g.err);
+  hipStream_t stv = static_cast<hipStream_t>(stream);
+  const size_t items_bytes = p->q4_items.size() * sizeof(pkv::Q4Item);
+  const size_t blk_off = align16(items_bytes);
+  const size_t bytes = blk_off + p->q4_blocks.size() * sizeof(int32_t);
+  pkv_status s = upload(p, p->decode_plan, bytes, stv, [&](char* dst) {
+    std::memcpy(dst, p->q4_items.data(), items_bytes);
+    std::memcpy(dst + blk_off, p->q4_blocks.data(), p->q4_blocks.size() * sizeof(int32_t));
+  });
+  if (s != PKV_OK) return s;
+  p->dcache_valid = false;   // the decode plan buffer now holds this call's lists
+  const char* base = static_cast<const char*>(p->decode_plan.ptr);
+  pkv::Q4DecodeParams dp{};
+  dp.items = reinterpret_cast<const pkv::Q4Item*>(base);
+  dp.blocks = reinterpret_cast<const int32_t*>(base + blk_off);
+  dp.q = static_cast<const uint16_t*>(q);
+  dp.k_codes = p->k_codes;
+  dp.v_codes = p->v_codes;
+  dp.k_norms = p->k_norms;
+  dp.v_norms = p->v_norms;
+  dp.signs = static_cast<const float*>(p->signs.ptr);
+  dp.out = out;
+  dp.lse = lse;
+  dp.layer = layer;
+  dp.N = sh.num_blocks;
+  dp.Hq = sh.num_q_heads;
+  dp.Hkv = sh.num_kv_heads;
+  dp.G = sh.num_q_heads / sh.num_kv_heads;
+  dp.B = sh.block_size;
+  dp.log2B = p->core.log2_block();
+  dp.scale_log2 = sm_scale * pkv::kLog2eHost;
+  hipEvent_t ev_a = nullptr, ev_b = nullptr;
+  const bool timed = p->timing && (p->timing_tick++ % p->timing_every) == 0;
+  if (timed) {
+    s = take_event(p, &ev_a);
+    if (s == PKV_OK) s = take_event(p, &ev_b);
+    if (s != PKV_OK) return s;
+  }
+  PKV_HIP(pkv::launch_q4_decode(dp, n_seqs, sh.head_dim, stv, ev_a, ev_b));
+  if (timed) p->ev_pending.emplace_back(ev_a, ev_b);
+  return PKV_OK;
+}
+
+}  // namespace
+
 pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs,
                              const void* q, float sm_scale, float* out, float* lse, void* stream) {
   if (!p) return fail(PKV_ERR_ARG, "paged_attn_decode: NULL pool");
@@ -568,6 +715,7 @@ pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, in
     return fail(PKV_ERR_ARG, "paged_attn_decode: layer out of range");
   if (!aligned16(q) || !aligned16(out))
     return fail(PKV_ERR_ARG, "paged_attn_decode: q and out must be 16-byte aligned");
+  if (p->q4) return decode_q4(p, layer, seqs, n_seqs, q, sm_scale, out, lse, stream);
   DeviceGuard g(p->dev);
   PKV_HIP(g.err);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -610,6 +758,7 @@ pkv_status paged_attn_tree_verify(pkv_pool* p, int32_t layer, const int64_t* seq
                                   float sm_scale, float* out, float* lse, void* stream) {
   if (!p) return fail(PKV_ERR_ARG, "paged_attn_tree_verify: NULL pool");
   if (!p->device) return fail(PKV_ERR_ARG, "paged_attn_tree_verify: the pool has no device storage");
+  if (p->q4) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_tree_verify: 4-bit pools support decode only");
   if (n_seqs < 0) return fail(PKV_ERR_ARG, "paged_attn_tree_verify: negative n_seqs");
   if (n_seqs == 0) return PKV_OK;
   if (!seqs || !parent || !q || !out)
@@ -638,6 +787,7 @@ pkv_status paged_attn_prefill(pkv_pool* p, int32_t layer, const int64_t* seqs, i
                               float* lse, void* stream) {
   if (!p) return fail(PKV_ERR_ARG, "paged_attn_prefill: NULL pool");
   if (!p->device) return fail(PKV_ERR_ARG, "paged_attn_prefill: the pool has no device storage");
+  if (p->q4) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill: 4-bit pools support decode only");
   if (n_seqs < 0) return fail(PKV_ERR_ARG, "paged_attn_prefill: negative n_seqs");
   if (n_seqs == 0) return PKV_OK;
   if (!seqs || !n_new) return fail(PKV_ERR_ARG, "paged_attn_prefill: NULL seqs or n_new");

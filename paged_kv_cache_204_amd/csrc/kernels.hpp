@@ -49,6 +49,51 @@ struct AttnParams {
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
+// 4-bit pools: codes u8 [L][N][Hkv][B][D/2] (two 4-bit codes per byte, the
+// lower dim in the low nibble) and fp16 norms [L][N][Hkv][B], for K and V.
+constexpr int kQ4MaxRowDims = 512;   // G * head_dim of a 4-bit pool (LDS lookup tables)
+
+struct Q4AppendParams {
+  const uint16_t* k_new;   // [L][n_rows][Hkv][D] bf16
+  const uint16_t* v_new;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  uint16_t* k_norms;
+  uint16_t* v_norms;
+  const float* signs;      // [D] +-1
+  const int32_t* slots;    // [n_rows] block * B + offset
+  const int32_t* cow;      // [n_cow][3] (src, dst, filled slots)
+  int32_t n_rows, n_cow;
+  int32_t L, N, Hkv, B, log2B, D;
+};
+
+struct Q4Item {
+  int32_t blk_off;   // the query's table at blocks[blk_off ...]
+  int32_t n_tok;     // keys
+  int32_t q_index;   // query vector (q, out, lse rows)
+  int32_t pad;
+};
+
+struct Q4DecodeParams {
+  const Q4Item* items;
+  const int32_t* blocks;
+  const uint16_t* q;       // [n][Hq][D] bf16
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint16_t* k_norms;
+  const uint16_t* v_norms;
+  const float* signs;
+  float* out;              // [n][Hq][D]
+  float* lse;              // [n][Hq] or null
+  int32_t layer, N, Hq, Hkv, G, B, log2B;
+  float scale_log2;
+};
+
+hipError_t launch_q4_append(const Q4AppendParams& p, hipStream_t s);
+// One workgroup per (item, kv head); head_dim 64 or 128, G * head_dim <= kQ4MaxRowDims.
+hipError_t launch_q4_decode(const Q4DecodeParams& p, int32_t n_items, int32_t head_dim, hipStream_t s,
+                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+
 // Draft-tree commit: per sequence, copy-on-write copies then token moves
 // (physical slots block * B + offset), one thread per pool column.
 struct CommitParams {

@@ -24,7 +24,7 @@ from scipy import stats
 import synth
 from oracle import PoolModel, bf16_bits_to_f64, decode
 from oracle.quant import (DECISION_POS, LEVELS, MAX_MSE, RECON_POS, decode_q4, dequantize,
-                          hadamard, quantize, rotation)
+                          fp16_nearest_sqrt, hadamard, quantize, rotation)
 
 
 def bits(rng, shape, scale=1.0):
@@ -137,3 +137,29 @@ def test_attention_over_codes():
             assert math.isclose(lse[1, h], z.max() + math.log(p.sum()), abs_tol=1e-12)
         # close to attention over the original bf16 vectors
         assert np.abs(out - exact).mean() < 0.05
+
+
+def test_norm_is_the_nearest_fp16_of_the_square_root():
+    """Brute force over every positive finite fp16: the stored norm of S is
+    the fp16 closest to sqrt(S) (exact rational comparison), ties to even."""
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    all_h = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    # S from bf16 sums of squares, plus exact squares of fp16 values and of midpoints
+    x = bits(rng, (300, 64)).astype(np.uint32) << 16
+    S = list((x.view(np.float32).astype(np.float64) ** 2).sum(-1))
+    S += [v * v for v in all_h[::97]]
+    S += [(0.5 * (a + b)) ** 2 for a, b in zip(all_h[:-1:211], all_h[1::211])]
+    got = fp16_nearest_sqrt(np.array(S)).view(np.float16).astype(np.float64)
+    for s_, g in zip(S, got):
+        fs = Fraction(s_)
+        i = np.searchsorted(all_h, np.sqrt(s_))
+        cands = [c for c in all_h[max(0, i - 2):i + 2]]
+        # |c - sqrt(S)| compared through (c^2 - S) signs: pick by squared midpoints
+        best = min(cands, key=lambda c: (abs(Fraction(c) ** 2 - fs) / (Fraction(c) + Fraction(np.sqrt(s_)))))
+        if best != g:
+            # only a tie may differ, and then g must have the even mantissa
+            lo, hi = sorted([best, g])
+            mid = (Fraction(lo) + Fraction(hi)) / 2
+            assert mid * mid == fs
+            assert int(np.float16(g).view(np.uint16)) % 2 == 0
