@@ -17,7 +17,8 @@
 //
 // Decode: one workgroup per (query, kv head).  The G query rows are rotated
 // once, qh = H (s * q), and turned into per-row tables T[d][c] = qh_d *
-// level_c * scale / D, so a key's score is norm * sum_d T[d][code_d] -- table
+// level_c * scale / D (all rows of an entry side by side), so a key's score
+// is norm * sum_d T[d][code_d] -- table
 // lookups on the codes, no dequantized keys.  Chunks of 256 keys, one per
 // thread, with an online softmax across chunks; V is accumulated in the
 // rotated space, acc_d = sum_t p_t norm_t level(code_t,d), by lanes over
@@ -194,8 +195,8 @@ template <int D>
 __global__ __launch_bounds__(kChunk) void q4_decode_kernel(Q4DecodeParams p) {
   constexpr int HALF = D / 2;
   constexpr int MAXG = kQ4MaxRowDims / D;
-  __shared__ float lut[kQ4MaxRowDims * 16];        // [g][d][code]
-  __shared__ float sc[MAXG][kChunk];               // scores, then p * v-norm
+  __shared__ __align__(16) float lut[kQ4MaxRowDims * 16];   // [d][code][g], MAXG rows
+  __shared__ __align__(16) float sc[kChunk][MAXG];   // [key][row]: scores, then probabilities
   __shared__ __align__(16) uint8_t vcs[kChunk][HALF];   // V codes of the chunk
   __shared__ float accs[4][kQ4MaxRowDims];         // per-wave partial V sums [g][d]
   __shared__ float vn_s[kChunk];                   // V norms of the chunk
@@ -226,8 +227,8 @@ __global__ __launch_bounds__(kChunk) void q4_decode_kernel(Q4DecodeParams p) {
     if (on) {
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
-        lut[(g * D + 2 * lane) * 16 + c] = y0 * kLevels[c] * tscale;
-        lut[(g * D + 2 * lane + 1) * 16 + c] = y1 * kLevels[c] * tscale;
+        lut[((2 * lane) * 16 + c) * MAXG + g] = y0 * kLevels[c] * tscale;
+        lut[((2 * lane + 1) * 16 + c) * MAXG + g] = y1 * kLevels[c] * tscale;
       }
     }
   }
@@ -263,32 +264,46 @@ __global__ __launch_bounds__(kChunk) void q4_decode_kernel(Q4DecodeParams p) {
       }
       const float kn = __half2float(__ushort_as_half(p.k_norms[vec]));
       vn_s[tid] = __half2float(__ushort_as_half(p.v_norms[vec]));
-      for (int g = 0; g < G; ++g) {
-        const float* tg = lut + g * D * 16;
-        float s = 0.f;
+      // one accumulator per row; the MAXG row values of a (dim, code) entry
+      // are contiguous, so a key dim costs MAXG / 4 128-bit reads (rows past
+      // G hold no data and are never used)
+      float sg[MAXG];
 #pragma unroll
-        for (int w = 0; w < HALF / 4; ++w) {
-          const uint32_t word = kw[w];
+      for (int g = 0; g < MAXG; ++g) sg[g] = 0.f;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) s += tg[(8 * w + j) * 16 + ((word >> (4 * j)) & 15u)];
+      for (int w = 0; w < HALF / 4; ++w) {
+        const uint32_t word = kw[w];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float4* e = reinterpret_cast<const float4*>(
+              lut + ((8 * w + j) * 16 + ((word >> (4 * j)) & 15u)) * MAXG);
+#pragma unroll
+          for (int g4 = 0; g4 < MAXG / 4; ++g4) {
+            const float4 v = e[g4];
+            sg[4 * g4 + 0] += v.x;
+            sg[4 * g4 + 1] += v.y;
+            sg[4 * g4 + 2] += v.z;
+            sg[4 * g4 + 3] += v.w;
+          }
         }
-        sc[g][tid] = s * kn;
       }
+#pragma unroll
+      for (int g = 0; g < MAXG; ++g) sc[tid][g] = sg[g] * kn;
     }
     __syncthreads();
     // per row: chunk max, new running max, probabilities (times the V norm)
     for (int g = wave; g < G; g += 4) {
       float mx = -INFINITY;
-      for (int i = lane; i < nt; i += 64) mx = fmaxf(mx, sc[g][i]);
+      for (int i = lane; i < nt; i += 64) mx = fmaxf(mx, sc[i][g]);
       mx = wave_max(mx);
       const float m_old = m_s[g];
       const float m_new = fmaxf(m_old, mx);
       const float alpha = m_old == -INFINITY ? 0.f : fast_exp2(m_old - m_new);
       float ps = 0.f;
       for (int i = lane; i < nt; i += 64) {
-        const float pr = fast_exp2(sc[g][i] - m_new);
+        const float pr = fast_exp2(sc[i][g] - m_new);
         ps += pr;
-        sc[g][i] = pr;
+        sc[i][g] = pr;
       }
       ps = wave_sum(ps);
       if (lane == 0) {
@@ -301,24 +316,39 @@ __global__ __launch_bounds__(kChunk) void q4_decode_kernel(Q4DecodeParams p) {
     // V: lanes over dims (two per lane), waves over keys of the chunk
 #pragma unroll
     for (int g = 0; g < MAXG; ++g) {
-      if (g < G) {
-        const float al = a_s[g];
-        acc0[g] *= al;
-        acc1[g] *= al;
-      }
+      const float al = g < G ? a_s[g] : 0.f;
+      acc0[g] *= al;
+      acc1[g] *= al;
     }
     if (on) {
-      for (int i = wave; i < nt; i += 4) {
-        const float vn = vn_s[i];
-        const uint32_t byte = vcs[i][lane];
-        const float l0 = lv_s[byte & 15u] * vn;
-        const float l1 = lv_s[byte >> 4] * vn;
+      // four keys per step, every load of the step issued before the sums;
+      // keys past the chunk's end re-read its last key with weight 0
+      for (int i0 = wave; i0 < nt; i0 += 16) {
+        float l0[4], l1[4];
+        int ic[4];
 #pragma unroll
-        for (int g = 0; g < MAXG; ++g) {
-          if (g < G) {
-            const float pr = sc[g][i];
-            acc0[g] = fmaf(pr, l0, acc0[g]);
-            acc1[g] = fmaf(pr, l1, acc1[g]);
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + 4 * u;
+          ic[u] = min(i, nt - 1);
+          const uint32_t byte = vcs[ic[u]][lane];
+          const float vn = i < nt ? vn_s[ic[u]] : 0.f;
+          l0[u] = lv_s[byte & 15u] * vn;
+          l1[u] = lv_s[byte >> 4] * vn;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float4* pr4 = reinterpret_cast<const float4*>(sc[ic[u]]);
+#pragma unroll
+          for (int g4 = 0; g4 < MAXG / 4; ++g4) {
+            const float4 pr = pr4[g4];
+            acc0[4 * g4 + 0] = fmaf(pr.x, l0[u], acc0[4 * g4 + 0]);
+            acc1[4 * g4 + 0] = fmaf(pr.x, l1[u], acc1[4 * g4 + 0]);
+            acc0[4 * g4 + 1] = fmaf(pr.y, l0[u], acc0[4 * g4 + 1]);
+            acc1[4 * g4 + 1] = fmaf(pr.y, l1[u], acc1[4 * g4 + 1]);
+            acc0[4 * g4 + 2] = fmaf(pr.z, l0[u], acc0[4 * g4 + 2]);
+            acc1[4 * g4 + 2] = fmaf(pr.z, l1[u], acc1[4 * g4 + 2]);
+            acc0[4 * g4 + 3] = fmaf(pr.w, l0[u], acc0[4 * g4 + 3]);
+            acc1[4 * g4 + 3] = fmaf(pr.w, l1[u], acc1[4 * g4 + 3]);
           }
         }
       }
