@@ -431,8 +431,6 @@ pkv_status kv_pool_create_q4(const pkv_desc* d, void* k_codes, void* v_codes, vo
   if (!pkv::valid_shape(s, &why)) return fail(PKV_ERR_ARG, "kv_pool_create_q4: " + why);
   if (s.head_dim != 64 && s.head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "kv_pool_create_q4: head_dim must be 64 or 128");
-  if (static_cast<int64_t>(s.num_q_heads / s.num_kv_heads) * s.head_dim > pkv::kQ4MaxRowDims)
-    return fail(PKV_ERR_UNSUPPORTED, "kv_pool_create_q4: (q heads per kv head) x head_dim must be <= 512");
   for (int32_t i = 0; i < s.head_dim; ++i)
     if (signs[i] != 1 && signs[i] != -1) return fail(PKV_ERR_ARG, "kv_pool_create_q4: signs must be +1 or -1");
   // a placeholder bf16 pair keeps the device path of kv_pool_create; never read

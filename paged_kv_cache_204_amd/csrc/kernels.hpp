@@ -51,7 +51,6 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
 // 4-bit pools: codes u8 [L][N][Hkv][B][D/2] (two 4-bit codes per byte, the
 // lower dim in the low nibble) and fp16 norms [L][N][Hkv][B], for K and V.
-constexpr int kQ4MaxRowDims = 512;   // G * head_dim of a 4-bit pool (LDS lookup tables)
 
 struct Q4AppendParams {
   const uint16_t* k_new;   // [L][n_rows][Hkv][D] bf16
@@ -90,7 +89,7 @@ struct Q4DecodeParams {
 };
 
 hipError_t launch_q4_append(const Q4AppendParams& p, hipStream_t s);
-// One workgroup per (item, kv head); head_dim 64 or 128, G * head_dim <= kQ4MaxRowDims.
+// One workgroup per (item, kv head); head_dim 64 or 128, G <= 16.
 hipError_t launch_q4_decode(const Q4DecodeParams& p, int32_t n_items, int32_t head_dim, hipStream_t s,
                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 

@@ -16,13 +16,12 @@
 // (decision level b_k) is decided exactly, the same on any implementation.
 //
 // Decode: one workgroup per (query, kv head).  The G query rows are rotated
-// once, qh = H (s * q), and turned into per-row tables T[d][c] = qh_d *
-// level_c * scale / D (all rows of an entry side by side), so a key's score
-// is norm * sum_d T[d][code_d] -- table
-// lookups on the codes, no dequantized keys.  Chunks of 256 keys, one per
-// thread, with an online softmax across chunks; V is accumulated in the
-// rotated space, acc_d = sum_t p_t norm_t level(code_t,d), by lanes over
-// dims, and rotated back once at the end: out = s * (H acc) / (D l).
+// once, qh = H (s * q); in the rotated space a key's score is
+// (scale / D) * norm_k * sum_d qh_d level(code_d), so the MFMA contracts qh
+// with the codes' levels (fp16, from a byte -> two-levels table) and never
+// forms a dequantized key; V is accumulated in the rotated space, acc_d =
+// sum_t p_t norm_t level(code_t,d), and rotated back once at the end:
+// out = s * (H acc) / (D l).
 #include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 
@@ -42,8 +41,6 @@ __constant__ float kLevels[16] = {-2.7326f, -2.0690f, -1.6180f, -1.2562f, -0.942
                                   -0.3881f, -0.1284f, 0.1284f,  0.3881f,  0.6568f,  0.9423f,
                                   1.2562f,  1.6180f,  2.0690f,  2.7326f};
 constexpr double kDecision[7] = {0.2582, 0.5224, 0.7996, 1.0993, 1.4371, 1.8435, 2.4008};
-
-constexpr int kChunk = 256;     // keys per chunk = threads per decode workgroup
 
 __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
   return __shfl_xor(v, m, 64);
@@ -191,17 +188,52 @@ __device__ __forceinline__ void fwht_f32(float& y0, float& y1, int lane, int hal
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kChunk) void q4_decode_kernel(Q4DecodeParams p) {
+// ---- MFMA decode ------------------------------------------------------------
+// One workgroup per (query, kv head) with W waves taking the 32-key steps in
+// turn, as the bf16 direct decode does, but the MFMA operands come from the
+// codes: a 256-entry LDS table turns each code byte into its two fp16
+// levels, so 8 dims of a key are four table reads.  In the rotated space a
+// key's score is (scale / D) * n_k * sum_d qh_d level_d, qh = H (s * q): the
+// MFMA contracts qh (fp16) with the levels and the key norm scales the
+// result; the V norm scales the probability before P.V.  The waves' softmax
+// states meet in LDS, and the merged rows are rotated back once.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef short v4i16q __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16q* lds_v4i16q_ptr;
+
+constexpr int kQStep = 32;   // keys per step
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+template <int D, int W>
+union Q4Smem {
+  uint16_t v[W][kQStep][D + 8];   // each wave's V tile as fp16 levels, padded pitch
+  struct {
+    float o[W][16][D + 4];
+    float m[W][16];
+    float l[W][16];
+  } fin;
+};
+
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void q4_mfma_kernel(Q4DecodeParams p) {
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  constexpr int CPR = D / 8;                 // 8-dim chunks per key row
+  constexpr int VPER = kQStep * CPR / 64;    // V chunks per lane per step
   constexpr int HALF = D / 2;
-  constexpr int MAXG = kQ4MaxRowDims / D;
-  __shared__ __align__(16) float lut[kQ4MaxRowDims * 16];   // [d][code][g], MAXG rows
-  __shared__ __align__(16) float sc[kChunk][MAXG];   // [key][row]: scores, then probabilities
-  __shared__ __align__(16) uint8_t vcs[kChunk][HALF];   // V codes of the chunk
-  __shared__ float accs[4][kQ4MaxRowDims];         // per-wave partial V sums [g][d]
-  __shared__ float vn_s[kChunk];                   // V norms of the chunk
-  __shared__ float m_s[MAXG], l_s[MAXG], a_s[MAXG];
-  __shared__ float lv_s[16];
+  __shared__ uint32_t pair_lut[256];         // code byte -> (fp16 level lo, hi)
+  __shared__ __align__(16) float qrot[16][D];   // rotated query rows, then merged outputs
+  __shared__ __align__(16) Q4Smem<D, W> sm;
 
   const int G = p.G;
   const int item = static_cast<int>(blockIdx.x) / p.Hkv;
@@ -210,178 +242,174 @@ __global__ __launch_bounds__(kChunk) void q4_decode_kernel(Q4DecodeParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const bool on = lane < HALF;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
   const int64_t row0 = static_cast<int64_t>(it.q_index) * p.Hq + static_cast<int64_t>(h) * G;
-  if (tid < 16) lv_s[tid] = kLevels[tid];
-
-  // rotated query rows -> lookup tables (scale, log2 e and 1/D folded in)
-  const float tscale = p.scale_log2 / static_cast<float>(D);
-  for (int g = wave; g < G; g += 4) {
+  for (int i = tid; i < 256; i += 64 * W)
+    pair_lut[i] = static_cast<uint32_t>(f16_bits(kLevels[i & 15])) |
+                  (static_cast<uint32_t>(f16_bits(kLevels[i >> 4])) << 16);
+  for (int g = wave; g < 16; g += W) {
     float y0 = 0.f, y1 = 0.f;
-    if (on) {
+    if (g < G && lane < HALF) {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(p.q + (row0 + g) * D + 2 * lane);
       y0 = p.signs[2 * lane] * bf16_lo(w);
       y1 = p.signs[2 * lane + 1] * bf16_hi(w);
     }
     fwht_f32(y0, y1, lane, HALF);
-    if (on) {
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        lut[((2 * lane) * 16 + c) * MAXG + g] = y0 * kLevels[c] * tscale;
-        lut[((2 * lane + 1) * 16 + c) * MAXG + g] = y1 * kLevels[c] * tscale;
-      }
+    if (lane < HALF) {
+      qrot[g][2 * lane] = y0;
+      qrot[g][2 * lane + 1] = y1;
     }
   }
-  if (tid < MAXG) {
-    m_s[tid] = -INFINITY;
-    l_s[tid] = 0.f;
-  }
-  float acc0[MAXG], acc1[MAXG];
-#pragma unroll
-  for (int g = 0; g < MAXG; ++g) acc0[g] = acc1[g] = 0.f;
   __syncthreads();
+  // B operand: row l16, dims 32 kk + 8 g4 .. + 7
+  f16x8 qf[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[kk][e] = static_cast<_Float16>(qrot[l16][32 * kk + 8 * g4 + e]);
 
-  const int64_t head_vecs = static_cast<int64_t>(p.Hkv) * p.B;   // vectors per block and layer
+  const int64_t head_vecs = static_cast<int64_t>(p.Hkv) * p.B;
   const int64_t layer_vecs = head_vecs * p.N;
-  for (int c0 = 0; c0 < it.n_tok; c0 += kChunk) {
-    const int t = c0 + tid;
-    const int nt = min(kChunk, it.n_tok - c0);
-    if (t < it.n_tok) {
-      const int32_t blk = p.blocks[it.blk_off + (t >> p.log2B)];
-      const int64_t vec = p.layer * layer_vecs + blk * head_vecs + static_cast<int64_t>(h) * p.B +
-                          (t & (p.B - 1));
-      const uint4* kc = reinterpret_cast<const uint4*>(p.k_codes + vec * HALF);
-      const uint4* vc = reinterpret_cast<const uint4*>(p.v_codes + vec * HALF);
-      uint32_t kw[HALF / 4];
+  const uint32_t* kc32 = reinterpret_cast<const uint32_t*>(p.k_codes);
+  const uint32_t* vc32 = reinterpret_cast<const uint32_t*>(p.v_codes);
+  const int t_last = it.n_tok - 1;
+  auto vec_of = [&](int t) {
+    t = min(t, t_last);
+    const int32_t blk = p.blocks[it.blk_off + (t >> p.log2B)];
+    return p.layer * layer_vecs + blk * head_vecs + static_cast<int64_t>(h) * p.B + (t & (p.B - 1));
+  };
+  auto levels8 = [&](uint32_t word) {
+    const uint32_t a = pair_lut[word & 255u], b = pair_lut[(word >> 8) & 255u];
+    const uint32_t c = pair_lut[(word >> 16) & 255u], d = pair_lut[word >> 24];
+    const uint4 u = make_uint4(a, b, c, d);
+    return __builtin_bit_cast(f16x8, u);
+  };
+  const float zscale = p.scale_log2 / static_cast<float>(D);
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4v o[ND];
 #pragma unroll
-      for (int i = 0; i < HALF / 16; ++i) {
-        const uint4 a = kc[i];
-        kw[4 * i + 0] = a.x;
-        kw[4 * i + 1] = a.y;
-        kw[4 * i + 2] = a.z;
-        kw[4 * i + 3] = a.w;
-        reinterpret_cast<uint4*>(vcs[tid])[i] = vc[i];
-      }
-      const float kn = __half2float(__ushort_as_half(p.k_norms[vec]));
-      vn_s[tid] = __half2float(__ushort_as_half(p.v_norms[vec]));
-      // one accumulator per row; the MAXG row values of a (dim, code) entry
-      // are contiguous, so a key dim costs MAXG / 4 128-bit reads (rows past
-      // G hold no data and are never used)
-      float sg[MAXG];
+  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  uint16_t (*vs)[D + 8] = sm.v[wave];
+
+  const int nsteps = (it.n_tok + kQStep - 1) / kQStep;
+  for (int s = wave; s < nsteps; s += W) {
+    const int t0 = s * kQStep;
+    // K operands and the norms of this lane's two K keys
+    uint32_t kw[2][NK];
+    float kn_l[2], vn_l[2];
 #pragma unroll
-      for (int g = 0; g < MAXG; ++g) sg[g] = 0.f;
+    for (int tt = 0; tt < 2; ++tt) {
+      const int64_t vec = vec_of(t0 + 16 * tt + l16);
 #pragma unroll
-      for (int w = 0; w < HALF / 4; ++w) {
-        const uint32_t word = kw[w];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float4* e = reinterpret_cast<const float4*>(
-              lut + ((8 * w + j) * 16 + ((word >> (4 * j)) & 15u)) * MAXG);
-#pragma unroll
-          for (int g4 = 0; g4 < MAXG / 4; ++g4) {
-            const float4 v = e[g4];
-            sg[4 * g4 + 0] += v.x;
-            sg[4 * g4 + 1] += v.y;
-            sg[4 * g4 + 2] += v.z;
-            sg[4 * g4 + 3] += v.w;
-          }
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < MAXG; ++g) sc[tid][g] = sg[g] * kn;
+      for (int kk = 0; kk < NK; ++kk) kw[tt][kk] = kc32[vec * (D / 8) + 4 * kk + g4];
+      kn_l[tt] = __half2float(__ushort_as_half(p.k_norms[vec]));
+      vn_l[tt] = __half2float(__ushort_as_half(p.v_norms[vec]));
     }
-    __syncthreads();
-    // per row: chunk max, new running max, probabilities (times the V norm)
-    for (int g = wave; g < G; g += 4) {
-      float mx = -INFINITY;
-      for (int i = lane; i < nt; i += 64) mx = fmaxf(mx, sc[i][g]);
-      mx = wave_max(mx);
-      const float m_old = m_s[g];
-      const float m_new = fmaxf(m_old, mx);
-      const float alpha = m_old == -INFINITY ? 0.f : fast_exp2(m_old - m_new);
-      float ps = 0.f;
-      for (int i = lane; i < nt; i += 64) {
-        const float pr = fast_exp2(sc[i][g] - m_new);
-        ps += pr;
-        sc[i][g] = pr;
-      }
-      ps = wave_sum(ps);
-      if (lane == 0) {
-        m_s[g] = m_new;
-        l_s[g] = l_s[g] * alpha + ps;
-        a_s[g] = alpha;
-      }
+    uint32_t vw[VPER];
+#pragma unroll
+    for (int i = 0; i < VPER; ++i) {
+      const int ci = lane + 64 * i;
+      vw[i] = vc32[vec_of(t0 + ci / CPR) * (D / 8) + ci % CPR];
     }
-    __syncthreads();
-    // V: lanes over dims (two per lane), waves over keys of the chunk
+    // V tile as fp16 levels (this wave's earlier reads of it are done)
+    wave_sync_lds();
 #pragma unroll
-    for (int g = 0; g < MAXG; ++g) {
-      const float al = g < G ? a_s[g] : 0.f;
-      acc0[g] *= al;
-      acc1[g] *= al;
+    for (int i = 0; i < VPER; ++i) {
+      const int ci = lane + 64 * i;
+      *reinterpret_cast<f16x8*>(&vs[ci / CPR][(ci % CPR) * 8]) = levels8(vw[i]);
     }
-    if (on) {
-      // four keys per step, every load of the step issued before the sums;
-      // keys past the chunk's end re-read its last key with weight 0
-      for (int i0 = wave; i0 < nt; i0 += 16) {
-        float l0[4], l1[4];
-        int ic[4];
+    // S^T = K Q^T: lane (l16, g4) gets keys 16 tt + 4 g4 + i of row l16
+    f32x4v sacc[2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + 4 * u;
-          ic[u] = min(i, nt - 1);
-          const uint32_t byte = vcs[ic[u]][lane];
-          const float vn = i < nt ? vn_s[ic[u]] : 0.f;
-          l0[u] = lv_s[byte & 15u] * vn;
-          l1[u] = lv_s[byte >> 4] * vn;
-        }
+    for (int tt = 0; tt < 2; ++tt) {
+      sacc[tt] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float4* pr4 = reinterpret_cast<const float4*>(sc[ic[u]]);
+      for (int kk = 0; kk < NK; ++kk)
+        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(levels8(kw[tt][kk]), qf[kk], sacc[tt], 0, 0, 0);
+    }
+    float z[8], vnk[8];
 #pragma unroll
-          for (int g4 = 0; g4 < MAXG / 4; ++g4) {
-            const float4 pr = pr4[g4];
-            acc0[4 * g4 + 0] = fmaf(pr.x, l0[u], acc0[4 * g4 + 0]);
-            acc1[4 * g4 + 0] = fmaf(pr.x, l1[u], acc1[4 * g4 + 0]);
-            acc0[4 * g4 + 1] = fmaf(pr.y, l0[u], acc0[4 * g4 + 1]);
-            acc1[4 * g4 + 1] = fmaf(pr.y, l1[u], acc1[4 * g4 + 1]);
-            acc0[4 * g4 + 2] = fmaf(pr.z, l0[u], acc0[4 * g4 + 2]);
-            acc1[4 * g4 + 2] = fmaf(pr.z, l1[u], acc1[4 * g4 + 2]);
-            acc0[4 * g4 + 3] = fmaf(pr.w, l0[u], acc0[4 * g4 + 3]);
-            acc1[4 * g4 + 3] = fmaf(pr.w, l1[u], acc1[4 * g4 + 3]);
-          }
-        }
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int src = 4 * g4 + i;                 // the lane that loaded key 16 tt + 4 g4 + i
+        const float kn = __shfl(kn_l[tt], src, 64);
+        vnk[4 * tt + i] = __shfl(vn_l[tt], src, 64);
+        const int tok = t0 + 16 * tt + src;
+        z[4 * tt + i] = tok < it.n_tok ? sacc[tt][i] * kn * zscale : -INFINITY;
       }
+    float mx = z[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
+    mx = xor32_max(xor16_max(mx));
+    const float m_new = fmaxf(m_run, mx);          // finite: every step holds a key
+    const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+    m_run = m_new;
+    f16x8 pf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pr = fast_exp2(z[j] - m_new);
+      l_run += pr;
+      pf[j] = static_cast<_Float16>(pr * vnk[j]);
     }
-    __syncthreads();   // the next chunk overwrites sc and vcs
+    wave_sync_lds();
+    // O^T += V^T P^T, V^T read transposed from the wave's tile
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      const int r = 4 * g4 + (l16 >> 2);
+      const int c = 16 * dt + 4 * (l16 & 3);
+      const v4i16q lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16q_ptr)(&vs[r][c]));
+      const v4i16q hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16q_ptr)(&vs[16 + r][c]));
+      const v4i16q both[2] = {lo, hi};
+      const f16x8 a = __builtin_bit_cast(f16x8, both);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, o[dt], 0, 0, 0);
+    }
   }
-  // combine the waves' partial sums, rotate back, normalise
-  if (on) {
+
+  // ---- merge of the W wave states, rotation back --------------------------
+  const float l_w = xor32_sum(xor16_sum(l_run));
+  __syncthreads();   // every wave is done with its V tile (aliased below)
 #pragma unroll
-    for (int g = 0; g < MAXG; ++g) {
-      if (g < G) {
-        accs[wave][g * D + 2 * lane] = acc0[g];
-        accs[wave][g * D + 2 * lane + 1] = acc1[g];
-      }
-    }
+  for (int dt = 0; dt < ND; ++dt)
+    *reinterpret_cast<float4*>(&sm.fin.o[wave][l16][16 * dt + 4 * g4]) =
+        make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  if (g4 == 0) {
+    sm.fin.m[wave][l16] = m_run;
+    sm.fin.l[wave][l16] = l_w;
   }
   __syncthreads();
-  for (int g = wave; g < G; g += 4) {
-    float y0 = 0.f, y1 = 0.f;
-    if (on) {
+  for (int e = tid; e < G * D; e += 64 * W) {
+    const int row = e / D;
+    const int d = e - row * D;
+    float mx = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        y0 += accs[w][g * D + 2 * lane];
-        y1 += accs[w][g * D + 2 * lane + 1];
-      }
+    for (int w = 0; w < W; ++w) mx = fmaxf(mx, sm.fin.m[w][row]);
+    float l = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = sm.fin.m[w][row];
+      const float a = mw == -INFINITY ? 0.f : fast_exp2(mw - mx);
+      l = fmaf(a, sm.fin.l[w][row], l);
+      acc = fmaf(a, sm.fin.o[w][row][d], acc);
+    }
+    qrot[row][d] = acc / (static_cast<float>(D) * l);
+    if (d == 0 && p.lse) p.lse[row0 + row] = (mx + log2f(l)) * kLn2;
+  }
+  __syncthreads();
+  for (int g = wave; g < G; g += W) {
+    float y0 = 0.f, y1 = 0.f;
+    if (lane < HALF) {
+      y0 = qrot[g][2 * lane];
+      y1 = qrot[g][2 * lane + 1];
     }
     fwht_f32(y0, y1, lane, HALF);
-    const float inv = 1.f / (static_cast<float>(D) * l_s[g]);
-    if (on) {
-      float2 o = make_float2(p.signs[2 * lane] * y0 * inv, p.signs[2 * lane + 1] * y1 * inv);
-      *reinterpret_cast<float2*>(p.out + (row0 + g) * D + 2 * lane) = o;
-    }
-    if (lane == 0 && p.lse) p.lse[row0 + g] = (m_s[g] + log2f(l_s[g])) * kLn2;
+    if (lane < HALF)
+      *reinterpret_cast<float2*>(p.out + (row0 + g) * D + 2 * lane) =
+          make_float2(p.signs[2 * lane] * y0, p.signs[2 * lane + 1] * y1);
   }
 }
 
@@ -402,9 +430,9 @@ hipError_t launch_q4_decode(const Q4DecodeParams& p, int32_t n_items, int32_t he
   if (n_items == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(n_items) * p.Hkv));
   if (head_dim == 64)
-    hipExtLaunchKernelGGL(q4_decode_kernel<64>, grid, dim3(kChunk), 0, s, ev_start, ev_stop, 0, p);
+    hipExtLaunchKernelGGL((q4_mfma_kernel<64, 8>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p);
   else if (head_dim == 128)
-    hipExtLaunchKernelGGL(q4_decode_kernel<128>, grid, dim3(kChunk), 0, s, ev_start, ev_stop, 0, p);
+    hipExtLaunchKernelGGL((q4_mfma_kernel<128, 4>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

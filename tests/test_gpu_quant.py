@@ -6,12 +6,11 @@
   K and V.
 * Decode parity: attention from the codes within max |d| <= 4e-3 and mean
   |d| <= 5e-4 of the oracle's float64 attention over the dequantized
-  vectors, lse within 4e-3; head_dim 64 and 128, GQA groups 4 and 8, block
-  sizes 16 and 32, several 256-key chunks and ragged lengths.
+  vectors, lse within 4e-3; head_dim 64 and 128, GQA groups 3, 4, 8 and 16,
+  block sizes 16 and 32, keys from a few to several hundred, ragged lengths.
 * Calls a 4-bit pool does not support fail with PKV_ERR_UNSUPPORTED.
 """
 
-import math
 
 import numpy as np
 import pytest
@@ -103,6 +102,8 @@ CASES = [
     ("q4_d64_g8", Shape(32, 4, 64, 32, 2, 128), 256, 5, 70, 2),
     ("q4_d64_g4_b16", Shape(8, 2, 64, 16, 1, 256), 777, 3, 33, 2),
     ("q4_d128_short", Shape(16, 4, 128, 16, 1, 64), 5, 4, 3, 3),
+    ("q4_d64_g16", Shape(16, 1, 64, 16, 1, 128), 300, 2, 40, 2),
+    ("q4_d128_g3", Shape(12, 4, 128, 32, 1, 128), 610, 2, 17, 2),
 ]
 
 
@@ -172,7 +173,7 @@ def test_q4_pool_refuses_other_calls(dev):
         torch.cuda.synchronize()
     finally:
         gp.close()
-    # G x head_dim above 512 is refused at creation
+    # head_dim other than 64 / 128 is refused at creation
     with pytest.raises(pkv.PkvError) as e:
-        Q4Pool(Shape(16, 1, 64, 16, 1, 8), np.ones(64, np.int8))
+        Q4Pool(Shape(8, 2, 32, 16, 1, 8), np.ones(32, np.int8))
     assert e.value.code == pkv.PKV_ERR_UNSUPPORTED
