@@ -12,6 +12,8 @@
 """
 
 
+import math
+
 import numpy as np
 import pytest
 
@@ -177,3 +179,49 @@ def test_q4_pool_refuses_other_calls(dev):
     with pytest.raises(pkv.PkvError) as e:
         Q4Pool(Shape(8, 2, 32, 16, 1, 8), np.ones(32, np.int8))
     assert e.value.code == pkv.PKV_ERR_UNSUPPORTED
+
+
+def test_prefix_cache_over_a_q4_pool(dev):
+    """The radix cache is format-blind: a request that matches a cached
+    prompt on a 4-bit pool shares its coded blocks, and its decode equals the
+    oracle's attention over the codes of the whole prompt."""
+    import torch
+    import paged_kv_cache_204_amd as pkv
+    from gpu_harness import to_dev
+    from oracle import PoolModel
+    shape = Shape(32, 8, 128, 16, 1, 64)
+    wl = synth.Workload("q4_radix", 95, shape, [], 1.0 / math.sqrt(128))
+    signs = wl.rotation_signs()
+    gp = Q4Pool(shape, signs)
+    cache = pkv.radix_create(gp.pool)
+    rng = np.random.default_rng(3)
+    prompt = list(rng.integers(0, 1000, 100))
+    k, v = wl.append_data(1, 1, 100)
+    try:
+        a, m = pkv.radix_match(cache, prompt)
+        assert m == 0
+        pkv.kv_append(gp.pool, [a], 100, to_dev(k), to_dev(v), gp.stream)
+        pkv.radix_insert(cache, a, prompt)
+        pkv.radix_release(cache, a)
+        b, m = pkv.radix_match(cache, prompt[:90] + [1])
+        assert m == 80 and pkv.seq_block_table(gp.pool, b)[0] == pkv.seq_block_table(gp.pool, a)[0][:5]
+        # b's own tokens: the prompt's tokens 80..89 and a new one
+        k2 = np.concatenate([k[:, :, 80:90], wl.append_data(2, 1, 1)[0]], axis=2)
+        v2 = np.concatenate([v[:, :, 80:90], wl.append_data(2, 1, 1)[1]], axis=2)
+        pkv.kv_append(gp.pool, [b], 11, to_dev(k2), to_dev(v2), gp.stream)
+        q = wl.decode_query(3, 1)
+        out = torch.empty((1, 32, 128), device="cuda")
+        lse = torch.empty((1, 32), device="cuda")
+        pkv.paged_attn_decode(gp.pool, 0, [b], to_dev(q), wl.sm_scale, out, lse, gp.stream)
+        torch.cuda.synchronize()
+        om = PoolModel(16, 16, 1, 8, 128)
+        t = om.allocate()
+        om.append([t], 91, np.concatenate([k[:, :, :80], k2], axis=2), np.concatenate([v[:, :, :80], v2], axis=2))
+        eo, el = decode_q4(om, 0, [t], q, wl.sm_scale, signs)
+        d = np.abs(out.cpu().numpy().astype(np.float64) - eo)
+        assert d.max() <= TOL_MAX and d.mean() <= TOL_MEAN
+        assert np.abs(lse.cpu().numpy() - el).max() <= TOL_MAX
+        pkv.radix_release(cache, b)
+    finally:
+        pkv.radix_destroy(cache)
+        gp.close()
