@@ -384,6 +384,15 @@ pkv_status pkv_timing_enable(pkv_pool* pool, int32_t enable);
 pkv_status pkv_timing_read(pkv_pool* pool, double* total_ms, int64_t* calls,
                            int32_t reset);
 
+/* ---- measurement ------------------------------------------------------ */
+
+/* Enqueue one streaming read of `bytes` (a multiple of 16) of device memory
+ * at `src` (16-byte aligned) by `blocks` workgroups of 256 threads, 128-bit
+ * loads (sink: a device word the kernel writes only when the data fold to
+ * a fixed 32-bit value, so the loads cannot be optimised away).  Timed by the caller with events on `stream`: the
+ * HBM read ceiling the attention kernels are compared with. */
+pkv_status pkv_hbm_read_probe(const void* src, size_t bytes, void* sink, int32_t blocks, void* stream);
+
 /* Message of the calling thread's last error ("" if none). */
 const char* pkv_last_error(void);
 

@@ -25,6 +25,7 @@ __all__ = [
     "paged_attn_decode", "paged_attn_tree_verify", "paged_attn_prefill", "kv_tree_commit",
     "seq_block_table", "block_refcount", "free_list", "kv_last_append",
     "paged_attn_decode_plan_stats", "pkv_timing_enable", "pkv_timing_read", "pkv_last_error",
+    "pkv_hbm_read_probe",
     "seq_ids",
     "radix_create", "radix_destroy", "radix_match", "radix_insert", "radix_release",
     "radix_evict", "radix_stats", "radix_dump",
@@ -114,6 +115,7 @@ def load():
         "pkv_timing_enable": (_I32, [_P, _I32]),
         "pkv_timing_read": (_I32, [_P, ctypes.POINTER(ctypes.c_double), _PI64, _I32]),
         "pkv_last_error": (ctypes.c_char_p, []),
+        "pkv_hbm_read_probe": (_I32, [_P, ctypes.c_size_t, _P, _I32, _P]),
         "radix_create": (_I32, [_P, ctypes.POINTER(_P)]),
         "radix_destroy": (None, [_P]),
         "radix_match": (_I32, [_P, _PI32, _I32, _PI64, _PI32]),
@@ -374,6 +376,10 @@ def pkv_timing_read(pool, reset=True):
 
 def pkv_last_error() -> str:
     return load().pkv_last_error().decode()
+
+
+def pkv_hbm_read_probe(src, nbytes, sink, blocks, stream=None):
+    _check(load().pkv_hbm_read_probe(_addr(src), int(nbytes), _addr(sink), int(blocks), _stream(stream)))
 
 
 # ---- radix prefix cache ---------------------------------------------------

@@ -27,6 +27,7 @@ SOURCES = [
     "kernels/attn.hip",
     "kernels/merge.hip",
     "kernels/quant.hip",
+    "kernels/probe.hip",
 ]
 
 ARCH = "gfx950"

@@ -967,6 +967,14 @@ pkv_status paged_attn_decode_plan_stats(pkv_pool* p, const int64_t* seqs, int32_
   return PKV_OK;
 }
 
+pkv_status pkv_hbm_read_probe(const void* src, size_t bytes, void* sink, int32_t blocks, void* stream) {
+  if (!src || !sink || blocks < 1 || !aligned16(src) || (bytes & 15))
+    return fail(PKV_ERR_ARG, "pkv_hbm_read_probe: NULL buffer, unaligned range or no workgroups");
+  PKV_HIP(pkv::launch_read_probe(src, bytes, static_cast<uint32_t*>(sink), blocks,
+                                 static_cast<hipStream_t>(stream)));
+  return PKV_OK;
+}
+
 pkv_status pkv_timing_enable(pkv_pool* p, int32_t enable) {
   if (!p) return fail(PKV_ERR_ARG, "pkv_timing_enable: NULL pool");
   if (!p->device) return fail(PKV_ERR_ARG, "pkv_timing_enable: the pool has no device storage");

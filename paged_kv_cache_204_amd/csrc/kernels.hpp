@@ -89,6 +89,9 @@ struct Q4DecodeParams {
 };
 
 hipError_t launch_q4_append(const Q4AppendParams& p, hipStream_t s);
+
+// Streaming read of `bytes` (16-byte aligned) by `blocks` workgroups of 256.
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, hipStream_t s);
 // One workgroup per (item, kv head); head_dim 64 or 128, G <= 16.
 hipError_t launch_q4_decode(const Q4DecodeParams& p, int32_t n_items, int32_t head_dim, hipStream_t s,
                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
