@@ -40,7 +40,7 @@ constexpr int kThreads = 256;
 // block `blk` starts at chunk blk * (Hkv * B * D / 8) + off * D / 8.  The pool
 // creation keeps a layer under 2^32 chunks and a block under 2^24 chunks, so
 // the index is one 24-bit multiply-add in 32 bits.
-__device__ __forceinline__ const uint4* layer_head_base(const AttnParams& p, const uint16_t* pool,
+__host__ __device__ inline const uint4* layer_head_base(const AttnParams& p, const uint16_t* pool,
                                                         int h, int D) {
   const size_t blk_stride = static_cast<size_t>(p.Hkv) * p.B * D;
   return reinterpret_cast<const uint4*>(pool + static_cast<size_t>(p.layer) * p.N * blk_stride +
@@ -781,39 +781,75 @@ union DirectSmem {
   } fin;
 };
 
+//
+// The grid is (kv head, item), so a workgroup finds its item and head
+// without arithmetic on kernel arguments, and the first loads (the item's
+// block list, its WorkItem, the query rows) leave together at wave start:
+// the block-list loads are unconditional (indexes clamped into the list)
+// and come first in program order, the query row needs only the WorkItem.
+// Everything the prologue and the K/V addressing read from the arguments
+// sits in the first 14 dwords (hq; g and log2 of the block size packed in
+// one dword; the block pitch in 16-byte chunks; the layer's K/V bases),
+// which arrive preloaded in SGPRs, so no argument load stands in the chain.  Only the K/V loads
+// wait for the list, through LDS and one barrier.
 template <int D, int W, int DEPTH>
 __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restrict__ items,
                                                           const int32_t* __restrict__ blocks,
                                                           const uint16_t* __restrict__ q,
-                                                          int32_t stride, AttnParams p) {
+                                                          int32_t stride, int32_t hq,
+                                                          uint32_t g_log2B, uint32_t blk_chunks,
+                                                          const uint4* __restrict__ k_layer,
+                                                          const uint4* __restrict__ v_layer,
+                                                          AttnParams p) {
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
   constexpr int CPR = D / 8;
   constexpr int VPER = kStep * CPR / 64;   // V chunks per lane per step
+  constexpr int LPER = (kMaxItemBlocks + 64 * W - 1) / (64 * W);   // block-list entries per thread
   static_assert(VPER * 64 == kStep * CPR, "a step's V splits evenly over a wave");
   __shared__ DirectSmem<D, W> sm;
   __shared__ int32_t blk_s[kMaxItemBlocks];
 
-  const int item = static_cast<int>(blockIdx.x) / p.Hkv;
-  const int h = static_cast<int>(blockIdx.x) - item * p.Hkv;
-  const int32_t* lst = blocks + static_cast<size_t>(item) * stride;
-  for (int i = threadIdx.x; i < stride; i += 64 * W) blk_s[i] = lst[i];
-  const WorkItem it = items[item];
+  const int h = static_cast<int>(blockIdx.x);
+  const int item = static_cast<int>(blockIdx.y);
+  const int g = static_cast<int>(g_log2B & 0xFFu);
+  const int log2B = static_cast<int>(g_log2B >> 8);
   const int tid = threadIdx.x;
+  const int32_t* lst = blocks + static_cast<size_t>(item) * stride;
+  int32_t blk_r[LPER];
+#pragma unroll
+  for (int k = 0; k < LPER; ++k) blk_r[k] = lst[min(tid + 64 * W * k, stride - 1)];
+  // keep the list loads ahead of the WorkItem's (whose wait they need not share)
+  __builtin_amdgcn_sched_barrier(0);
+  const int n_tok = items[item].n_tok;
+  const int q_index = items[item].q_index[0];
+  const int bmask = (1 << log2B) - 1;
+  const uint4* kb = k_layer + ((static_cast<size_t>(h) * (D / 8)) << log2B);
+  const uint4* vb = v_layer + ((static_cast<size_t>(h) * (D / 8)) << log2B);
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
-  const size_t row0 = static_cast<size_t>(it.q_index[0]) * p.Hq + static_cast<size_t>(h) * p.G;
+  const size_t row0 = static_cast<size_t>(q_index) * hq + static_cast<size_t>(h) * g;
 
   bf16x8 qf[1][NK];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) qf[0][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  if (l16 < p.G) {
-    const uint16_t* qrow = q + (row0 + l16) * D;
+  {
+    // rows past the group re-read row 0 of it and are zeroed after the load
+    const uint16_t* qrow = q + (row0 + (l16 < g ? l16 : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) qf[0][kk] = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * g4);
   }
+  // entries past the list repeat its last id and are never read
+#pragma unroll
+  for (int k = 0; k < LPER; ++k)
+    if (64 * W * (k + 1) <= kMaxItemBlocks || tid + 64 * W * k < kMaxItemBlocks) blk_s[tid + 64 * W * k] = blk_r[k];
+  if (l16 >= g) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qf[0][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  WorkItem it{};
+  it.n_tok = n_tok;
+  it.tail_start = INT_MAX;
   const uint64_t anc[1] = {0};
   float m_run[1] = {-INFINITY}, l_run[1] = {0.f};
   f32x4 o[1][ND];
@@ -825,13 +861,10 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
   // (tt, kk); V chunk ci = lane + 64 i is (token ci / CPR, chunk ci % CPR).
   // Tokens past the end re-read the last token (masked in the softmax).
   uint16_t (*vs)[D + 8] = sm.v[wave];
-  const uint4* kb = layer_head_base(p, p.k_pool, h, D);
-  const uint4* vb = layer_head_base(p, p.v_pool, h, D);
-  const uint32_t blk_chunks = static_cast<uint32_t>(p.Hkv * p.B * D / 8);
   const int t_last = it.n_tok - 1;
   auto ldg = [&](const uint4* src, int t, int c) {
     t = min(t, t_last);
-    return src[chunk_index(blk_s[t >> p.log2B], blk_chunks, (t & (p.B - 1)) * CPR + c)];
+    return src[chunk_index(blk_s[t >> log2B], blk_chunks, (t & bmask) * CPR + c)];
   };
   bf16x8 rk[DEPTH][2][NK];
   uint4 rv[DEPTH][VPER];
@@ -970,13 +1003,20 @@ hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim,
   if (stride < 1 || stride > kMaxItemBlocks || p.G > 16) return hipErrorInvalidValue;
   const int64_t n_wg = static_cast<int64_t>(n_items) * p.Hkv;
   if (n_wg > INT32_MAX) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<uint32_t>(n_wg));
+  if (n_items > 65535) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(p.Hkv), static_cast<uint32_t>(n_items));
+  const uint4* kl = layer_head_base(p, p.k_pool, 0, head_dim);
+  const uint4* vl = layer_head_base(p, p.v_pool, 0, head_dim);
+  const uint32_t blk_chunks = static_cast<uint32_t>(p.Hkv * p.B * head_dim / 8);
+  const uint32_t g_log2B = static_cast<uint32_t>(p.G) | (static_cast<uint32_t>(p.log2B) << 8);
   // eight waves at head_dim 64; at 128 a wave's loads in flight need more
   // registers than eight waves per workgroup leave, so four
   if (head_dim == 64)
-    hipExtLaunchKernelGGL((direct_kernel<64, 8, 2>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.q, stride, p);
+    hipExtLaunchKernelGGL((direct_kernel<64, 8, 2>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.q,
+                          stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
   else if (head_dim == 128)
-    hipExtLaunchKernelGGL((direct_kernel<128, 4, 2>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.q, stride, p);
+    hipExtLaunchKernelGGL((direct_kernel<128, 4, 2>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.q,
+                          stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
