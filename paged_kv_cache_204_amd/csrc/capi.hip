@@ -301,9 +301,12 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
   if (plan.direct.empty())
     PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles,
                               plan.valu_max_rows * ap.G, plan.mfma_waves, stream, ev_a, ev_b));
-  else
+  else {
+    int32_t max_tok = 0;
+    for (const pkv::WorkItem& it : plan.direct) max_tok = std::max(max_tok, it.n_tok);
     PKV_HIP(pkv::launch_direct(ap, static_cast<int32_t>(plan.direct.size()), sh.head_dim,
-                                plan.stride_direct, stream, ev_a, ev_b));
+                                plan.stride_direct, max_tok, stream, ev_a, ev_b));
+  }
   if (timed) p->ev_pending.emplace_back(ev_a, ev_b);
   if (!plan.merges.empty()) {
     pkv::MergeParams mp{};

@@ -122,8 +122,10 @@ hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, i
 // Direct decode: one workgroup per (item, kv head), each item one query
 // over all of its keys (n_grp 1, tail_start INT_MAX), written straight to
 // out / lse; items[i]'s block list at blocks + i * stride (<= kMaxItemBlocks).
+// max_tok: the largest n_tok of the items (it picks the kernel's form).
 hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
-                         hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                         int32_t max_tok, hipStream_t s, hipEvent_t ev_start = nullptr,
+                         hipEvent_t ev_stop = nullptr);
 
 // Log-sum-exp merge of the partial states of several work items.
 struct MergeParams {

@@ -25,6 +25,8 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "../kernels.hpp"
 #include "common.hpp"
 
@@ -102,6 +104,21 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// s_waitcnt vmcnt(STEP * n) for 0 <= n <= MAXN (n a constant once unrolled;
+// a larger n waits for STEP * MAXN).
+template <int STEP, int MAXN>
+__device__ __forceinline__ void wait_vmcnt_steps(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<STEP * MAXN>();
+      return;
+    }
+    wait_vmcnt_steps<STEP, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
 }
 
 // A step's K or V tile in LDS: 32 token rows of D bf16 without padding.  The
@@ -772,16 +789,24 @@ __global__ __launch_bounds__(64 * W) void attn_kernel(const WorkItem* __restrict
 // its steps ahead and need only wave-level ordering.  At the end the waves'
 // softmax states (m, l, O) meet in LDS and are merged by log-sum-exp.
 template <int D, int W>
+struct DirectFin {
+  float o[W][16][D + 4];
+  float m[W][16];
+  float l[W][16];
+};
+template <int D, int W>
 union DirectSmem {
   uint16_t v[W][kStep][D + 8];   // each wave's V rows, padded pitch
-  struct {
-    float o[W][16][D + 4];
-    float m[W][16];
-    float l[W][16];
-  } fin;
+  DirectFin<D, W> fin;
+};
+// One-round form: every step of a wave has a V tile of its own (the
+// swizzled layout of the MFMA path, filled by LDS DMA).
+template <int D, int W, int S>
+union DirectSmemAll {
+  char vt[W][S][kStep * D * 2];
+  DirectFin<D, W> fin;
 };
 
-//
 // The grid is (kv head, item), so a workgroup finds its item and head
 // without arithmetic on kernel arguments, and the first loads (the item's
 // block list, its WorkItem, the query rows) leave together at wave start:
@@ -790,9 +815,14 @@ union DirectSmem {
 // Everything the prologue and the K/V addressing read from the arguments
 // sits in the first 14 dwords (hq; g and log2 of the block size packed in
 // one dword; the block pitch in 16-byte chunks; the layer's K/V bases),
-// which arrive preloaded in SGPRs, so no argument load stands in the chain.  Only the K/V loads
-// wait for the list, through LDS and one barrier.
-template <int D, int W, int DEPTH>
+// which arrive preloaded in SGPRs, so no argument load stands in the chain.
+// Only the K/V loads wait for the list, through LDS and one barrier.
+//
+// ALL (calls whose every wave has at most DEPTH steps): a wave issues the
+// loads of all of its steps at once -- K into registers, then V by LDS DMA
+// into DEPTH tiles of its own -- so the call waits for one memory round
+// trip, not one per DEPTH steps; V then costs no registers.
+template <int D, int W, int DEPTH, bool ALL>
 __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restrict__ items,
                                                           const int32_t* __restrict__ blocks,
                                                           const uint16_t* __restrict__ q,
@@ -807,7 +837,8 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
   constexpr int VPER = kStep * CPR / 64;   // V chunks per lane per step
   constexpr int LPER = (kMaxItemBlocks + 64 * W - 1) / (64 * W);   // block-list entries per thread
   static_assert(VPER * 64 == kStep * CPR, "a step's V splits evenly over a wave");
-  __shared__ DirectSmem<D, W> sm;
+  using Smem = std::conditional_t<ALL, DirectSmemAll<D, W, DEPTH>, DirectSmem<D, W>>;
+  __shared__ Smem sm;
   __shared__ int32_t blk_s[kMaxItemBlocks];
 
   const int h = static_cast<int>(blockIdx.x);
@@ -860,13 +891,64 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
   // K of token t0 + 16 tt + l16, chunk 4 kk + g4 is the lane's operand for
   // (tt, kk); V chunk ci = lane + 64 i is (token ci / CPR, chunk ci % CPR).
   // Tokens past the end re-read the last token (masked in the softmax).
-  uint16_t (*vs)[D + 8] = sm.v[wave];
   const int t_last = it.n_tok - 1;
-  auto ldg = [&](const uint4* src, int t, int c) {
+  auto chunk_at = [&](int t, int c) {
     t = min(t, t_last);
-    return src[chunk_index(blk_s[t >> log2B], blk_chunks, (t & bmask) * CPR + c)];
+    return chunk_index(blk_s[t >> log2B], blk_chunks, (t & bmask) * CPR + c);
   };
+  auto ldg = [&](const uint4* src, int t, int c) { return src[chunk_at(t, c)]; };
+  const int nsteps = (it.n_tok + kStep - 1) / kStep;
+  const int mine = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;   // steps of this wave
   bf16x8 rk[DEPTH][2][NK];
+  if constexpr (ALL) {
+    // K of the wave's steps j = 0 .. DEPTH-1 (step wave + j W), then their V:
+    // run u of step j's tile is lanes' chunk slots 64 u + lane, row q / CPR,
+    // chunk (q % CPR) ^ tile_swz(row).  Steps past the wave's own re-read
+    // the last token and are not computed.
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+          rk[j][tt][kk] = __builtin_bit_cast(bf16x8, ldg(kb, (wave + j * W) * kStep + 16 * tt + l16, 4 * kk + g4));
+    // (the sources are all looked up before the first copy: each copy is a
+    // memory barrier to the compiler, which would otherwise wait for one
+    // block-list read per copy)
+    uint32_t vci[DEPTH][VPER];
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j)
+#pragma unroll
+      for (int u = 0; u < VPER; ++u) {
+        const int q = 64 * u + lane;
+        const int r = q / CPR;
+        vci[j][u] = chunk_at((wave + j * W) * kStep + r, (q % CPR) ^ tile_swz<D>(r));
+      }
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j)
+#pragma unroll
+      for (int u = 0; u < VPER; ++u) lds_dma16(vb + vci[j][u], sm.vt[wave][j] + 1024 * u);
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      if (j >= mine) break;
+      // step j's V runs have landed: only later steps' runs may be in flight
+      wait_vmcnt_steps<VPER, DEPTH - 1>(DEPTH - 1 - j);
+      const char* vt = sm.vt[wave][j];
+      const auto kop = [&](int tt, int kk) { return rk[j][tt][kk]; };
+      const auto vop = [&](int dt) {
+        const int r = 4 * g4 + (l16 >> 2);
+        const int c = 2 * dt + ((l16 & 3) >> 1);
+        const int off = (l16 & 1) * 8;
+        const v4i16 lo = lds_read_tr16(vt + tile_byte<D>(r, c) + off);
+        const v4i16 hi = lds_read_tr16(vt + tile_byte<D>(16 + r, c) + off);
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      mfma_tile<D, 1>(kop, vop, [] {}, qf, anc, it, (wave + j * W) * kStep, p.scale_log2, m_run, l_run, o);
+    }
+    // every run has landed before the tiles are reused for the merge
+    wait_vmcnt<0>();
+  } else {
+  uint16_t (*vs)[D + 8] = sm.v[wave];
   uint4 rv[DEPTH][VPER];
   auto fetch = [&](int slot, int t0) {
 #pragma unroll
@@ -906,8 +988,6 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
     mfma_tile<D, 1>(kop, vop, after_qk, qf, anc, it, s * kStep, p.scale_log2, m_run, l_run, o);
   };
 
-  const int nsteps = (it.n_tok + kStep - 1) / kStep;
-  const int mine = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;   // steps of this wave
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) fetch(j, (wave + j * W) * kStep);
   // whole rounds in which every step fetches the one DEPTH ahead, then the
@@ -920,6 +1000,7 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
 #pragma unroll
   for (int j = 0; j < 2 * DEPTH - 1; ++j)
     if (j0 + j < mine) step(j % DEPTH, wave + (j0 + j) * W, j0 + j + DEPTH < mine);
+  }
 
   // ---- merge of the W wave states ------------------------------------------
   const float l_w = xor32_sum(xor16_sum(l_run[0]));
@@ -998,7 +1079,7 @@ hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, i
 
 
 hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
-                         hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                         int32_t max_tok, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (n_items == 0) return hipSuccess;
   if (stride < 1 || stride > kMaxItemBlocks || p.G > 16) return hipErrorInvalidValue;
   const int64_t n_wg = static_cast<int64_t>(n_items) * p.Hkv;
@@ -1010,13 +1091,18 @@ hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim,
   const uint32_t blk_chunks = static_cast<uint32_t>(p.Hkv * p.B * head_dim / 8);
   const uint32_t g_log2B = static_cast<uint32_t>(p.G) | (static_cast<uint32_t>(p.log2B) << 8);
   // eight waves at head_dim 64; at 128 a wave's loads in flight need more
-  // registers than eight waves per workgroup leave, so four
-  if (head_dim == 64)
-    hipExtLaunchKernelGGL((direct_kernel<64, 8, 2>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.q,
-                          stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
+  // registers than eight waves per workgroup leave, so four.  At 64, calls
+  // of at most 3 steps per wave (768 keys) load everything in one round.
+  constexpr int kAllSteps = 3;
+  if (head_dim == 64 && max_tok <= kAllSteps * 8 * kStep)
+    hipExtLaunchKernelGGL((direct_kernel<64, 8, kAllSteps, true>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p.items,
+                          p.blocks, p.q, stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
+  else if (head_dim == 64)
+    hipExtLaunchKernelGGL((direct_kernel<64, 8, 2, false>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p.items, p.blocks,
+                          p.q, stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
   else if (head_dim == 128)
-    hipExtLaunchKernelGGL((direct_kernel<128, 4, 2>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, p.items, p.blocks, p.q,
-                          stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
+    hipExtLaunchKernelGGL((direct_kernel<128, 4, 2, false>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, p.items,
+                          p.blocks, p.q, stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
