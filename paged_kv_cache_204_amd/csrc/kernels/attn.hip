@@ -800,9 +800,10 @@ union DirectSmem {
   DirectFin<D, W> fin;
 };
 // One-round form: every step of a wave has a V tile of its own (the
-// swizzled layout of the MFMA path, filled by LDS DMA).
+// swizzled layout of the MFMA path, filled by LDS DMA); the merge area is
+// separate, so a wave stores its state without waiting for the others.
 template <int D, int W, int S>
-union DirectSmemAll {
+struct DirectSmemAll {
   char vt[W][S][kStep * D * 2];
   DirectFin<D, W> fin;
 };
@@ -1004,7 +1005,7 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
 
   // ---- merge of the W wave states ------------------------------------------
   const float l_w = xor32_sum(xor16_sum(l_run[0]));
-  lds_barrier();   // every wave is done with its V region (aliased below)
+  if constexpr (!ALL) lds_barrier();   // every wave is done with its V region (aliased below)
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
     *reinterpret_cast<float4*>(&sm.fin.o[wave][l16][16 * dt + 4 * g4]) =
@@ -1014,30 +1015,24 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
     sm.fin.l[wave][l16] = l_w;
   }
   lds_barrier();
-  for (int e = tid; e < p.G * (D / 4); e += 64 * W) {
-    const int row = e / (D / 4);
-    const int c4 = e - row * (D / 4);
+  // one output element per lane (G * D <= 16 * D elements over 64 W lanes)
+  for (int e = tid; e < p.G * D; e += 64 * W) {
+    const int row = e / D;
+    const int c = e % D;
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < W; ++w) mx = fmaxf(mx, sm.fin.m[w][row]);
     // wave 0 holds token 0, so mx is finite and l > 0
-    float l = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f, acc = 0.f;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const float mw = sm.fin.m[w][row];
       const float a = mw == -INFINITY ? 0.f : fast_exp2(mw - mx);
-      const float4 ow = *reinterpret_cast<const float4*>(&sm.fin.o[w][row][4 * c4]);
       l = fmaf(a, sm.fin.l[w][row], l);
-      acc.x = fmaf(a, ow.x, acc.x);
-      acc.y = fmaf(a, ow.y, acc.y);
-      acc.z = fmaf(a, ow.z, acc.z);
-      acc.w = fmaf(a, ow.w, acc.w);
+      acc = fmaf(a, sm.fin.o[w][row][c], acc);
     }
-    const float inv = 1.f / l;
-    *reinterpret_cast<float4*>(p.out + (row0 + row) * D + 4 * c4) =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    if (c4 == 0 && p.lse) p.lse[row0 + row] = (mx + log2f(l)) * kLn2;
+    p.out[(row0 + row) * D + c] = acc / l;
+    if (c == 0 && p.lse) p.lse[row0 + row] = (mx + log2f(l)) * kLn2;
   }
 }
 
