@@ -224,13 +224,20 @@ def test_shape_edges(dev, shape, label, path, monkeypatch):
 
 # Direct decode at its edges: fewer 32-token steps than waves (1..9 keys),
 # ragged lengths within one call, lengths around the step size, G 1 / 3 / 16
-# at both head dims (eight- and four-wave kernels).
+# at both head dims (eight- and four-wave kernels).  At head_dim 64 calls of
+# at most 768 keys load every step of a wave in one round and longer ones
+# roll two steps ahead: the fifth case's calls hold 765 .. 769 keys (both
+# forms, 768 the last one-round call); the sixth has 16-token blocks (two
+# per step) and G 16, the seventh 64-token blocks (half a block per step).
 DIRECT_CASES = [
-    # shape, prefix, own keys of branch i = base + i * inc, branches
+    # shape, prefix, own keys of branch i = base + i * inc, branches[, decode steps]
     (Shape(8, 8, 64, 16, 1, 64), 1, 0, 1, 6),
     (Shape(24, 8, 64, 4, 1, 256), 31, 1, 16, 5),
     (Shape(16, 1, 128, 16, 1, 256), 64, 0, 31, 4),
     (Shape(32, 4, 128, 32, 1, 512), 200, 290, 9, 7),
+    (Shape(32, 4, 64, 32, 1, 256), 760, 4, 0, 3, 5),
+    (Shape(16, 1, 64, 16, 1, 256), 40, 0, 100, 6),
+    (Shape(32, 4, 64, 64, 1, 64), 100, 3, 50, 5),
 ]
 
 
@@ -252,8 +259,9 @@ def ragged_fork(name, cfg_id, shape, prefix, base, inc, n, decode_steps=3):
 @pytest.mark.parametrize("case", range(len(DIRECT_CASES)))
 def test_direct_decode_edges(dev, case, monkeypatch):
     set_path(monkeypatch, "direct")
-    shape, prefix, base, inc, n = DIRECT_CASES[case]
-    parity(ragged_fork(f"direct_{case}", 70 + case, shape, prefix, base, inc, n), label=f"direct_{case}")
+    shape, prefix, base, inc, n, *steps = DIRECT_CASES[case]
+    parity(ragged_fork(f"direct_{case}", 70 + case, shape, prefix, base, inc, n, *steps),
+           label=f"direct_{case}")
 
 
 # Planner settings (read from the environment when a pool is created) pick
