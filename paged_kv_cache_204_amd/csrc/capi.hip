@@ -328,7 +328,8 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15)
 // Planner knobs may be overridden from the environment for tuning sweeps:
 // PKV_MFMA_MIN_ROWS (0 turns the MFMA kernel off), PKV_MFMA_ROW_TILES (1|2),
 // PKV_MFMA_WAVES (4|8), PKV_UNSHARE_MAX_QUERIES, PKV_UNSHARE_MAX_TOKENS,
-// PKV_TARGET_WGS, PKV_TARGET_MFMA_WGS, PKV_MAX_CHUNK, PKV_MAX_PARTS, PKV_DIRECT_MAX_TOKENS
+// PKV_TARGET_WGS, PKV_TARGET_MFMA_WGS, PKV_MAX_CHUNK, PKV_MAX_PARTS, PKV_WIDE_PAIRS,
+// PKV_WIDE_MAX_PARTS, PKV_DIRECT_MAX_TOKENS
 // and PKV_DIRECT_MAX_WGS (either 0 turns direct decode plans off).
 void apply_env(pkv::PlanConfig* c) {
   auto get = [](const char* name, int32_t* v, int32_t lo, int32_t hi) {
@@ -346,6 +347,8 @@ void apply_env(pkv::PlanConfig* c) {
   get("PKV_TARGET_MFMA_WGS", &c->target_mfma_wgs, 1, 1 << 20);
   get("PKV_MAX_CHUNK", &c->max_chunk, 64, 1 << 20);
   get("PKV_MAX_PARTS", &c->max_parts, 0, 1 << 20);
+  get("PKV_WIDE_PAIRS", &c->wide_pairs, 0, 1 << 30);
+  get("PKV_WIDE_MAX_PARTS", &c->wide_max_parts, 0, 1 << 20);
   get("PKV_DIRECT_MAX_TOKENS", &c->direct_max_tokens, 0, 1 << 20);
   get("PKV_DIRECT_MAX_WGS", &c->direct_max_wgs, 0, 1 << 30);
 }

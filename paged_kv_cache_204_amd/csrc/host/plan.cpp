@@ -336,7 +336,11 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
                                cfg.target_mfma_wgs * 4 / plan->mfma_waves, cap);
   {
     std::vector<int32_t> parts(n_seqs);
-    limit_parts(cfg, unit, cap, cap_v, &chunk_m, &chunk_v, [&](int32_t cm, int32_t cv) {
+    PlanConfig lim = cfg;
+    if (cfg.max_parts > 0 && cfg.wide_max_parts > 0 &&
+        static_cast<int64_t>(n_seqs) * sh.num_kv_heads >= cfg.wide_pairs)
+      lim.max_parts = std::min(cfg.max_parts, cfg.wide_max_parts);
+    limit_parts(lim, unit, cap, cap_v, &chunk_m, &chunk_v, [&](int32_t cm, int32_t cv) {
       std::fill(parts.begin(), parts.end(), 0);
       int32_t most = 0;
       for (const Segment& sg : segs) {

@@ -51,6 +51,10 @@ struct PlanConfig {
   int32_t max_parts = kMergeInline;  // partial states per query at most where the chunk
                                      // caps allow (beyond the merge row's inline list the
                                      // merge walks the parts serially); 0 = no limit
+  int32_t wide_pairs = 1024;     // decode calls over at least this many (query, kv head)
+  int32_t wide_max_parts = 6;    // pairs take at most this many partial states per query
+                                 // (there is parallelism to spare: fewer, longer chunks
+                                 // and a cheaper merge); 0 turns this off
   int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)
 };
 

@@ -282,6 +282,29 @@ def test_long_shared_prefix_is_cut_into_few_parts(monkeypatch):
     assert st_["max_parts"] > 1
 
 
+def test_wide_decode_calls_take_fewer_parts(monkeypatch):
+    """A decode call over many (query, kv head) pairs (the MCTS leaves: 256
+    queries x 8 kv heads) has parallelism to spare: its chunks are lengthened
+    until no query has more than 6 partial states, not 12.  Narrow calls
+    (the Dendrite fork: 6 x 4 pairs) keep the 12.  What the call reads does
+    not change."""
+    off = first_decode_stats("c4_mcts", {"PKV_WIDE_MAX_PARTS": "0"}, monkeypatch)
+    monkeypatch.delenv("PKV_WIDE_MAX_PARTS")
+    wide = first_decode_stats("c4_mcts", {}, monkeypatch)
+    assert off["max_parts"] > 6 and 1 < wide["max_parts"] <= 6
+    assert wide["work_items"] < off["work_items"]
+    for k in ("unique_tokens", "unique_blocks", "logical_tokens", "merged_rows", "segments"):
+        assert wide[k] == off[k], k
+    # a threshold above the call's 2048 pairs turns it off
+    high = first_decode_stats("c4_mcts", {"PKV_WIDE_PAIRS": "2049"}, monkeypatch)
+    assert high["max_parts"] == off["max_parts"]
+    monkeypatch.delenv("PKV_WIDE_PAIRS")
+    narrow = first_decode_stats("c3_dendrite", {}, monkeypatch)
+    narrow_off = first_decode_stats("c3_dendrite", {"PKV_WIDE_MAX_PARTS": "0"}, monkeypatch)
+    assert narrow == narrow_off
+    assert narrow["max_parts"] > 6
+
+
 @pytest.mark.parametrize("env,direct", [
     ({}, True),
     ({"PKV_DIRECT_MAX_TOKENS": "512"}, False),   # queries hold 513 keys
