@@ -784,10 +784,13 @@ __global__ __launch_bounds__(64 * W) void attn_kernel(const WorkItem* __restrict
 // w the steps w, w + W, ...) and run mfma_tile on one 16-row tile that holds
 // the query's G <= 16 heads (rows G..15 are zero).  No wave reads another's
 // tile, so K goes from global memory straight into the lane's MFMA operand
-// registers and V is staged untransposed in an LDS region of the wave's own,
-// read back transposed with ds_read_b64_tr_b16; a wave's loads run DEPTH of
-// its steps ahead and need only wave-level ordering.  At the end the waves'
-// softmax states (m, l, O) meet in LDS and are merged by log-sum-exp.
+// registers and V sits in an LDS region of the wave's own, read back
+// transposed with ds_read_b64_tr_b16; only wave-level ordering is needed.
+// Two forms: the rolling one stages V through registers into a row buffer
+// and runs its loads DEPTH steps ahead; the one-round one (ALL, below)
+// issues every load of the wave at once.  At the end the waves' softmax
+// states (m, l, O) meet in LDS and are merged by log-sum-exp, one output
+// element per lane.
 template <int D, int W>
 struct DirectFin {
   float o[W][16][D + 4];
