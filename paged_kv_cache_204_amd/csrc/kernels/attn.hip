@@ -905,6 +905,8 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
   const int mine = wave < nsteps ? (nsteps - 1 - wave) / W + 1 : 0;   // steps of this wave
   bf16x8 rk[DEPTH][2][NK];
   if constexpr (ALL) {
+    // waves with the most steps set the workgroup's time: issue them first
+    if (mine * W > nsteps) __builtin_amdgcn_s_setprio(2);
     // K of the wave's steps j = 0 .. DEPTH-1 (step wave + j W), then their V:
     // run u of step j's tile is lanes' chunk slots 64 u + lane, row q / CPR,
     // chunk (q % CPR) ^ tile_swz(row).  Steps past the wave's own re-read
