@@ -25,6 +25,7 @@ SOURCES = [
     "kernels/append.hip",
     "kernels/commit.hip",
     "kernels/attn.hip",
+    "kernels/wide.hip",
     "kernels/merge.hip",
     "kernels/quant.hip",
     "kernels/probe.hip",

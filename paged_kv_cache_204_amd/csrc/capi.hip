@@ -298,7 +298,13 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
     if (s != PKV_OK) return s;
   }
   // the events ride on the kernel's own dispatch: they take its start and end
-  if (plan.direct.empty())
+  if (plan.direct.empty() && plan.valu.empty() && !p->cfg.mixed_kernel_only)
+  {
+    int32_t max_rows = 0;
+    for (const pkv::WorkItem& it : plan.mfma) max_rows = std::max(max_rows, it.n_grp * ap.G);
+    PKV_HIP(pkv::launch_wide(ap, n_items, sh.head_dim, plan.stride_mfma, max_rows, stream, ev_a, ev_b));
+  }
+  else if (plan.direct.empty())
     PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles,
                               plan.valu_max_rows * ap.G, plan.mfma_waves, stream, ev_a, ev_b));
   else {
@@ -330,7 +336,9 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15)
 // PKV_MFMA_WAVES (4|8), PKV_UNSHARE_MAX_QUERIES, PKV_UNSHARE_MAX_TOKENS,
 // PKV_TARGET_WGS, PKV_TARGET_MFMA_WGS, PKV_MAX_CHUNK, PKV_MAX_PARTS, PKV_WIDE_PAIRS,
 // PKV_WIDE_MAX_PARTS, PKV_DIRECT_MAX_TOKENS
-// and PKV_DIRECT_MAX_WGS (either 0 turns direct decode plans off).
+// and PKV_DIRECT_MAX_WGS (either 0 turns direct decode plans off), and
+// PKV_MIXED_KERNEL_ONLY (1: plans of dense tiles only also run on the mixed
+// MFMA / VALU kernel instead of the pipelined dense-tile kernel).
 void apply_env(pkv::PlanConfig* c) {
   auto get = [](const char* name, int32_t* v, int32_t lo, int32_t hi) {
     const char* e = std::getenv(name);
@@ -351,6 +359,7 @@ void apply_env(pkv::PlanConfig* c) {
   get("PKV_WIDE_MAX_PARTS", &c->wide_max_parts, 0, 1 << 20);
   get("PKV_DIRECT_MAX_TOKENS", &c->direct_max_tokens, 0, 1 << 20);
   get("PKV_DIRECT_MAX_WGS", &c->direct_max_wgs, 0, 1 << 30);
+  get("PKV_MIXED_KERNEL_ONLY", &c->mixed_kernel_only, 0, 1);
 }
 
 }  // namespace

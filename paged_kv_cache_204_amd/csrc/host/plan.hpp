@@ -56,6 +56,7 @@ struct PlanConfig {
                                  // (there is parallelism to spare: fewer, longer chunks
                                  // and a cheaper merge); 0 turns this off
   int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)
+  int32_t mixed_kernel_only = 0; // 1: dense-tile-only plans run on the mixed kernel too
 };
 
 // Rows of one MFMA work item for a row-tile setting (4 waves x 16 x tiles).

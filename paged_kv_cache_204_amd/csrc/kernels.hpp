@@ -119,6 +119,14 @@ hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, i
                        int32_t valu_rows, int32_t waves, hipStream_t s, hipEvent_t ev_start = nullptr,
                        hipEvent_t ev_stop = nullptr);
 
+// Dense tiles only (every item an MFMA item, up to 256 rows): one workgroup
+// of four waves per (item, kv head), software-pipelined steps; items[i]'s
+// block list at blocks + i * stride (<= kMaxItemBlocks); max_rows: the most
+// rows (row groups x G) of any item, 1..256.
+hipError_t launch_wide(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
+                       int32_t max_rows, hipStream_t s, hipEvent_t ev_start = nullptr,
+                       hipEvent_t ev_stop = nullptr);
+
 // Direct decode: one workgroup per (item, kv head), each item one query
 // over all of its keys (n_grp 1, tail_start INT_MAX), written straight to
 // out / lse; items[i]'s block list at blocks + i * stride (<= kMaxItemBlocks).
