@@ -357,7 +357,7 @@ typedef struct pkv_plan_stats {
   int64_t logical_tokens;  /* sum over queries of the keys each attends to */
   int32_t unique_blocks;   /* distinct physical blocks the call reads */
   int32_t segments;        /* shared-prefix segments (runs of blocks with one query set) */
-  int32_t work_items;      /* workgroups per kv head */
+  int32_t work_items;      /* workgroups per kv head (MFMA, VALU, direct and path items) */
   int32_t merged_rows;     /* query rows whose partial states are merged */
   int32_t direct;          /* 1: one workgroup per query and kv head (direct kernel) */
   int32_t max_parts;       /* most partial states merged into one query (0: no merge) */

@@ -21,11 +21,13 @@ SOURCES = [
     "host/pool.cpp",
     "host/plan.cpp",
     "host/radix.cpp",
+    "host/tree.cpp",
     "capi.hip",
     "kernels/append.hip",
     "kernels/commit.hip",
     "kernels/attn.hip",
     "kernels/wide.hip",
+    "kernels/path.hip",
     "kernels/merge.hip",
     "kernels/quant.hip",
     "kernels/probe.hip",

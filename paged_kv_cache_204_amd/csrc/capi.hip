@@ -49,7 +49,7 @@ size_t align16(size_t x) { return (x + 15) & ~size_t{15}; }
 
 // Offsets of the plan arrays inside one contiguous upload.
 struct PlanLayout {
-  size_t items = 0, groups = 0, blocks = 0, merges = 0, parts = 0, total = 0;
+  size_t items = 0, groups = 0, blocks = 0, merges = 0, parts = 0, paths = 0, steps = 0, total = 0;
 };
 
 PlanLayout layout_of(const pkv::Plan& p) {
@@ -64,6 +64,8 @@ PlanLayout layout_of(const pkv::Plan& p) {
   put(o.blocks, p.item_blocks.size() * sizeof(int32_t));
   put(o.merges, p.merges.size() * sizeof(pkv::MergeRow));
   put(o.parts, p.parts.size() * sizeof(int32_t));
+  put(o.paths, p.paths.size() * sizeof(pkv::PathItem));
+  put(o.steps, p.steps.size() * sizeof(pkv::PathStep));
   o.total = at;
   return o;
 }
@@ -81,6 +83,8 @@ void serialize(const pkv::Plan& p, const PlanLayout& o, char* dst) {
   cp(o.blocks, p.item_blocks.data(), p.item_blocks.size() * sizeof(int32_t));
   cp(o.merges, p.merges.data(), p.merges.size() * sizeof(pkv::MergeRow));
   cp(o.parts, p.parts.data(), p.parts.size() * sizeof(int32_t));
+  cp(o.paths, p.paths.data(), p.paths.size() * sizeof(pkv::PathItem));
+  cp(o.steps, p.steps.data(), p.steps.size() * sizeof(pkv::PathStep));
 }
 
 // Makes the pool's device current for the duration of a call.
@@ -233,6 +237,35 @@ pkv_status take_event(pkv_pool* p, hipEvent_t* ev) {
 // per workgroup); the planner guarantees it, this re-checks before launch.
 bool plan_fits_kernels(const pkv::Plan& plan, const pkv::Shape& sh) {
   const int32_t G = sh.num_q_heads / sh.num_kv_heads;
+  if (plan.tree) {
+    // MFMA items of up to 256 rows writing partial states, path items of at
+    // most 16 rows whose steps name pool blocks, merge rows of inline parts
+    if (!plan.valu.empty() || !plan.direct.empty() || G > 16 || sh.block_size < 16) return false;
+    for (const pkv::WorkItem& it : plan.mfma)
+      if (it.n_tok < 1 || it.n_grp < 1 || it.n_grp * G > 256 || it.part_base < 0 ||
+          it.tail_start != INT_MAX)
+        return false;
+    for (const pkv::MergeRow& m : plan.merges)
+      if (m.n_parts < 1 || m.n_parts > pkv::kMergeInline) return false;
+    const int64_t n_steps = static_cast<int64_t>(plan.steps.size());
+    for (const pkv::PathItem& pi : plan.paths) {
+      if (pi.n_q < 1 || pi.n_q * G > 16 || pi.n_steps < 0 || pi.step_off < 0 ||
+          pi.step_off + static_cast<int64_t>(pi.n_steps) > n_steps)
+        return false;
+      for (int32_t j = 0; j < pi.n_q; ++j)
+        if (pi.merge[j] >= static_cast<int32_t>(plan.merges.size())) return false;
+    }
+    for (const pkv::PathStep& ps : plan.steps) {
+      const int32_t n = (ps.meta >> 8) & 0xFF, off = ps.meta & 0xFF;
+      // 16-token blocks: tokens 0..15 in blk_a, 16..31 in blk_b; larger
+      // blocks: the step's tokens are slots off .. off + n - 1 of one block
+      const bool in_block = sh.block_size == 16 ? off == 0 : (ps.blk_a == ps.blk_b && off + n <= sh.block_size);
+      if (ps.blk_a < 0 || ps.blk_a >= sh.num_blocks || ps.blk_b < 0 || ps.blk_b >= sh.num_blocks ||
+          n < 1 || n > 32 || !in_block)
+        return false;
+    }
+    return true;
+  }
   const int32_t mrows = pkv::mfma_item_rows(plan.mfma_row_tiles, plan.mfma_waves);
   if (plan.mfma_waves == 8 && !plan.valu.empty()) return false;
   for (const pkv::WorkItem& it : plan.valu)
@@ -297,7 +330,26 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
     if (s == PKV_OK) s = take_event(p, &ev_b);
     if (s != PKV_OK) return s;
   }
+  const hipEvent_t ev_first = ev_a;
   // the events ride on the kernel's own dispatch: they take its start and end
+  if (plan.tree) {
+    // the MFMA items write their partial states, the path items merge them
+    // and write out / lse: events on the first launch's start, the last's end
+    ap.steps = reinterpret_cast<const pkv::PathStep*>(base + lay.steps);
+    ap.merges = reinterpret_cast<const pkv::MergeRow*>(base + lay.merges);
+    const auto* paths = reinterpret_cast<const pkv::PathItem*>(base + lay.paths);
+    if (!plan.mfma.empty()) {
+      int32_t max_rows = 0;
+      for (const pkv::WorkItem& it : plan.mfma) max_rows = std::max(max_rows, it.n_grp * ap.G);
+      PKV_HIP(pkv::launch_wide(ap, static_cast<int32_t>(plan.mfma.size()), sh.head_dim, plan.stride_mfma,
+                               max_rows, stream, ev_a, nullptr));
+      ev_a = nullptr;
+    }
+    PKV_HIP(pkv::launch_path(ap, paths, static_cast<int32_t>(plan.paths.size()), sh.head_dim, stream, ev_a,
+                             ev_b));
+    if (timed) p->ev_pending.emplace_back(ev_first, ev_b);
+    return PKV_OK;
+  }
   if (plan.direct.empty() && plan.valu.empty() && !p->cfg.mixed_kernel_only)
   {
     int32_t max_rows = 0;
@@ -338,7 +390,10 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15)
 // PKV_WIDE_MAX_PARTS, PKV_DIRECT_MAX_TOKENS
 // and PKV_DIRECT_MAX_WGS (either 0 turns direct decode plans off), and
 // PKV_MIXED_KERNEL_ONLY (1: plans of dense tiles only also run on the mixed
-// MFMA / VALU kernel instead of the pipelined dense-tile kernel).
+// MFMA / VALU kernel instead of the pipelined dense-tile kernel), and the
+// tree decode planner's PKV_TREE_DECODE (0 turns it off), PKV_TREE_WIDE_ROWS,
+// PKV_TREE_WIDE_TOKENS, PKV_TREE_PATH_TOKENS, PKV_TREE_ITEM_ROWS,
+// PKV_TREE_TARGET_WGS and PKV_TREE_MAX_PARTS.
 void apply_env(pkv::PlanConfig* c) {
   auto get = [](const char* name, int32_t* v, int32_t lo, int32_t hi) {
     const char* e = std::getenv(name);
@@ -360,6 +415,13 @@ void apply_env(pkv::PlanConfig* c) {
   get("PKV_DIRECT_MAX_TOKENS", &c->direct_max_tokens, 0, 1 << 20);
   get("PKV_DIRECT_MAX_WGS", &c->direct_max_wgs, 0, 1 << 30);
   get("PKV_MIXED_KERNEL_ONLY", &c->mixed_kernel_only, 0, 1);
+  get("PKV_TREE_DECODE", &c->tree_decode, 0, 1);
+  get("PKV_TREE_WIDE_ROWS", &c->tree_wide_rows, 1, 1 << 20);
+  get("PKV_TREE_WIDE_TOKENS", &c->tree_wide_tokens, 1, 1 << 20);
+  get("PKV_TREE_PATH_TOKENS", &c->tree_path_tokens, 1, 1 << 20);
+  get("PKV_TREE_ITEM_ROWS", &c->tree_item_rows, 16, 256);
+  get("PKV_TREE_TARGET_WGS", &c->tree_target_wgs, 1, 1 << 20);
+  get("PKV_TREE_MAX_PARTS", &c->tree_max_parts, 1, pkv::kMergeInline);
 }
 
 }  // namespace
@@ -974,7 +1036,8 @@ pkv_status paged_attn_decode_plan_stats(pkv_pool* p, const int64_t* seqs, int32_
   out->logical_tokens = plan.logical_tokens;
   out->unique_blocks = plan.unique_blocks;
   out->segments = plan.segments;
-  out->work_items = static_cast<int32_t>(plan.valu.size() + plan.mfma.size() + plan.direct.size());
+  out->work_items = static_cast<int32_t>(plan.valu.size() + plan.mfma.size() + plan.direct.size() +
+                                         plan.paths.size());
   out->merged_rows = static_cast<int32_t>(plan.merges.size()) * p->core.shape().num_q_heads;
   out->direct = plan.direct.empty() ? 0 : 1;
   out->max_parts = 0;

@@ -125,6 +125,8 @@ void list_tails(Plan* plan) {
     }
 }
 
+}  // namespace
+
 // Copies every item's block list to a fixed-stride slot (MFMA items first,
 // as the kernel numbers them, then VALU, then direct items), padding with the
 // item's last block.
@@ -148,8 +150,6 @@ void pack_item_blocks(Plan* plan, int32_t block_size) {
   put(plan->valu, plan->stride_valu);
   put(plan->direct, plan->stride_direct);
 }
-
-}  // namespace
 
 bool ancestor_masks(const int32_t* parent, int32_t n_nodes, uint64_t* anc) {
   if (n_nodes < 1 || n_nodes > 64 || !parent || parent[0] != -1) return false;
@@ -304,6 +304,9 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
     return Err::ok;
   }
 
+  // ---- tree plan: shared segments through MFMA items, the rest by path items ----
+  if (plan_tree(pool, seqs, n_seqs, cfg, plan)) return Err::ok;
+
   // ---- work items ----
   // Segments read by many rows (a shared prefix under many queries) are a
   // dense contraction and go to the MFMA kernel in row subsets of
@@ -389,7 +392,7 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
 
 bool patch_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, const PlanConfig& cfg,
                   Plan* plan) {
-  if (plan->q_epoch.size() != static_cast<size_t>(n_seqs)) return false;
+  if (plan->tree || plan->q_epoch.size() != static_cast<size_t>(n_seqs)) return false;
   std::vector<int32_t> grow(n_seqs);
   std::vector<int32_t> last_block(n_seqs);
   for (int32_t q = 0; q < n_seqs; ++q) {

@@ -57,6 +57,15 @@ struct PlanConfig {
                                  // and a cheaper merge); 0 turns this off
   int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)
   int32_t mixed_kernel_only = 0; // 1: dense-tile-only plans run on the mixed kernel too
+  // tree decode plans (block size >= 16): shared segments with many rows go
+  // to MFMA items as partial states, everything else to path items
+  int32_t tree_decode = 1;       // 0 turns tree plans off
+  int32_t tree_wide_rows = 128;  // a segment read by at least this many rows ...
+  int32_t tree_wide_tokens = 256;// ... and this many keys is shared through MFMA items
+  int32_t tree_path_tokens = 1024; // longer segments always are
+  int32_t tree_item_rows = 128;  // rows per MFMA item of a tree plan (16 .. 256)
+  int32_t tree_target_wgs = 256; // MFMA workgroups to aim for over all kv heads
+  int32_t tree_max_parts = 8;    // partial states per query at most (<= kMergeInline)
 };
 
 // Rows of one MFMA work item for a row-tile setting (4 waves x 16 x tiles).
@@ -71,6 +80,11 @@ struct Plan {
   std::vector<MergeRow> merges;
   std::vector<int32_t> parts;
   std::vector<int32_t> item_blocks;   // per-item block lists, fixed strides
+  // tree decode plans: path items and their steps (MFMA items above write
+  // partial states that the path items merge; no merge launch)
+  bool tree = false;
+  std::vector<PathItem> paths;
+  std::vector<PathStep> steps;
   int32_t stride_mfma = 0, stride_valu = 0, stride_direct = 0;
   int64_t partial_rows = 0;
   int32_t mfma_row_tiles = 1;   // row tiles per wave the MFMA items were cut for
@@ -108,11 +122,18 @@ struct Plan {
     q_epoch.clear();
     q_len.clear();
     tail_items.clear();
+    tree = false;
+    paths.clear();
+    steps.clear();
   }
 };
 
 Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
                 const PlanConfig& cfg, Plan* plan, std::string* why);
+
+// The planners' last pass: each item's block list (plan.blocks from its
+// blk_off) copied to a fixed stride per item kind in plan.item_blocks.
+void pack_item_blocks(Plan* plan, int32_t block_size);
 
 // Brings a decode plan for the same sequence list up to date without
 // replanning when no table changed since it was made (same epochs) and the
@@ -121,6 +142,14 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
 // that does not hold; the caller then plans afresh.
 bool patch_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, const PlanConfig& cfg,
                   Plan* plan);
+
+// Tree decode plan of the call (its sequences already checked: known and
+// non-empty).  False, with *plan untouched, when the call does not suit it
+// (block size below 16, more than 16 query heads per kv head, a query that
+// would need more partial states than tree_max_parts); the caller then
+// plans segments and merges instead.
+bool plan_tree(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, const PlanConfig& cfg,
+               Plan* plan);
 
 Err plan_verify(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
                 int32_t n_nodes, const int32_t* parent, const PlanConfig& cfg,

@@ -45,6 +45,10 @@ struct AttnParams {
   int32_t layer, N, Hq, Hkv, G, B, log2B;
   uint32_t g_magic;        // ceil(2^16 / G): r / G == (r * g_magic) >> 16 for r < 1024
   float scale_log2;        // sm_scale * log2(e)
+  // tree decode plans: the path items' steps and the merge rows of their
+  // queries' partial states
+  const PathStep* steps;
+  const MergeRow* merges;
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
@@ -126,6 +130,13 @@ hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, i
 hipError_t launch_wide(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
                        int32_t max_rows, hipStream_t s, hipEvent_t ev_start = nullptr,
                        hipEvent_t ev_stop = nullptr);
+
+// Path items of a tree decode plan: one workgroup of four waves per (path
+// item, kv head); the waves take the item's steps in turn, then merge their
+// states with the queries' partial states (p.merges, p.part_o / part_lse)
+// and write out / lse.  p.steps: the plan's step list.
+hipError_t launch_path(const AttnParams& p, const PathItem* items, int32_t n_items, int32_t head_dim,
+                       hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Direct decode: one workgroup per (item, kv head), each item one query
 // over all of its keys (n_grp 1, tail_start INT_MAX), written straight to

@@ -59,6 +59,30 @@ struct MergeRow {
   int32_t inl[kMergeInline];
 };
 
+// Narrow part of a tree decode plan: one path item per group of up to 16
+// rows (queries x G, whole queries) that covers every key of its queries
+// outside the shared segments given to MFMA items, step by step; each step
+// is 32 consecutive tokens of one segment, seen by the item's queries in
+// qmask.  The item merges its own softmax states with its queries' partial
+// states from the MFMA items and writes out / lse.
+constexpr int kPathMaxQ = 16;
+
+struct PathItem {
+  int32_t step_off;            // first step in the plan's step list
+  int32_t n_steps;
+  int32_t n_q;                 // queries of the item (q_index[0 .. n_q)), n_q * G <= 16
+  int32_t pad;
+  int32_t q_index[kPathMaxQ];
+  int32_t merge[kPathMaxQ];    // MergeRow listing query j's partial states, -1 when none
+};
+
+struct PathStep {
+  int32_t blk_a;               // block holding the step's tokens 0..15
+  int32_t blk_b;               // block holding tokens 16..31 (blk_a when block_size >= 32)
+  int32_t meta;                // bits 0..7: slot of token 0 in blk_a; bits 8..15: tokens (1..32)
+  uint32_t qmask;              // bit j: query j of the item sees these tokens
+};
+
 // Device block lists: MFMA item i (kernel order) reads
 // item_blocks[i * stride_mfma ...], VALU item j reads
 // item_blocks[n_mfma * stride_mfma + j * stride_valu ...]; entries past an
@@ -67,5 +91,7 @@ struct MergeRow {
 static_assert(sizeof(WorkItem) == 64, "WorkItem layout");
 static_assert(sizeof(RowGroup) == 32, "RowGroup layout");
 static_assert(sizeof(MergeRow) == 64, "MergeRow layout");
+static_assert(sizeof(PathItem) == 144, "PathItem layout");
+static_assert(sizeof(PathStep) == 16, "PathStep layout");
 
 }  // namespace pkv

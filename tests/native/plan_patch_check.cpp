@@ -42,6 +42,7 @@ int main() {
   std::map<int, int64_t> h;
   std::string why;
   PlanConfig cfg;
+  cfg.tree_decode = 0;   // tree plans are replanned, never patched: the segment planner here
   if (const char* e = std::getenv("PATCH_CHECK_DIRECT")) cfg.direct_max_tokens = std::atoi(e);
   Plan cached;
   std::vector<int64_t> cached_ids;

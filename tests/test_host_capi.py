@@ -235,8 +235,11 @@ def test_c2_plan_reads_the_shared_prompt_once(direct, monkeypatch):
         # 16 queries x 4 kv heads with 513 keys each: one item per query, no merge
         assert st_["work_items"] == 16 and st_["merged_rows"] == 0
     else:
-        # the shared prompt is its own item(s): every query's heads are merged
-        assert st_["work_items"] > 16 and st_["merged_rows"] == 16 * 32
+        # the shared prompt (16 queries x 8 heads = 128 rows over 256 keys) is
+        # read once through MFMA items whose partial states every query's
+        # heads merge; the own keys go to path items of two queries (16 rows)
+        assert st_["merged_rows"] == 16 * 32
+        assert st_["work_items"] >= 1 + 16 // 2
 
 
 def first_decode_stats(name, env, monkeypatch):
@@ -266,7 +269,9 @@ def test_long_shared_prefix_is_cut_into_few_parts(monkeypatch):
     """The Dendrite fork (4096 shared tokens under 6 branches): chunks picked
     for parallelism alone give every query 69 partial states; the planner
     lengthens them until no query has more than max_parts (the merge row's
-    inline list by default).  What the call reads does not change."""
+    inline list by default).  What the call reads does not change.  (The
+    segment planner: tree plans off.)"""
+    monkeypatch.setenv("PKV_TREE_DECODE", "0")
     unlimited = first_decode_stats("c3_dendrite", {"PKV_MAX_PARTS": "0"}, monkeypatch)
     assert unlimited["max_parts"] == 69
     for limit in (24, 12, 8, 6):
@@ -287,7 +292,8 @@ def test_wide_decode_calls_take_fewer_parts(monkeypatch):
     queries x 8 kv heads) has parallelism to spare: its chunks are lengthened
     until no query has more than 6 partial states, not 12.  Narrow calls
     (the Dendrite fork: 6 x 4 pairs) keep the 12.  What the call reads does
-    not change."""
+    not change.  (The segment planner: tree plans off.)"""
+    monkeypatch.setenv("PKV_TREE_DECODE", "0")
     off = first_decode_stats("c4_mcts", {"PKV_WIDE_MAX_PARTS": "0"}, monkeypatch)
     monkeypatch.delenv("PKV_WIDE_MAX_PARTS")
     wide = first_decode_stats("c4_mcts", {}, monkeypatch)
@@ -447,7 +453,9 @@ def test_timing_sampling_period_is_validated():
 def test_small_shared_runs_are_handed_down(monkeypatch):
     """A run shared by a few queries (too sparse for the MFMA path) is read by
     each query's own work item instead of being a segment of its own: fewer
-    segments and items, the same unique and logical token counts."""
+    segments and items, the same unique and logical token counts.  (The
+    segment planner: tree plans off.)"""
+    monkeypatch.setenv("PKV_TREE_DECODE", "0")
     wl = synth.named("c4_mcts")
 
     def stats(unshare):
@@ -476,3 +484,19 @@ def test_small_shared_runs_are_handed_down(monkeypatch):
     # the level-3 edges (4 leaves, 64 tokens) are handed to the leaves
     assert shared["segments"] - handed["segments"] == 64
     assert handed["work_items"] < shared["work_items"]
+
+
+def test_tree_plans_keep_their_part_limit(monkeypatch):
+    """Tree plans (the MCTS leaves, the Dendrite fork): a long shared run is
+    split into key chunks only until each query has at most
+    PKV_TREE_MAX_PARTS partial states; what the call reads does not change."""
+    for name in ("c4_mcts", "c3_dendrite"):
+        base = None
+        for limit in (8, 4, 2, 1):
+            st_ = first_decode_stats(name, {"PKV_TREE_MAX_PARTS": str(limit)}, monkeypatch)
+            assert 1 <= st_["max_parts"] <= limit, (name, limit)
+            assert st_["merged_rows"] > 0
+            if base is None:
+                base = st_
+            for k in ("unique_tokens", "unique_blocks", "logical_tokens", "segments"):
+                assert st_[k] == base[k], (name, k)

@@ -24,7 +24,8 @@ def driver(tmp_path_factory):
         pytest.skip("g++ not found")
     exe = str(tmp_path_factory.mktemp("patch") / "plan_patch_check")
     subprocess.run([gxx, "-O1", "-std=c++17", f"-I{CSRC}", os.path.join(HERE, "native", "plan_patch_check.cpp"),
-                    os.path.join(CSRC, "host", "plan.cpp"), os.path.join(CSRC, "host", "pool.cpp"),
+                    os.path.join(CSRC, "host", "plan.cpp"), os.path.join(CSRC, "host", "tree.cpp"),
+                    os.path.join(CSRC, "host", "pool.cpp"),
                     "-o", exe], check=True)
     return exe
 

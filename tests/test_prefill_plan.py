@@ -25,7 +25,8 @@ def driver(tmp_path_factory):
     exe = str(tmp_path_factory.mktemp("prefill") / "prefill_plan_check")
     subprocess.run([gxx, "-O1", "-std=c++17", f"-I{CSRC}",
                     os.path.join(HERE, "native", "prefill_plan_check.cpp"),
-                    os.path.join(CSRC, "host", "plan.cpp"), os.path.join(CSRC, "host", "pool.cpp"),
+                    os.path.join(CSRC, "host", "plan.cpp"), os.path.join(CSRC, "host", "tree.cpp"),
+                    os.path.join(CSRC, "host", "pool.cpp"),
                     "-o", exe], check=True)
     return exe
 
