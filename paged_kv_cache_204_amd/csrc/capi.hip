@@ -239,17 +239,17 @@ bool plan_fits_kernels(const pkv::Plan& plan, const pkv::Shape& sh) {
   const int32_t G = sh.num_q_heads / sh.num_kv_heads;
   if (plan.tree) {
     // MFMA items of up to 256 rows writing partial states, path items of at
-    // most 16 rows whose steps name pool blocks, merge rows of inline parts
+    // most 32 rows whose steps name pool blocks, merge rows of inline parts
     if (!plan.valu.empty() || !plan.direct.empty() || G > 16 || sh.block_size < 16) return false;
     for (const pkv::WorkItem& it : plan.mfma)
       if (it.n_tok < 1 || it.n_grp < 1 || it.n_grp * G > 256 || it.part_base < 0 ||
           it.tail_start != INT_MAX)
         return false;
     for (const pkv::MergeRow& m : plan.merges)
-      if (m.n_parts < 1 || m.n_parts > pkv::kMergeInline) return false;
+      if (m.n_parts < 1 || m.n_parts > pkv::kPathMaxParts) return false;
     const int64_t n_steps = static_cast<int64_t>(plan.steps.size());
     for (const pkv::PathItem& pi : plan.paths) {
-      if (pi.n_q < 1 || pi.n_q * G > 16 || pi.n_steps < 0 || pi.step_off < 0 ||
+      if (pi.n_q < 1 || pi.n_q > pkv::kPathMaxQ || pi.n_q * G > pkv::kPathMaxRows || pi.n_steps < 0 || pi.step_off < 0 ||
           pi.step_off + static_cast<int64_t>(pi.n_steps) > n_steps)
         return false;
       for (int32_t j = 0; j < pi.n_q; ++j)
@@ -330,14 +330,15 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
     if (s == PKV_OK) s = take_event(p, &ev_b);
     if (s != PKV_OK) return s;
   }
-  const hipEvent_t ev_first = ev_a;
   // the events ride on the kernel's own dispatch: they take its start and end
   if (plan.tree) {
-    // the MFMA items write their partial states, the path items merge them
-    // and write out / lse: events on the first launch's start, the last's end
+    // the MFMA items (if any) write their partial states, then the path
+    // items merge them and write out / lse: events on the first launch's
+    // start and the last one's end
     ap.steps = reinterpret_cast<const pkv::PathStep*>(base + lay.steps);
     ap.merges = reinterpret_cast<const pkv::MergeRow*>(base + lay.merges);
     const auto* paths = reinterpret_cast<const pkv::PathItem*>(base + lay.paths);
+    const hipEvent_t ev_first = ev_a;
     if (!plan.mfma.empty()) {
       int32_t max_rows = 0;
       for (const pkv::WorkItem& it : plan.mfma) max_rows = std::max(max_rows, it.n_grp * ap.G);
@@ -393,7 +394,7 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15)
 // MFMA / VALU kernel instead of the pipelined dense-tile kernel), and the
 // tree decode planner's PKV_TREE_DECODE (0 turns it off), PKV_TREE_WIDE_ROWS,
 // PKV_TREE_WIDE_TOKENS, PKV_TREE_PATH_TOKENS, PKV_TREE_ITEM_ROWS,
-// PKV_TREE_TARGET_WGS and PKV_TREE_MAX_PARTS.
+// PKV_TREE_TARGET_WGS, PKV_TREE_MAX_PARTS and PKV_TREE_MIN_WGS.
 void apply_env(pkv::PlanConfig* c) {
   auto get = [](const char* name, int32_t* v, int32_t lo, int32_t hi) {
     const char* e = std::getenv(name);
@@ -421,7 +422,8 @@ void apply_env(pkv::PlanConfig* c) {
   get("PKV_TREE_PATH_TOKENS", &c->tree_path_tokens, 1, 1 << 20);
   get("PKV_TREE_ITEM_ROWS", &c->tree_item_rows, 16, 256);
   get("PKV_TREE_TARGET_WGS", &c->tree_target_wgs, 1, 1 << 20);
-  get("PKV_TREE_MAX_PARTS", &c->tree_max_parts, 1, pkv::kMergeInline);
+  get("PKV_TREE_MAX_PARTS", &c->tree_max_parts, 1, pkv::kPathMaxParts);
+  get("PKV_TREE_MIN_WGS", &c->tree_min_wgs, 0, 1 << 20);
 }
 
 }  // namespace

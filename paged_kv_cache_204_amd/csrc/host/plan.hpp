@@ -57,15 +57,16 @@ struct PlanConfig {
                                  // and a cheaper merge); 0 turns this off
   int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)
   int32_t mixed_kernel_only = 0; // 1: dense-tile-only plans run on the mixed kernel too
-  // tree decode plans (block size >= 16): shared segments with many rows go
-  // to MFMA items as partial states, everything else to path items
+  // tree decode plans (block size >= 16): path items over the trie, very
+  // long shared segments through MFMA items as partial states
   int32_t tree_decode = 1;       // 0 turns tree plans off
-  int32_t tree_wide_rows = 128;  // a segment read by at least this many rows ...
+  int32_t tree_wide_rows = 1 << 20; // a segment read by at least this many rows ...
   int32_t tree_wide_tokens = 256;// ... and this many keys is shared through MFMA items
-  int32_t tree_path_tokens = 1024; // longer segments always are
+  int32_t tree_path_tokens = 4096; // longer segments always are
   int32_t tree_item_rows = 128;  // rows per MFMA item of a tree plan (16 .. 256)
   int32_t tree_target_wgs = 256; // MFMA workgroups to aim for over all kv heads
-  int32_t tree_max_parts = 8;    // partial states per query at most (<= kMergeInline)
+  int32_t tree_max_parts = 8;    // partial states per query at most (<= kPathMaxParts)
+  int32_t tree_min_wgs = 128;    // path workgroups (items x kv heads) a tree plan needs
 };
 
 // Rows of one MFMA work item for a row-tile setting (4 waves x 16 x tiles).
@@ -81,7 +82,8 @@ struct Plan {
   std::vector<int32_t> parts;
   std::vector<int32_t> item_blocks;   // per-item block lists, fixed strides
   // tree decode plans: path items and their steps (MFMA items above write
-  // partial states that the path items merge; no merge launch)
+  // partial states in a launch before the path items', which merge them;
+  // no merge launch)
   bool tree = false;
   std::vector<PathItem> paths;
   std::vector<PathStep> steps;

@@ -6,20 +6,21 @@
 // of shared prefixes, SGLang RadixAttention page, data-structure foundations
 // and the match / split operations; keyed on the blocks the pool already
 // shares, so no token comparison is needed).
-//  - A node read by many rows (queries x the G query heads of a kv head) over
-//    many keys -- a long shared prefix -- is a dense contraction: MFMA items of
-//    up to tree_item_rows rows x one key chunk each, writing partial softmax
-//    states.  Every node longer than tree_path_tokens goes there too, so that
-//    no path item walks a long run alone.
-//  - Everything else is covered by path items: the queries in trie order are
-//    cut into groups of whole queries of at most 16 rows; a group's item walks
-//    the other nodes on its queries' paths, root first, in 32-token steps, each
-//    step carrying the mask of the group's queries that see it.  Siblings are
-//    adjacent in trie order, so the narrow levels of a search tree are read
-//    once per group, and a leaf's own keys once.
-// The path item then merges its queries' partial states by log-sum-exp and
-// writes the output: the call is at most two launches and needs no merge
-// launch.
+//  - The queries in trie order are cut into groups of whole queries of at
+//    most 32 rows (queries x the G query heads of a kv head); a group's path
+//    item walks the nodes on its queries' paths, root first, in 32-token
+//    steps, each step carrying the mask of the group's queries that see it.
+//    Siblings are adjacent in trie order, so the narrow levels of a search
+//    tree are read once per group and a leaf's own keys once; a shared run
+//    is read by every group below it, at the same time, so for a run of a
+//    few thousand keys (a few MB over all kv heads) the repeats come from
+//    the L2 cache of the XCD running that kv head, not from HBM.  No partial
+//    states and no merge: each path item writes its rows of out / lse.
+//  - A run longer than tree_path_tokens, or read by at least tree_wide_rows
+//    rows over at least tree_wide_tokens keys, is instead a dense
+//    contraction: MFMA items of up to tree_item_rows rows x one key chunk
+//    each, writing partial softmax states in a launch before the path items,
+//    which merge them into their rows by log-sum-exp.
 #include <algorithm>
 #include <climits>
 #include <unordered_map>
@@ -49,7 +50,7 @@ bool plan_tree(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, const
   const int32_t B = sh.block_size;
   const int32_t G = sh.num_q_heads / sh.num_kv_heads;
   if (cfg.tree_decode <= 0 || B < 16 || G > 16 || n_seqs < 1) return false;
-  const int32_t max_parts = std::min(cfg.tree_max_parts, kMergeInline);
+  const int32_t max_parts = std::min(cfg.tree_max_parts, kPathMaxParts);
   if (max_parts < 1) return false;
   std::vector<const SeqState*> st(n_seqs);
   for (int32_t i = 0; i < n_seqs; ++i) {
@@ -212,7 +213,7 @@ bool plan_tree(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, const
   }
 
   // ---- path items: groups of whole queries in trie order ----
-  const int32_t qp = std::max(1, std::min(kPathMaxQ, 16 / G));
+  const int32_t qp = std::max(1, std::min(kPathMaxQ, kPathMaxRows / G));
   std::vector<int32_t> mark(nodes.size(), -1);   // node -> index in the item's node list
   std::vector<int32_t> item_nodes;
   std::vector<uint32_t> item_mask;
@@ -257,6 +258,9 @@ bool plan_tree(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs, const
     pi.n_steps = static_cast<int32_t>(plan.steps.size()) - pi.step_off;
     plan.paths.push_back(pi);
   }
+  // a batch too small to fill the chip this way goes to the segment planner
+  if (static_cast<int64_t>(plan.paths.size()) * sh.num_kv_heads < cfg.tree_min_wgs) return false;
+
   plan.segments = static_cast<int32_t>(nodes.size());
   pack_item_blocks(&plan, B);
   // what the call reads and the sequences it was made for stay the caller's

@@ -131,10 +131,11 @@ hipError_t launch_wide(const AttnParams& p, int32_t n_items, int32_t head_dim, i
                        int32_t max_rows, hipStream_t s, hipEvent_t ev_start = nullptr,
                        hipEvent_t ev_stop = nullptr);
 
-// Path items of a tree decode plan: one workgroup of four waves per (path
-// item, kv head); the waves take the item's steps in turn, then merge their
-// states with the queries' partial states (p.merges, p.part_o / part_lse)
-// and write out / lse.  p.steps: the plan's step list.
+// Path items of a tree decode plan: one workgroup of eight waves per (path
+// item, kv head); the waves take the item's steps (p.steps) in turn, then
+// combine their states with the queries' partial states from the MFMA items
+// (p.merges, p.part_o / part_lse, written by an earlier launch) and write
+// out / lse.
 hipError_t launch_path(const AttnParams& p, const PathItem* items, int32_t n_items, int32_t head_dim,
                        hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 

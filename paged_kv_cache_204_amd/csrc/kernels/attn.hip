@@ -320,13 +320,6 @@ __device__ __forceinline__ float dot8(const uint4& q, const uint4& k, float acc)
   return acc;
 }
 
-// Orders this wave's LDS writes before its later LDS reads (no other wave
-// takes part, so no workgroup barrier).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
 
 // Phase 3 for items of one row per wave (RM = 4): the waves split the
 // tokens, each lane accumulates all rows for its 8 dims, a butterfly over

@@ -1,21 +1,27 @@
-// Path items of a tree decode plan: the narrow part of a decode call over
-// prefix-sharing branches -- the levels of a search tree below its shared
-// root, each leaf's own keys (SGLang RadixAttention page, measured benchmark:
-// many branches over one parent; decode is bound by memory bandwidth,
-// KV-cache lifecycle section).
+// Path items of a tree decode plan: a decode call over prefix-sharing
+// branches -- a search tree's shared root, the levels below it, each leaf's
+// own keys (SGLang RadixAttention page, measured benchmark: many branches
+// over one parent; decode is bound by memory bandwidth, KV-cache lifecycle
+// section).
 //
-// One workgroup of four waves per (path item, kv head).  The item holds up to
-// 16 rows (its queries x the G query heads of the kv head) in one 16-row MFMA
-// tile and a list of 32-token steps, each from one shared segment and seen by
-// the queries in its mask.  Wave w takes steps w, w + 4, ...; each wave has
-// two K/V slots of its own in LDS, filled by global_load_lds_dwordx4 one step
-// ahead of the step it computes, so the waves never wait for each other until
-// the end.  Per step: S^T = K Q^T (v_mfma_f32_16x16x32_bf16; A = K rows from
-// LDS, B = the tile's Q in registers), the masked online softmax, and
-// O^T += V^T P^T (V^T from the transposing LDS read), with the row sums from
-// the same product against a tile of ones.  At the end the four waves' states
-// and the queries' partial states from the MFMA items over the shared
-// segments are merged by log-sum-exp and written as out / lse.
+// One workgroup of eight waves per (path item, kv head).  The item holds up
+// to 32 rows (its queries x the G query heads of the kv head) as two 16-row
+// MFMA tiles, and a list of 32-token steps, each from one segment of the
+// trie and seen by the queries in its mask.  Wave w takes steps w, w + 8,
+// ...; each wave has a K and a V tile of its own in LDS, filled by
+// global_load_lds_dwordx4: the next step's K as soon as this step's score
+// products have read the K tile, its V once the P V products have read the
+// V tile.  The waves never wait for each other until the end.  Per step and
+// tile: S^T = K Q^T (v_mfma_f32_16x16x32_bf16; A = K rows from LDS, shared
+// by both tiles, B = the tile's Q in registers), the masked online softmax,
+// and O^T += V^T P^T (V^T from the transposing LDS read), the row sums from
+// the same product against a tile of ones.  At the end the eight waves'
+// states and the queries' partial states from MFMA items (an earlier
+// launch) are combined by log-sum-exp and written as out / lse.
+//
+// The workgroups of one kv head read the head's shared segments at the same
+// time; with the kv heads' workgroups interleaved in launch order (eight kv
+// heads: each XCD runs one head) the repeats are served by that XCD's L2.
 #include <hip/hip_ext.h>
 #include <math.h>
 
@@ -26,37 +32,43 @@
 namespace pkv {
 namespace {
 
-constexpr int kPathWaves = 4;
-constexpr int kPathSlots = 2;        // K/V slots per wave
-constexpr float kPathLoShare = 16.f; // residual term while a weight exceeds sum / 16
+constexpr int kPathWaves = 8;
+constexpr int kPathThreads = 64 * kPathWaves;
+constexpr int kPathTiles = kPathMaxRows / 16;
+constexpr float kPathLoShare = 16.f;   // residual term while a weight exceeds sum / 16
 
 template <int D>
 struct PathFin {
-  float o[kPathWaves][16][D + 4];
-  float m[kPathWaves][16];
-  float l[kPathWaves][16];
-  float wgt[16][kPathWaves + kMergeInline];   // normalised weights of each row's states
-  int32_t prow[16][kMergeInline];             // partial rows (+ query head) of each row
-  int32_t np[16];
+  float o[kPathWaves][kPathMaxRows][D];   // each wave's unnormalised state (swizzled columns)
+  float m[kPathWaves][kPathMaxRows];
+  float l[kPathWaves][kPathMaxRows];
+  float wgt[kPathMaxRows][kPathWaves + kPathMaxParts];   // each row's state weights
 };
 template <int D>
 union PathSmem {
-  char slot[kPathWaves][kPathSlots][2][kStep * D * 2];   // [wave][slot][K, V]
+  char slot[kPathWaves][2][kStep * D * 2];   // [wave][K, V]: the wave's step
   PathFin<D> fin;
 };
 
+// column c (a multiple of 4) of row r in PathFin::o: 16-byte groups rotated
+// by the row, so a wave's stores of 16 rows spread over the banks
+__device__ __forceinline__ int fin_col(int r, int c) { return c ^ ((r & 7) << 2); }
+
 template <int D>
-__global__ __launch_bounds__(64 * kPathWaves) void path_kernel(const PathItem* __restrict__ items,
-                                                              const PathStep* __restrict__ steps,
-                                                              AttnParams p) {
+__global__ __launch_bounds__(kPathThreads) void path_kernel(const PathItem* __restrict__ items,
+                                                          const PathStep* __restrict__ steps,
+                                                          AttnParams p) {
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
   constexpr int CPR = D / 8;
   constexpr int RUNS = kStep * CPR / 64;   // 1 KB runs per K (or V) tile
+  constexpr int Q4 = D / 4;
+  constexpr int NT = kPathTiles;
   __shared__ PathSmem<D> sm;
 
-  const int h = static_cast<int>(blockIdx.x);
-  const int item = static_cast<int>(blockIdx.y);
+  // consecutive workgroups take the kv heads of one item
+  const int h = static_cast<int>(blockIdx.x) % p.Hkv;
+  const int item = static_cast<int>(blockIdx.x) / p.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -68,111 +80,164 @@ __global__ __launch_bounds__(64 * kPathWaves) void path_kernel(const PathItem* _
   const int step0 = it.step_off;
   const int R = it.n_q * G;
 
-  // the tile's row l16: query l16 / G, head l16 % G of this kv head
-  const int my_q = l16 / G;
-  const bool row_ok = l16 < R;
-  bf16x8 qf[NK];
-  {
-    const int qi = row_ok ? it.q_index[my_q] : it.q_index[0];
-    const uint16_t* qrow = p.q + (static_cast<size_t>(qi) * p.Hq + h * G + (row_ok ? l16 % G : 0)) * D;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * g4);
-    if (!row_ok) {
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) qf[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-
   const uint4* kb = layer_head_base(p, p.k_pool, h, D);
   const uint4* vb = layer_head_base(p, p.v_pool, h, D);
   const uint32_t blk_chunks = static_cast<uint32_t>(p.Hkv * p.B * D / 8);
   const int bmask = p.B - 1;
   const int mine = wave < n_steps ? (n_steps - 1 - wave) / kPathWaves + 1 : 0;   // this wave's steps
 
-  // step k of this wave (item step wave + 4 k) into slot k % 2: run u (K runs
-  // first, then V) fills chunk slot c = 64 (u % RUNS) + lane of its tile,
-  // row c / CPR, chunk (c % CPR) ^ tile_swz(row).  Tokens past the step's
-  // count re-read its last token (masked below), so every run stays in the
-  // pool.
-  auto issue = [&](int k) __attribute__((always_inline)) {
-    const PathStep ps = steps[step0 + wave + kPathWaves * k];
+  // K (V) of a step into the wave's K (V) tile: run u fills chunk slot
+  // c = 64 u + lane, row c / CPR, chunk (c % CPR) ^ tile_swz(row).  Tokens
+  // past the step's count re-read its last token (masked below), so every
+  // run stays in the pool.
+  auto issue = [&](const PathStep& ps, int kv) __attribute__((always_inline)) {
     const int off = ps.meta & 0xFF;
     const int last = ((ps.meta >> 8) & 0xFF) - 1;
-    char* dst = sm.slot[wave][k % kPathSlots][0];
+    char* dst = sm.slot[wave][kv];
+    const uint4* src = kv ? vb : kb;
 #pragma unroll
-    for (int u = 0; u < 2 * RUNS; ++u) {
-      const int c = (u % RUNS) * 64 + lane;
+    for (int u = 0; u < RUNS; ++u) {
+      const int c = u * 64 + lane;
       const int r = c / CPR;
       const int ch = (c % CPR) ^ tile_swz<D>(r);
       const int t = min(r, last);
       const int blk = t < 16 ? ps.blk_a : ps.blk_b;
-      const uint32_t ci = chunk_index(blk, blk_chunks, ((off + t) & bmask) * CPR + ch);
-      lds_dma16((u < RUNS ? kb : vb) + ci, dst + (u >= RUNS ? kStep * D * 2 : 0) + (u % RUNS) * 1024);
+      lds_dma16(src + chunk_index(blk, blk_chunks, ((off + t) & bmask) * CPR + ch), dst + u * 1024);
     }
   };
 
-  float m_run = -INFINITY;
-  f32x4 o[ND + 1];   // o[ND]: row sums (P V against a tile of ones)
-#pragma unroll
-  for (int dt = 0; dt <= ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bf16x8 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80};
+  // The wave's steps in a rotated order (the item's index picks the first):
+  // the workgroups of one kv head then read different keys of a shared run
+  // at any moment, and read-mostly steps from the L2 mix with steps from
+  // HBM.  Step descriptors are read one step ahead of their use; the first
+  // step's K and V are requested before the query rows.
+  const int rot = mine > 0 ? item % mine : 0;
+  auto step_at = [&](int k) __attribute__((always_inline)) {
+    const int kk = k + rot < mine ? k + rot : k + rot - mine;
+    return steps[step0 + wave + kPathWaves * kk];
+  };
+  PathStep cur{}, nxt{};
+  if (mine > 0) {
+    cur = step_at(0);
+    nxt = step_at(mine > 1 ? 1 : 0);
+    issue(cur, 0);
+    issue(cur, 1);
+  }
 
-  if (mine > 0) issue(0);
-  if (mine > 1) issue(1);
-  // the query operands were loaded first: the compiler's wait for them lands here
+  // tile j's row l16 is item row 16 j + l16: query (16 j + l16) / G, head
+  // (16 j + l16) % G of this kv head
+  int my_q[NT];
+  bool row_ok[NT];
+  bf16x8 qf[NT][NK];
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) asm volatile("" : "+v"(qf[kk]));
+  for (int j = 0; j < NT; ++j) {
+    const int r = 16 * j + l16;
+    row_ok[j] = r < R;
+    my_q[j] = row_ok[j] ? r / G : 0;
+    const int qi = it.q_index[my_q[j]];
+    const uint16_t* qrow = p.q + (static_cast<size_t>(qi) * p.Hq + h * G + (row_ok[j] ? r % G : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) qf[j][kk] = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * g4);
+    if (!row_ok[j]) {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) qf[j][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  // the compiler's wait for the query operands lands here
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) asm volatile("" : "+v"(qf[j][kk]));
+
+  float m_run[NT];
+  f32x4 o[NT][ND + 1];   // o[j][ND]: row sums (P V against a tile of ones)
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    m_run[j] = -INFINITY;
+#pragma unroll
+    for (int dt = 0; dt <= ND; ++dt) o[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const bf16x8 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80};
+  const char* kt = sm.slot[wave][0];
+  const char* vt = sm.slot[wave][1];
   for (int k = 0; k < mine; ++k) {
-    // step k's runs have landed once only step k + 1's (2 RUNS) may be in flight
-    if (k + 1 < mine)
-      wait_vmcnt<2 * RUNS>();
-    else
-      wait_vmcnt<0>();
-    const PathStep ps = steps[step0 + wave + kPathWaves * k];
-    const int n_tok = (ps.meta >> 8) & 0xFF;
-    const bool vis_row = row_ok && ((ps.qmask >> my_q) & 1u);
-    const char* kt = sm.slot[wave][k % kPathSlots][0];
-    const char* vt = kt + kStep * D * 2;
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // step k's K has landed (its V, issued last, may still be in flight;
+    // everything issued before it has landed too)
+    wait_vmcnt<RUNS>();
+    const int n_tok = (cur.meta >> 8) & 0xFF;
+    f32x4 sacc[NT][2];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      sacc[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + tile_byte<D>(16 * tt + l16, 4 * kk + g4));
-        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sacc[tt], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          sacc[j][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j][kk], sacc[j][tt], 0, 0, 0);
       }
-    // each lane holds keys 16 tt + 4 g4 + i of its row l16
-    float sv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tok = 16 * (e >> 2) + 4 * g4 + (e & 3);
-      sv[e] = (vis_row && tok < n_tok) ? sacc[e >> 2][e & 3] : -INFINITY;
+    // the K tile's reads are done: the next step's K goes into it now, while
+    // this step's softmax and P V run
+    if (k + 1 < mine) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads have returned
+      issue(nxt, 0);
     }
-    float m = sv[0];
+    // per tile: each lane holds keys 16 tt + 4 g4 + i of its row l16.  A
+    // row's reference max moves only when the row's max passes it by more
+    // than kSlack (to that max): P <= 2^kSlack, the O rescale is rare.
+    float pv[NT][8];
+    float mx[NT], m_new[NT];
+    bool grow = false;
 #pragma unroll
-    for (int e = 1; e < 8; ++e) m = fmaxf(m, sv[e]);
-    const float mx = xor32_max(xor16_max(m)) * p.scale_log2;
-    // the reference max moves only when the row's max passes it by more than
-    // kSlack (to that max): P <= 2^kSlack, the O rescale is rare
-    const float m_new = mx > m_run + kSlack ? mx : m_run;
-    if (__ballot(m_new != m_run)) {
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+    for (int j = 0; j < NT; ++j) {
+      const bool vis_row = row_ok[j] && ((cur.qmask >> my_q[j]) & 1u);
+      float sv[8];
 #pragma unroll
-      for (int dt = 0; dt <= ND; ++dt) o[dt] *= alpha;
-      m_run = m_new;
+      for (int e = 0; e < 8; ++e) {
+        const int tok = 16 * (e >> 2) + 4 * g4 + (e & 3);
+        sv[e] = (vis_row && tok < n_tok) ? sacc[j][e >> 2][e & 3] : -INFINITY;
+      }
+      float m = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) m = fmaxf(m, sv[e]);
+      mx[j] = xor32_max(xor16_max(m)) * p.scale_log2;
+      m_new[j] = mx[j] > m_run[j] + kSlack ? mx[j] : m_run[j];
+      grow = grow || m_new[j] != m_run[j];
+      const float m_use = (m_new[j] == -INFINITY) ? 0.f : m_new[j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[j][e] = fast_exp2(fmaf(sv[e], p.scale_log2, -m_use));
+      // the weights are taken here, before the rescale branch (the compiler
+      // would otherwise sink them past it, away from the score products)
+      asm volatile("" ::"v"(pv[j][0]), "v"(pv[j][1]), "v"(pv[j][2]), "v"(pv[j][3]), "v"(pv[j][4]),
+                   "v"(pv[j][5]), "v"(pv[j][6]), "v"(pv[j][7]));
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float pv[8];
-    uint32_t ph[4];
+    if (__ballot(grow)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(sv[e], p.scale_log2, -m_use));
+      for (int j = 0; j < NT; ++j) {
+        const float alpha = (m_run[j] == -INFINITY) ? 0.f : fast_exp2(m_run[j] - m_new[j]);
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) ph[e >> 1] = pack_bf16x2(pv[e], pv[e + 1]);
-    uint4 hv = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-    const bf16x8 pf = *reinterpret_cast<bf16x8*>(&hv);
-    // the row's largest weight of this step against its sum over the steps before
-    const float p_top = mx == -INFINITY ? 0.f : fast_exp2(mx - m_use);
-    const bool need_lo = __ballot(vis_row && p_top * kPathLoShare > o[ND][0]) != 0;
+        for (int dt = 0; dt <= ND; ++dt) o[j][dt] *= alpha;
+        m_run[j] = m_new[j];
+      }
+    }
+    bf16x8 pf[NT];
+    uint32_t ph[NT][4];
+    bool need_lo = false;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) ph[j][e >> 1] = pack_bf16x2(pv[j][e], pv[j][e + 1]);
+      uint4 hv = make_uint4(ph[j][0], ph[j][1], ph[j][2], ph[j][3]);
+      pf[j] = *reinterpret_cast<bf16x8*>(&hv);
+      // the row's largest weight of this step against its sum over the steps before
+      const float m_use = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
+      const float p_top = mx[j] == -INFINITY ? 0.f : fast_exp2(mx[j] - m_use);
+      need_lo = need_lo || (row_ok[j] && p_top * kPathLoShare > o[j][ND][0]);
+    }
     auto vop = [&](int dt) __attribute__((always_inline)) {
       const int r = 4 * g4 + (l16 >> 2);
       const int c = 2 * dt + ((l16 & 3) >> 1);
@@ -181,59 +246,79 @@ __global__ __launch_bounds__(64 * kPathWaves) void path_kernel(const PathItem* _
       const v4i16 vhi = lds_read_tr16(vt + tile_byte<D>(16 + r, c) + off);
       return bf16x8{vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
     };
+    // V has landed: only the next step's K (issued after the score
+    // products) may still be in flight
+    if (k + 1 < mine)
+      wait_vmcnt<RUNS>();
+    else
+      wait_vmcnt<0>();
 #pragma unroll
-    for (int dt = 0; dt <= ND; ++dt)
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dt < ND ? vop(dt) : ones, pf, o[dt], 0, 0, 0);
-    if (need_lo) {
-      uint32_t pl[4];
+    for (int dt = 0; dt <= ND; ++dt) {
+      const bf16x8 a = dt < ND ? vop(dt) : ones;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        pl[e >> 1] = pack_bf16x2(pv[e] - __uint_as_float(ph[e >> 1] << 16),
-                                 pv[e + 1] - __uint_as_float(ph[e >> 1] & 0xFFFF0000u));
-      uint4 lv = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-      const bf16x8 pfl = *reinterpret_cast<bf16x8*>(&lv);
-#pragma unroll
-      for (int dt = 0; dt <= ND; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dt < ND ? vop(dt) : ones, pfl, o[dt], 0, 0, 0);
+      for (int j = 0; j < NT; ++j) o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[j], o[j][dt], 0, 0, 0);
     }
-    // the slot's reads are done (their products consumed them): refill it
-    if (k + 2 < mine) issue(k + 2);
+    if (__ballot(need_lo)) {
+      bf16x8 pfl[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        uint32_t pl[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          pl[e >> 1] = pack_bf16x2(pv[j][e] - __uint_as_float(ph[j][e >> 1] << 16),
+                                   pv[j][e + 1] - __uint_as_float(ph[j][e >> 1] & 0xFFFF0000u));
+        uint4 lv = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+        pfl[j] = *reinterpret_cast<bf16x8*>(&lv);
+      }
+#pragma unroll
+      for (int dt = 0; dt <= ND; ++dt) {
+        const bf16x8 a = dt < ND ? vop(dt) : ones;
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          o[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pfl[j], o[j][dt], 0, 0, 0);
+      }
+    }
+    // likewise the V tile once the products have read it
+    if (k + 1 < mine) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      issue(nxt, 1);
+    }
+    cur = nxt;
+    nxt = step_at(k + 2 < mine ? k + 2 : 0);
   }
   wait_vmcnt<0>();
 
-  // ---- merge: the four waves' states, then the queries' partial states ----
+  // ---- the eight waves' states, then the queries' partial states ----
   lds_barrier();   // every wave is done with its slots (aliased below)
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
-    *reinterpret_cast<float4*>(&sm.fin.o[wave][l16][16 * dt + 4 * g4]) =
-        make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-  if (g4 == 0) {
-    sm.fin.m[wave][l16] = m_run;
-    sm.fin.l[wave][l16] = o[ND][0];
+  for (int j = 0; j < NT; ++j) {
+    const int r = 16 * j + l16;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+      *reinterpret_cast<float4*>(&sm.fin.o[wave][r][fin_col(r, 16 * dt + 4 * g4)]) =
+          make_float4(o[j][dt][0], o[j][dt][1], o[j][dt][2], o[j][dt][3]);
+    if (g4 == 0) {
+      sm.fin.m[wave][r] = m_run[j];
+      sm.fin.l[wave][r] = o[j][ND][0];
+    }
   }
   lds_barrier();
   // one thread per row: the common max and every state's normalised weight
-  // (the partial states' lse loads leave together)
   if (tid < R) {
     const int row = tid;
-    const int j = row / G;
-    const int hq = h * G + row % G;
-    const int mi = it.merge[j];
+    const int mi = it.merge[row / G];
     const int np = mi >= 0 ? p.merges[mi].n_parts : 0;
-    float lk[kMergeInline];
-    int32_t pr[kMergeInline];
+    float lk[kPathMaxParts];
 #pragma unroll
-    for (int k = 0; k < kMergeInline; ++k) {
-      pr[k] = k < np ? p.merges[mi].inl[k] + hq : 0;
-      lk[k] = k < np ? p.part_lse[pr[k]] : -INFINITY;
-    }
+    for (int k = 0; k < kPathMaxParts; ++k)
+      lk[k] = k < np ? p.part_lse[static_cast<size_t>(p.merges[mi].inl[k]) + h * G + row % G] : -INFINITY;
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kPathWaves; ++w)
       if (sm.fin.l[w][row] > 0.f) mx = fmaxf(mx, sm.fin.m[w][row]);
 #pragma unroll
-    for (int k = 0; k < kMergeInline; ++k) mx = fmaxf(mx, lk[k]);
-    float aw[kPathWaves], ak[kMergeInline];
+    for (int k = 0; k < kPathMaxParts; ++k) mx = fmaxf(mx, lk[k]);
+    float aw[kPathWaves], ak[kPathMaxParts];
     float l = 0.f;
 #pragma unroll
     for (int w = 0; w < kPathWaves; ++w) {
@@ -242,7 +327,7 @@ __global__ __launch_bounds__(64 * kPathWaves) void path_kernel(const PathItem* _
       l = fmaf(aw[w], lw, l);
     }
 #pragma unroll
-    for (int k = 0; k < kMergeInline; ++k) {
+    for (int k = 0; k < kPathMaxParts; ++k) {
       ak[k] = lk[k] == -INFINITY ? 0.f : fast_exp2(lk[k] - mx);
       l += ak[k];
     }
@@ -250,45 +335,35 @@ __global__ __launch_bounds__(64 * kPathWaves) void path_kernel(const PathItem* _
 #pragma unroll
     for (int w = 0; w < kPathWaves; ++w) sm.fin.wgt[row][w] = aw[w] * inv;
 #pragma unroll
-    for (int k = 0; k < kMergeInline; ++k) {
-      sm.fin.wgt[row][kPathWaves + k] = ak[k] * inv;
-      sm.fin.prow[row][k] = pr[k];
-    }
-    sm.fin.np[row] = np;
-    const size_t orow = static_cast<size_t>(it.q_index[j]) * p.Hq + hq;
+    for (int k = 0; k < kPathMaxParts; ++k) sm.fin.wgt[row][kPathWaves + k] = ak[k] * inv;
+    const size_t orow = static_cast<size_t>(it.q_index[row / G]) * p.Hq + h * G + row % G;
     if (p.lse) p.lse[orow] = (mx + log2f(l)) * kLn2;
   }
   lds_barrier();
-  // four consecutive dims of one row per thread and pass; the partial rows'
-  // loads of a pass leave together
-  constexpr int Q4 = D / 4;
-  for (int u = tid; u < R * Q4; u += 64 * kPathWaves) {
+  // four consecutive dims of one row per thread and unit
+  for (int u = tid; u < R * Q4; u += kPathThreads) {
     const int row = u / Q4;
     const int c = (u % Q4) * 4;
-    const int np = sm.fin.np[row];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < kPathWaves; ++w) {
       const float a = sm.fin.wgt[row][w];
-      const float4 x = *reinterpret_cast<const float4*>(&sm.fin.o[w][row][c]);
+      const float4 x = *reinterpret_cast<const float4*>(&sm.fin.o[w][row][fin_col(row, c)]);
       acc.x = fmaf(a, x.x, acc.x);
       acc.y = fmaf(a, x.y, acc.y);
       acc.z = fmaf(a, x.z, acc.z);
       acc.w = fmaf(a, x.w, acc.w);
     }
-    if (np > 0) {
-      float4 x[kMergeInline];
-#pragma unroll
-      for (int k = 0; k < kMergeInline; ++k)
-        x[k] = *reinterpret_cast<const float4*>(p.part_o + static_cast<size_t>(sm.fin.prow[row][k < np ? k : 0]) * D + c);
-#pragma unroll
-      for (int k = 0; k < kMergeInline; ++k) {
-        const float a = k < np ? sm.fin.wgt[row][kPathWaves + k] : 0.f;
-        acc.x = fmaf(a, x[k].x, acc.x);
-        acc.y = fmaf(a, x[k].y, acc.y);
-        acc.z = fmaf(a, x[k].z, acc.z);
-        acc.w = fmaf(a, x[k].w, acc.w);
-      }
+    const int mi = it.merge[row / G];
+    const int np = mi >= 0 ? p.merges[mi].n_parts : 0;
+    for (int k = 0; k < np; ++k) {
+      const float a = sm.fin.wgt[row][kPathWaves + k];
+      const float4 y = *reinterpret_cast<const float4*>(
+          p.part_o + (static_cast<size_t>(p.merges[mi].inl[k]) + h * G + row % G) * D + c);
+      acc.x = fmaf(a, y.x, acc.x);
+      acc.y = fmaf(a, y.y, acc.y);
+      acc.z = fmaf(a, y.z, acc.z);
+      acc.w = fmaf(a, y.w, acc.w);
     }
     const size_t orow = static_cast<size_t>(it.q_index[row / G]) * p.Hq + h * G + row % G;
     *reinterpret_cast<float4*>(p.out + orow * D + c) = acc;
@@ -300,13 +375,15 @@ __global__ __launch_bounds__(64 * kPathWaves) void path_kernel(const PathItem* _
 hipError_t launch_path(const AttnParams& p, const PathItem* items, int32_t n_items, int32_t head_dim,
                        hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (n_items == 0) return hipSuccess;
-  if (n_items > 65535 || p.G > 16 || p.B < 16) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<uint32_t>(p.Hkv), static_cast<uint32_t>(n_items));
+  if (p.G > 16 || p.B < 16) return hipErrorInvalidValue;
+  const int64_t n_wg = static_cast<int64_t>(n_items) * p.Hkv;
+  if (n_wg > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(n_wg));
   if (head_dim == 64)
-    hipExtLaunchKernelGGL((path_kernel<64>), grid, dim3(64 * kPathWaves), 0, s, ev_start, ev_stop, 0, items,
+    hipExtLaunchKernelGGL((path_kernel<64>), grid, dim3(kPathThreads), 0, s, ev_start, ev_stop, 0, items,
                           p.steps, p);
   else if (head_dim == 128)
-    hipExtLaunchKernelGGL((path_kernel<128>), grid, dim3(64 * kPathWaves), 0, s, ev_start, ev_stop, 0, items,
+    hipExtLaunchKernelGGL((path_kernel<128>), grid, dim3(kPathThreads), 0, s, ev_start, ev_stop, 0, items,
                           p.steps, p);
   else
     return hipErrorInvalidValue;

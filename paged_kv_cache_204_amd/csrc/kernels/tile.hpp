@@ -105,4 +105,12 @@ __device__ __forceinline__ int tile_swz(int r) { return D == 128 ? (r & 15) : ((
 template <int D>
 __device__ __forceinline__ int tile_byte(int r, int c) { return r * (2 * D) + ((c ^ tile_swz<D>(r)) << 4); }
 
+// Orders this wave's LDS writes before its later LDS reads (no other wave
+// takes part, so no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 }  // namespace pkv

@@ -59,18 +59,20 @@ struct MergeRow {
   int32_t inl[kMergeInline];
 };
 
-// Narrow part of a tree decode plan: one path item per group of up to 16
+// Narrow part of a tree decode plan: one path item per group of up to 32
 // rows (queries x G, whole queries) that covers every key of its queries
 // outside the shared segments given to MFMA items, step by step; each step
 // is 32 consecutive tokens of one segment, seen by the item's queries in
 // qmask.  The item merges its own softmax states with its queries' partial
-// states from the MFMA items and writes out / lse.
-constexpr int kPathMaxQ = 16;
+// states from the MFMA items (a launch before it) and writes out / lse.
+constexpr int kPathMaxQ = 32;
+constexpr int kPathMaxRows = 32;   // two 16-row tiles
+constexpr int kPathMaxParts = 8;   // partial states per query of a tree plan at most
 
 struct PathItem {
   int32_t step_off;            // first step in the plan's step list
   int32_t n_steps;
-  int32_t n_q;                 // queries of the item (q_index[0 .. n_q)), n_q * G <= 16
+  int32_t n_q;                 // queries of the item (q_index[0 .. n_q)), n_q * G <= kPathMaxRows
   int32_t pad;
   int32_t q_index[kPathMaxQ];
   int32_t merge[kPathMaxQ];    // MergeRow listing query j's partial states, -1 when none
@@ -91,7 +93,7 @@ struct PathStep {
 static_assert(sizeof(WorkItem) == 64, "WorkItem layout");
 static_assert(sizeof(RowGroup) == 32, "RowGroup layout");
 static_assert(sizeof(MergeRow) == 64, "MergeRow layout");
-static_assert(sizeof(PathItem) == 144, "PathItem layout");
+static_assert(sizeof(PathItem) == 272, "PathItem layout");
 static_assert(sizeof(PathStep) == 16, "PathStep layout");
 
 }  // namespace pkv

@@ -2,7 +2,7 @@
 // "alloc h", "fork a b", "append n h...", "free h", "decode h...") through the
 // host pool and plans every decode call.  Each tree plan is checked against
 // the tables themselves:
-//  - every query is in exactly one path item, at most 16 rows each;
+//  - every query is in exactly one path item, at most 32 rows each;
 //  - the keys of a query -- tokens of the MFMA items that list it, plus the
 //    tokens of the steps of its path item whose mask names it -- are exactly
 //    the (block, slot) pairs of its table for tokens 0 .. len-1, each once;
@@ -46,7 +46,7 @@ static std::string check(const BlockPool& pool, const std::vector<int64_t>& ids,
     }
   }
   for (const PathItem& pi : plan.paths) {
-    if (pi.n_q < 1 || pi.n_q * G > 16) return "a path item's rows";
+    if (pi.n_q < 1 || pi.n_q > kPathMaxQ || pi.n_q * G > kPathMaxRows) return "a path item's rows";
     for (int32_t j = 0; j < pi.n_q; ++j) {
       const int32_t q = pi.q_index[j];
       ++in_path[q];
@@ -54,7 +54,7 @@ static std::string check(const BlockPool& pool, const std::vector<int64_t>& ids,
       std::vector<int32_t> have;
       if (pi.merge[j] >= 0) {
         const MergeRow& m = plan.merges[pi.merge[j]];
-        if (m.q_index != q || m.n_parts > kMergeInline) return "merge row";
+        if (m.q_index != q || m.n_parts > kPathMaxParts) return "merge row";
         have.assign(m.inl, m.inl + m.n_parts);
       }
       std::sort(want.begin(), want.end());
@@ -66,7 +66,7 @@ static std::string check(const BlockPool& pool, const std::vector<int64_t>& ids,
       const int32_t off = ps.meta & 0xFF, n = (ps.meta >> 8) & 0xFF;
       if (n < 1 || n > 32) return "step token count";
       if (B == 16 ? off != 0 : (off + n > B || ps.blk_a != ps.blk_b)) return "step leaves its block";
-      if (ps.qmask >> pi.n_q) return "step mask names a query outside the item";
+      if (pi.n_q < 32 && (ps.qmask >> pi.n_q)) return "step mask names a query outside the item";
       for (int32_t j = 0; j < pi.n_q; ++j) {
         if (!((ps.qmask >> j) & 1u)) continue;
         for (int32_t t = 0; t < n; ++t)
@@ -98,10 +98,12 @@ int main() {
   std::string why;
   PlanConfig cfg;
   cfg.direct_max_tokens = 0;   // every call planned as segments or as a tree
+  cfg.tree_min_wgs = 0;        // small batches too
   if (const char* e = std::getenv("TREE_CHECK_WIDE_ROWS")) cfg.tree_wide_rows = std::atoi(e);
   if (const char* e = std::getenv("TREE_CHECK_WIDE_TOKENS")) cfg.tree_wide_tokens = std::atoi(e);
   if (const char* e = std::getenv("TREE_CHECK_PATH_TOKENS")) cfg.tree_path_tokens = std::atoi(e);
   if (const char* e = std::getenv("TREE_CHECK_MAX_PARTS")) cfg.tree_max_parts = std::atoi(e);
+  if (const char* e = std::getenv("TREE_CHECK_MIN_WGS")) cfg.tree_min_wgs = std::atoi(e);
   int trees = 0, others = 0;
   while (std::getline(std::cin, line)) {
     std::istringstream ls(line);

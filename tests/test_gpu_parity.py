@@ -178,6 +178,15 @@ PATHS = {
     # shared prefixes give queries more partial states than a merge row
     # carries inline, so the merge walks its part list
     "manyparts": {"PKV_DIRECT_MAX_TOKENS": "0", "PKV_MAX_PARTS": "0"},
+    # tree decode plans for batches of any size: path items over the trie
+    # (shared runs re-read by every item below them) ...
+    "tree": {"PKV_DIRECT_MAX_TOKENS": "0", "PKV_TREE_MIN_WGS": "0"},
+    # ... and with shared runs through MFMA items (partial states in a launch
+    # before the path items, which merge them)
+    "treewide": {"PKV_DIRECT_MAX_TOKENS": "0", "PKV_TREE_MIN_WGS": "0", "PKV_TREE_WIDE_ROWS": "16",
+                 "PKV_TREE_WIDE_TOKENS": "32", "PKV_TREE_PATH_TOKENS": "256"},
+    # the wide-run rule the MCTS tree met before: the root as MFMA items
+    "treeroot": {"PKV_TREE_WIDE_ROWS": "128", "PKV_TREE_WIDE_TOKENS": "256", "PKV_TREE_PATH_TOKENS": "1024"},
 }
 
 
@@ -186,7 +195,7 @@ def set_path(monkeypatch, path):
         monkeypatch.setenv(k, v)
 
 
-@pytest.mark.parametrize("path", ["auto", "split"])
+@pytest.mark.parametrize("path", ["auto", "split", "tree", "treewide"])
 @pytest.mark.parametrize("name", list(REDUCED))
 def test_reduced_workload_parity(dev, name, path, monkeypatch):
     set_path(monkeypatch, path)
@@ -320,7 +329,8 @@ def sample_ops(wl, every):
     ("c2_trellis", 23, "auto"), ("c2_trellis", 23, "split"),
     ("c3_dendrite", 9, "auto"), ("c3_dendrite", 31, "direct"), ("c3_dendrite", 31, "manyparts"),
     ("c3_dendrite_aligned", 31, "auto"),
-    ("c4_mcts", 1, "auto"), ("c4_mcts_folded", 1, "auto"), ("c5_verify", 1, "auto"),
+    ("c3_dendrite", 31, "tree"),
+    ("c4_mcts", 1, "auto"), ("c4_mcts", 1, "treeroot"), ("c4_mcts_folded", 1, "auto"), ("c5_verify", 1, "auto"),
     ("c2_trellis_prefill", 1, "auto"), ("c5_verify_commit", 1, "auto"),
 ])
 def test_full_workload_parity(dev, name, every, path, monkeypatch):

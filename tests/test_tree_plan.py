@@ -71,8 +71,10 @@ def test_tree_plans_cover_every_key_once(driver, name):
 
 @pytest.mark.parametrize("name", ["c4_mcts", "mcts_ragged", "c3_dendrite"])
 def test_tree_plans_under_other_cut_rules(driver, name):
-    # everything shared through MFMA items / nothing but long runs / one part
+    # everything shared through MFMA items / nothing but long runs / two parts
+    # / long runs under many rows
     for env in ({"wide_rows": 1, "wide_tokens": 1}, {"wide_rows": 1 << 20, "path_tokens": 1 << 20},
-                {"wide_rows": 4, "wide_tokens": 16, "max_parts": 2}):
+                {"wide_rows": 4, "wide_tokens": 16, "max_parts": 2},
+                {"wide_rows": 128, "wide_tokens": 256, "path_tokens": 1024}):
         trees, others = run(driver, CASES[name](), **env)
         assert trees + others > 0
