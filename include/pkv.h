@@ -23,11 +23,12 @@
  *     (tables, refcounts, free list, sequence ids) is exactly as before the
  *     call and no device work has been enqueued.  pkv_last_error() gives a
  *     message for the calling thread's last failure.
- *   - Ownership: every device pointer (the two K/V pools, new K/V, Q, out,
- *     lse) is owned by the caller and must stay valid until the work enqueued
- *     on the stream has finished.  The pool handle owns its host metadata and
- *     the device scratch it allocates itself (plans and partial softmax
- *     states); kv_pool_destroy releases both after synchronising the device.
+ *   - Ownership: every device pointer (the two K/V pools, the workspace, new
+ *     K/V, Q, out, lse) is owned by the caller and must stay valid until the
+ *     work enqueued on the stream has finished.  The pool handle owns its host
+ *     metadata and any device memory it allocates itself (a workspace when
+ *     the caller gives none, the append / commit lists); kv_pool_destroy
+ *     releases both after synchronising the device.
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *     stream).  Device work of one pool must be issued on a single stream, or
  *     the caller must order the streams: calls reuse the pool's scratch.
@@ -54,7 +55,8 @@ typedef struct pkv_pool pkv_pool;
 typedef enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_ARG = -1,         /* bad argument, pointer or shape */
-  PKV_ERR_OOM = -2,         /* the free list cannot supply the blocks a call needs */
+  PKV_ERR_OOM = -2,         /* the free list cannot supply the blocks a call needs, or a
+                               call's plan / partial states do not fit the pool's workspace */
   PKV_ERR_SEQ = -3,         /* unknown or freed sequence id */
   PKV_ERR_HIP = -4,         /* a HIP runtime call failed (message says which) */
   PKV_ERR_EMPTY = -5,       /* attention over a sequence with no tokens */
@@ -74,20 +76,66 @@ typedef struct pkv_desc {
 size_t kv_pool_bytes(const pkv_desc* desc);
 
 /*
+ * Device workspace of a pool: the work lists ("plans") of its decode,
+ * tree-verify and prefill calls and their partial softmax states.
+ *   ptr:   device memory on the pool's device, 256-byte aligned, of `bytes`
+ *          bytes, owned by the caller; or NULL: the pool allocates its own
+ *          buffers and grows them when a call needs more (hipMalloc inside
+ *          that call; an outgrown buffer is freed once the work enqueued
+ *          before it has finished, with no device-wide synchronisation).
+ *   bytes: at least kv_workspace_bytes(desc, max_seqs, max_tree_nodes).
+ *   max_seqs:       sequences per attention call at most (0: 256).
+ *   max_tree_nodes: query tokens per sequence at most -- the draft-tree
+ *          nodes of a verify call, the new tokens of a prefill call (0: 64).
+ * With a caller workspace, decode / verify / prefill calls allocate no
+ * device memory: a call over more sequences or query tokens than these
+ * limits returns PKV_ERR_ARG; a call whose work lists would not fit is
+ * planned again with fewer, longer work items (no partial states where a
+ * whole sequence fits one item) and returns PKV_ERR_OOM only if even that
+ * plan does not fit -- never for calls within the limits when `bytes` is
+ * the bound below.  Both errors come before any work is enqueued.
+ */
+typedef struct pkv_workspace {
+  void* ptr;
+  size_t bytes;
+  int32_t max_seqs;
+  int32_t max_tree_nodes;
+} pkv_workspace;
+
+/* Bytes of workspace that make every attention call within (max_seqs,
+ * max_tree_nodes) on a pool of this shape fit, at any context length the
+ * pool can hold: the decode, verify and prefill work lists (regions of their
+ * own, so a cached decode plan survives the other calls) and the partial
+ * states, each region 256-byte aligned.  0 for an invalid desc or limits
+ * outside 1 .. 65536. */
+size_t kv_workspace_bytes(const pkv_desc* desc, int32_t max_seqs, int32_t max_tree_nodes);
+
+/* The regions of that workspace, in order: regions[0] decode work lists,
+ * [1] verify work lists, [2] prefill work lists, [3] partial states (bytes;
+ * they sum to kv_workspace_bytes). */
+pkv_status kv_workspace_layout(const pkv_desc* desc, int32_t max_seqs, int32_t max_tree_nodes,
+                               size_t* regions);
+
+/*
  * Create a pool over caller-owned device arrays k_pool / v_pool (bf16, layout
  * above, each kv_pool_bytes(desc) bytes, on the device current at this call).
  * Passing NULL for both makes a host-only pool: the same allocator and block
  * tables with no device storage, for planning and tests (kv_append then takes
  * NULL K/V and attention calls return PKV_ERR_ARG).
  * Device pools also need one layer of one array (num_blocks * num_kv_heads *
- * block_size * head_dim * 2 bytes) under 64 GiB; else PKV_ERR_UNSUPPORTED.
+ * block_size * head_dim * 2 bytes) under 64 GiB and fewer than 2^24 blocks;
+ * else PKV_ERR_UNSUPPORTED.
+ * ws: the device workspace (see pkv_workspace); NULL is {NULL, 0, 0, 0}.  A
+ * caller workspace smaller than kv_workspace_bytes(desc, max_seqs,
+ * max_tree_nodes) or not 256-byte aligned is PKV_ERR_ARG.  Host-only pools
+ * take none.
  * free_order: NULL for the initial free list 0..num_blocks-1, else a host
  * array holding a permutation of 0..num_blocks-1 (head first).
  * Blocks are taken from the head of the free list; a block whose refcount
  * drops to zero is appended at the tail (SGLang RadixAttention page,
  * source-level sketch: free page pool, extend on reclaim).
  */
-pkv_status kv_pool_create(const pkv_desc* desc, void* k_pool, void* v_pool,
+pkv_status kv_pool_create(const pkv_desc* desc, void* k_pool, void* v_pool, const pkv_workspace* ws,
                           const int32_t* free_order, pkv_pool** out);
 
 /*
@@ -123,7 +171,8 @@ size_t kv_pool_q4_bytes(const pkv_desc* desc, size_t* norm_bytes);
  * signs: host int8 [head_dim] of +1 / -1 (the rotation's random signs).
  * head_dim 64 or 128 and at most 16 query heads per kv head, else
  * PKV_ERR_UNSUPPORTED.  paged_attn_tree_verify, paged_attn_prefill and
- * kv_tree_commit return PKV_ERR_UNSUPPORTED on a 4-bit pool.
+ * kv_tree_commit return PKV_ERR_UNSUPPORTED on a 4-bit pool.  A 4-bit pool
+ * manages its own workspace (as kv_pool_create with ws NULL).
  */
 pkv_status kv_pool_create_q4(const pkv_desc* desc, void* k_codes, void* v_codes, void* k_norms,
                              void* v_norms, const int8_t* signs, const int32_t* free_order,
@@ -361,11 +410,21 @@ typedef struct pkv_plan_stats {
   int32_t merged_rows;     /* query rows whose partial states are merged */
   int32_t direct;          /* 1: one workgroup per query and kv head (direct kernel) */
   int32_t max_parts;       /* most partial states merged into one query (0: no merge) */
+  int64_t plan_bytes;      /* device bytes of the call's work lists */
+  int64_t partial_bytes;   /* device bytes of its partial softmax states */
 } pkv_plan_stats;
 
-/* What paged_attn_decode would read and launch for these sequences (host only). */
+/* What paged_attn_decode would read and launch for these sequences (host
+ * only; planned as the call would be, before any fitting to a workspace). */
 pkv_status paged_attn_decode_plan_stats(pkv_pool* pool, const int64_t* seqs,
                                         int32_t n_seqs, pkv_plan_stats* out);
+
+/* Likewise for paged_attn_tree_verify (parent as there) and
+ * paged_attn_prefill (n_new as there); segments is the number of sequences. */
+pkv_status paged_attn_verify_plan_stats(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
+                                        int32_t n_nodes, const int32_t* parent, pkv_plan_stats* out);
+pkv_status paged_attn_prefill_plan_stats(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
+                                         const int32_t* n_new, pkv_plan_stats* out);
 
 /* ---- kernel timing (benchmarks) --------------------------------------- */
 

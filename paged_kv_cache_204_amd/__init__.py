@@ -20,11 +20,12 @@ import numpy as np
 
 __all__ = [
     "PkvError", "PkvDesc", "load", "library_path",
-    "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_q4_bytes", "kv_pool_create_q4",
+    "kv_pool_bytes", "kv_workspace_bytes", "kv_workspace_layout", "kv_pool_create", "kv_pool_destroy", "kv_pool_q4_bytes", "kv_pool_create_q4",
     "seq_allocate", "seq_fork", "seq_free", "kv_append",
     "paged_attn_decode", "paged_attn_tree_verify", "paged_attn_prefill", "kv_tree_commit",
     "seq_block_table", "block_refcount", "free_list", "kv_last_append",
-    "paged_attn_decode_plan_stats", "pkv_timing_enable", "pkv_timing_read", "pkv_last_error",
+    "paged_attn_decode_plan_stats", "paged_attn_verify_plan_stats", "paged_attn_prefill_plan_stats",
+    "pkv_timing_enable", "pkv_timing_read", "pkv_last_error",
     "pkv_hbm_read_probe",
     "seq_ids",
     "radix_create", "radix_destroy", "radix_match", "radix_insert", "radix_release",
@@ -68,7 +69,13 @@ class PkvPlanStats(ctypes.Structure):
     _fields_ = [("unique_tokens", ctypes.c_int64), ("logical_tokens", ctypes.c_int64),
                 ("unique_blocks", ctypes.c_int32), ("segments", ctypes.c_int32),
                 ("work_items", ctypes.c_int32), ("merged_rows", ctypes.c_int32),
-                ("direct", ctypes.c_int32), ("max_parts", ctypes.c_int32)]
+                ("direct", ctypes.c_int32), ("max_parts", ctypes.c_int32),
+                ("plan_bytes", ctypes.c_int64), ("partial_bytes", ctypes.c_int64)]
+
+
+class PkvWorkspace(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("bytes", ctypes.c_size_t),
+                ("max_seqs", ctypes.c_int32), ("max_tree_nodes", ctypes.c_int32)]
 
 
 _lib = None
@@ -92,7 +99,10 @@ def load():
     lib = ctypes.CDLL(path)
     sig = {
         "kv_pool_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvDesc)]),
-        "kv_pool_create": (_I32, [ctypes.POINTER(PkvDesc), _P, _P, _PI32, ctypes.POINTER(_P)]),
+        "kv_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvDesc), _I32, _I32]),
+        "kv_workspace_layout": (_I32, [ctypes.POINTER(PkvDesc), _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+        "kv_pool_create": (_I32, [ctypes.POINTER(PkvDesc), _P, _P, ctypes.POINTER(PkvWorkspace), _PI32,
+                                  ctypes.POINTER(_P)]),
         "kv_pool_destroy": (None, [_P]),
         "kv_pool_q4_bytes": (ctypes.c_size_t, [ctypes.POINTER(PkvDesc), ctypes.POINTER(ctypes.c_size_t)]),
         "kv_pool_create_q4": (_I32, [ctypes.POINTER(PkvDesc), _P, _P, _P, _P,
@@ -112,6 +122,8 @@ def load():
         "free_list": (_I32, [_P, _PI32, _I32, _PI32]),
         "kv_last_append": (_I32, [_P, _PI32, _I32, _PI32, _PI32, _I32, _PI32]),
         "paged_attn_decode_plan_stats": (_I32, [_P, _PI64, _I32, ctypes.POINTER(PkvPlanStats)]),
+        "paged_attn_verify_plan_stats": (_I32, [_P, _PI64, _I32, _I32, _PI32, ctypes.POINTER(PkvPlanStats)]),
+        "paged_attn_prefill_plan_stats": (_I32, [_P, _PI64, _I32, _PI32, ctypes.POINTER(PkvPlanStats)]),
         "pkv_timing_enable": (_I32, [_P, _I32]),
         "pkv_timing_read": (_I32, [_P, ctypes.POINTER(ctypes.c_double), _PI64, _I32]),
         "pkv_last_error": (ctypes.c_char_p, []),
@@ -207,16 +219,39 @@ def kv_pool_bytes(desc) -> int:
     return load().kv_pool_bytes(ctypes.byref(d))
 
 
-def kv_pool_create(desc, k_pool=None, v_pool=None, free_order=None):
+def kv_workspace_bytes(desc, max_seqs, max_tree_nodes) -> int:
+    """Device bytes of workspace for calls of at most max_seqs sequences and
+    max_tree_nodes query tokens per sequence (0 for invalid arguments)."""
+    return int(load().kv_workspace_bytes(ctypes.byref(_desc(desc)), int(max_seqs), int(max_tree_nodes)))
+
+
+def kv_workspace_layout(desc, max_seqs, max_tree_nodes) -> dict:
+    """Bytes of each workspace region: decode, verify, prefill work lists and partial states."""
+    r = (ctypes.c_size_t * 4)()
+    _check(load().kv_workspace_layout(ctypes.byref(_desc(desc)), int(max_seqs), int(max_tree_nodes), r))
+    return dict(zip(("decode", "verify", "prefill", "partials"), (int(x) for x in r)))
+
+
+def kv_pool_create(desc, k_pool=None, v_pool=None, free_order=None, workspace=None, workspace_bytes=None,
+                   max_seqs=0, max_tree_nodes=0):
+    """workspace: a device buffer (tensor or address) the pool carves its
+    work lists and partial states from, of workspace_bytes bytes (default:
+    the tensor's size); None: the pool manages its own."""
     d = _desc(desc)
     fo = None
     keep = None
     if free_order is not None:
         keep = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
         fo = keep.ctypes.data_as(_PI32)
+    ws = None
+    if workspace is not None or max_seqs or max_tree_nodes:
+        nbytes = workspace_bytes
+        if nbytes is None and workspace is not None:
+            nbytes = workspace.numel() * workspace.element_size()
+        ws = PkvWorkspace(_addr(workspace), int(nbytes or 0), int(max_seqs), int(max_tree_nodes))
     out = _P()
-    _check(load().kv_pool_create(ctypes.byref(d), _addr(k_pool), _addr(v_pool), fo,
-                                 ctypes.byref(out)))
+    _check(load().kv_pool_create(ctypes.byref(d), _addr(k_pool), _addr(v_pool),
+                                 ctypes.byref(ws) if ws is not None else None, fo, ctypes.byref(out)))
     return out
 
 
@@ -356,6 +391,23 @@ def paged_attn_decode_plan_stats(pool, seqs) -> dict:
     p, n = _seq_array(seqs)
     st = PkvPlanStats()
     _check(load().paged_attn_decode_plan_stats(pool, p, n, ctypes.byref(st)))
+    return {f: getattr(st, f) for f, _ in PkvPlanStats._fields_}
+
+
+def paged_attn_verify_plan_stats(pool, seqs, n_nodes, parents) -> dict:
+    p, n = _seq_array(seqs)
+    par = np.ascontiguousarray(np.asarray(parents, dtype=np.int32).reshape(-1))
+    st = PkvPlanStats()
+    _check(load().paged_attn_verify_plan_stats(pool, p, n, int(n_nodes), par.ctypes.data_as(_PI32),
+                                               ctypes.byref(st)))
+    return {f: getattr(st, f) for f, _ in PkvPlanStats._fields_}
+
+
+def paged_attn_prefill_plan_stats(pool, seqs, n_new) -> dict:
+    p, n = _seq_array(seqs)
+    nn = np.ascontiguousarray(np.asarray(n_new, dtype=np.int32).reshape(-1))
+    st = PkvPlanStats()
+    _check(load().paged_attn_prefill_plan_stats(pool, p, n, nn.ctypes.data_as(_PI32), ctypes.byref(st)))
     return {f: getattr(st, f) for f, _ in PkvPlanStats._fields_}
 
 

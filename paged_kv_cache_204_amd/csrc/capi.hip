@@ -41,6 +41,7 @@ pkv_status to_status(pkv::Err e) { return static_cast<pkv_status>(static_cast<in
 struct DevBuf {
   void* ptr = nullptr;
   size_t cap = 0;
+  bool owned = true;   // false: a region of the caller's workspace (never grown or freed)
 };
 
 constexpr int kStageSlots = 4;
@@ -118,6 +119,12 @@ struct pkv_pool {
   uint16_t* k_pool = nullptr;
   uint16_t* v_pool = nullptr;
   DevBuf append_plan, commit_plan, decode_plan, verify_plan, prefill_plan, partials;
+  // a caller workspace: the four buffers above from decode_plan on are its
+  // fixed regions, and calls stay within these limits
+  bool ws_fixed = false;
+  int32_t ws_max_seqs = 0, ws_max_nodes = 0;
+  // outgrown buffers of the pool's own, freed once their event has completed
+  std::vector<std::pair<void*, hipEvent_t>> retired;
   // 4-bit pools: codes and norms instead of bf16 K/V (k_pool / v_pool unused)
   bool q4 = false;
   uint8_t* k_codes = nullptr;
@@ -181,17 +188,45 @@ void detach_radixes(pkv_pool* p) {
 
 namespace {
 
-pkv_status ensure(DevBuf& b, size_t bytes) {
-  if (bytes <= b.cap) return PKV_OK;
-  size_t want = bytes + bytes / 2 + 4096;
-  if (b.ptr) {
-    // the old buffer may still be read by enqueued kernels
-    PKV_HIP(hipDeviceSynchronize());
-    PKV_HIP(hipFree(b.ptr));
-    b.ptr = nullptr;
-    b.cap = 0;
+// Frees the outgrown buffers whose last readers have finished.
+void reap(pkv_pool* p) {
+  for (size_t i = 0; i < p->retired.size();) {
+    if (hipEventQuery(p->retired[i].second) == hipSuccess) {
+      (void)hipFree(p->retired[i].first);
+      (void)hipEventDestroy(p->retired[i].second);
+      p->retired[i] = p->retired.back();
+      p->retired.pop_back();
+    } else {
+      ++i;
+    }
   }
-  PKV_HIP(hipMalloc(&b.ptr, want));
+}
+
+// Room for `bytes` in b.  A region of the caller's workspace never grows
+// (PKV_ERR_OOM); a buffer of the pool's own is replaced by a larger one and
+// the old one kept until the work enqueued on `stream` so far has finished
+// with it (an event; no device-wide synchronisation).
+pkv_status ensure(pkv_pool* p, DevBuf& b, size_t bytes, hipStream_t stream) {
+  if (bytes <= b.cap) return PKV_OK;
+  if (!b.owned)
+    return fail(PKV_ERR_OOM, "a workspace region of " + std::to_string(b.cap) + " bytes cannot hold " +
+                                 std::to_string(bytes));
+  reap(p);
+  const size_t want = bytes + bytes / 2 + 4096;
+  void* np = nullptr;
+  PKV_HIP(hipMalloc(&np, want));
+  if (b.ptr) {
+    hipEvent_t ev = nullptr;
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(ev, stream);
+    if (e != hipSuccess) {
+      if (ev) (void)hipEventDestroy(ev);
+      (void)hipFree(np);
+      return fail(PKV_ERR_HIP, std::string("ensure: ") + hipGetErrorString(e));
+    }
+    p->retired.emplace_back(b.ptr, ev);
+  }
+  b.ptr = np;
   b.cap = want;
   return PKV_OK;
 }
@@ -201,7 +236,7 @@ pkv_status ensure(DevBuf& b, size_t bytes) {
 // that last read it has completed.
 template <class Fill>
 pkv_status upload(pkv_pool* p, DevBuf& dst, size_t bytes, hipStream_t stream, Fill fill) {
-  pkv_status s = ensure(dst, bytes);
+  pkv_status s = ensure(p, dst, bytes, stream);
   if (s != PKV_OK) return s;
   if (bytes == 0) return PKV_OK;
   const int i = p->stage_next;
@@ -231,6 +266,104 @@ pkv_status take_event(pkv_pool* p, hipEvent_t* ev) {
   }
   PKV_HIP(hipEventCreate(ev));
   return PKV_OK;
+}
+
+size_t partial_bytes(const pkv::Plan& plan, const pkv::Shape& sh) {
+  return static_cast<size_t>(plan.partial_rows) * (sh.head_dim + 1) * sizeof(float);
+}
+
+// ---- workspace ----------------------------------------------------------
+//
+// Regions for calls of at most S sequences and T query tokens per sequence,
+// from what the planners can produce (N blocks of B tokens, Hq query heads):
+//  - a work item's device entry is a WorkItem and a block list padded to
+//    the plan's longest, at most min(512, N) blocks;
+//  - the coarsest plan of a call (fit_plan: no shared runs, longest chunks)
+//    cuts a sequence into at most c = ceil(N B / min(4096, 512 B)) items;
+//  - a decode plan: up to 16 + c items and row groups per query, one merge
+//    row, 64 overflow part ids, one path item and 64 steps per query (plus
+//    65536 steps); up to max(12, c) partial states per query and head;
+//  - verify / prefill: S T query rows in windows of at least one row, each
+//    window up to max(4, c) items and partial states;
+//  - 4-bit decode: an item and a whole block table per query.
+constexpr size_t kWsAlign = 256;
+constexpr int32_t kDefaultMaxSeqs = 256;
+constexpr int32_t kDefaultMaxNodes = 64;
+
+size_t ws_align(size_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
+
+struct WsLayout {
+  size_t decode = 0, verify = 0, prefill = 0, partials = 0, total = 0;
+};
+
+WsLayout ws_layout(const pkv::Shape& sh, int64_t S, int64_t T) {
+  const int64_t N = sh.num_blocks, B = sh.block_size, Hq = sh.num_q_heads, D = sh.head_dim;
+  const int64_t mb = std::min<int64_t>(512, N);
+  const int64_t cap_tok = std::min<int64_t>(4096, 512 * B);
+  const int64_t c = (N * B + cap_tok - 1) / cap_tok;
+  const int64_t item = static_cast<int64_t>(sizeof(pkv::WorkItem)) + 4 * mb;
+  const int64_t grp = sizeof(pkv::RowGroup), mrg = sizeof(pkv::MergeRow);
+  const int64_t pad = 8 * 16;   // the plan arrays' 16-byte alignment
+  WsLayout w;
+  int64_t dec = S * (16 + c) * (item + grp) + S * mrg + S * 64 * 4 + S * static_cast<int64_t>(sizeof(pkv::PathItem)) +
+                (64 * S + 65536) * static_cast<int64_t>(sizeof(pkv::PathStep)) + pad;
+  dec = std::max<int64_t>(dec, S * static_cast<int64_t>(sizeof(pkv::Q4Item)) + S * N * 4 + pad);
+  const int64_t Q = S * T;
+  const int64_t pv = std::max<int64_t>(4, c);
+  const int64_t ver = Q * pv * item + Q * grp + Q * mrg + Q * pv * 4 + pad;
+  const int64_t rows = std::max(S * Hq * std::max<int64_t>(12, c), Q * Hq * pv);
+  w.decode = ws_align(static_cast<size_t>(dec));
+  w.verify = ws_align(static_cast<size_t>(ver));
+  w.prefill = w.verify;
+  w.partials = ws_align(static_cast<size_t>(rows * (D + 1) * 4));
+  w.total = w.decode + w.verify + w.prefill + w.partials;
+  return w;
+}
+
+// Planner settings for the smallest plan of a call: no tree or shared runs
+// (a decode query is one segment, or one direct item), every item a dense
+// tile, the longest chunks and so the fewest items and partial states.
+pkv::PlanConfig coarse_config(const pkv::PlanConfig& cfg) {
+  pkv::PlanConfig c = cfg;
+  c.tree_decode = 0;
+  c.private_segments = 1;
+  c.direct_max_tokens = 1 << 30;
+  c.direct_max_wgs = 1 << 30;
+  c.mfma_min_rows = 1;
+  c.max_parts = 1;
+  c.target_wgs = 1;
+  c.target_mfma_wgs = 1;
+  c.max_chunk = 4096;
+  c.max_chunk_blocks = 512;
+  return c;
+}
+
+// Whether a plan's work lists fit `region` and its partial states the
+// partial-state region; always true for a pool that grows its own buffers.
+bool fits_workspace(const pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay, const DevBuf& region) {
+  if (!p->ws_fixed) return true;
+  return lay.total <= region.cap && partial_bytes(plan, p->core.shape()) <= p->partials.cap;
+}
+
+// Plans a call with the pool's settings and, when that plan does not fit a
+// caller workspace, once more with coarse_config; PKV_ERR_OOM if neither fits.
+template <class PlanWith>
+pkv_status plan_to_fit(pkv_pool* p, const DevBuf& region, const char* what, pkv::Plan* plan, PlanLayout* lay,
+                       PlanWith plan_with) {
+  std::string why;
+  pkv::Err e = plan_with(p->cfg, plan, &why);
+  if (e != pkv::Err::ok) return fail(to_status(e), why);
+  *lay = layout_of(*plan);
+  if (fits_workspace(p, *plan, *lay, region)) return PKV_OK;
+  e = plan_with(coarse_config(p->cfg), plan, &why);
+  if (e != pkv::Err::ok) return fail(to_status(e), why);
+  *lay = layout_of(*plan);
+  if (fits_workspace(p, *plan, *lay, region)) return PKV_OK;
+  return fail(PKV_ERR_OOM, std::string(what) + ": the call's work lists (" + std::to_string(lay->total) +
+                               " bytes) or partial states (" +
+                               std::to_string(partial_bytes(*plan, p->core.shape())) +
+                               " bytes) do not fit the workspace regions (" + std::to_string(region.cap) +
+                               " and " + std::to_string(p->partials.cap) + " bytes)");
 }
 
 // Every item must fit the tiles its kernel path assumes (LDS arrays, rows
@@ -291,7 +424,7 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
                           float* out, float* lse, hipStream_t stream) {
   const pkv::Shape& sh = p->core.shape();
   const char* base = static_cast<const char*>(buf.ptr);
-  pkv_status s = ensure(p->partials, static_cast<size_t>(plan.partial_rows) * (sh.head_dim + 1) * sizeof(float));
+  pkv_status s = ensure(p, p->partials, partial_bytes(plan, sh), stream);
   if (s != PKV_OK) return s;
   float* part_o = static_cast<float*>(p->partials.ptr);
   float* part_lse = part_o + static_cast<size_t>(plan.partial_rows) * sh.head_dim;
@@ -394,7 +527,10 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15)
 // MFMA / VALU kernel instead of the pipelined dense-tile kernel), and the
 // tree decode planner's PKV_TREE_DECODE (0 turns it off), PKV_TREE_WIDE_ROWS,
 // PKV_TREE_WIDE_TOKENS, PKV_TREE_PATH_TOKENS, PKV_TREE_ITEM_ROWS,
-// PKV_TREE_TARGET_WGS, PKV_TREE_MAX_PARTS and PKV_TREE_MIN_WGS.
+// PKV_TREE_TARGET_WGS, PKV_TREE_MAX_PARTS and PKV_TREE_MIN_WGS, and
+// PKV_PRIVATE_SEGMENTS (1: every decode query one segment, no trie), and
+// PKV_COARSE_PLANS (1: every call planned as the coarsest plan a workspace
+// falls back to).
 void apply_env(pkv::PlanConfig* c) {
   auto get = [](const char* name, int32_t* v, int32_t lo, int32_t hi) {
     const char* e = std::getenv(name);
@@ -424,6 +560,10 @@ void apply_env(pkv::PlanConfig* c) {
   get("PKV_TREE_TARGET_WGS", &c->tree_target_wgs, 1, 1 << 20);
   get("PKV_TREE_MAX_PARTS", &c->tree_max_parts, 1, pkv::kPathMaxParts);
   get("PKV_TREE_MIN_WGS", &c->tree_min_wgs, 0, 1 << 20);
+  get("PKV_PRIVATE_SEGMENTS", &c->private_segments, 0, 1);
+  int32_t coarse = 0;
+  get("PKV_COARSE_PLANS", &coarse, 0, 1);
+  if (coarse) *c = coarse_config(*c);
 }
 
 }  // namespace
@@ -438,7 +578,26 @@ size_t kv_pool_bytes(const pkv_desc* d) {
          s.head_dim * sizeof(uint16_t);
 }
 
-pkv_status kv_pool_create(const pkv_desc* d, void* k_pool, void* v_pool,
+size_t kv_workspace_bytes(const pkv_desc* d, int32_t max_seqs, int32_t max_tree_nodes) {
+  size_t r[4];
+  return kv_workspace_layout(d, max_seqs, max_tree_nodes, r) == PKV_OK ? r[0] + r[1] + r[2] + r[3] : 0;
+}
+
+pkv_status kv_workspace_layout(const pkv_desc* d, int32_t max_seqs, int32_t max_tree_nodes, size_t* regions) {
+  if (!d || !regions || max_seqs < 1 || max_seqs > 65536 || max_tree_nodes < 1 || max_tree_nodes > 65536)
+    return fail(PKV_ERR_ARG, "kv_workspace_layout: NULL argument or limits outside 1 .. 65536");
+  pkv::Shape s{d->num_blocks, d->block_size, d->num_layers, d->num_q_heads, d->num_kv_heads, d->head_dim};
+  std::string why;
+  if (!pkv::valid_shape(s, &why)) return fail(PKV_ERR_ARG, "kv_workspace_layout: " + why);
+  const WsLayout w = ws_layout(s, max_seqs, max_tree_nodes);
+  regions[0] = w.decode;
+  regions[1] = w.verify;
+  regions[2] = w.prefill;
+  regions[3] = w.partials;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_create(const pkv_desc* d, void* k_pool, void* v_pool, const pkv_workspace* ws,
                           const int32_t* free_order, pkv_pool** out) {
   if (!d || !out) return fail(PKV_ERR_ARG, "kv_pool_create: desc and out must not be NULL");
   *out = nullptr;
@@ -459,6 +618,24 @@ pkv_status kv_pool_create(const pkv_desc* d, void* k_pool, void* v_pool,
     const int64_t layer_chunks = static_cast<int64_t>(s.num_blocks) * s.num_kv_heads * s.block_size * s.head_dim / 8;
     if (layer_chunks >= (int64_t{1} << 32) || static_cast<int64_t>(s.num_kv_heads) * s.block_size * s.head_dim / 8 >= (1 << 24))
       return fail(PKV_ERR_UNSUPPORTED, "kv_pool_create: one layer of a device pool must stay under 64 GiB");
+    // block ids enter the kernels' 24-bit multiplies
+    if (s.num_blocks >= (1 << 24))
+      return fail(PKV_ERR_UNSUPPORTED, "kv_pool_create: a device pool holds fewer than 2^24 blocks");
+  }
+  const pkv_workspace wsd = ws ? *ws : pkv_workspace{nullptr, 0, 0, 0};
+  const int32_t max_seqs = wsd.max_seqs > 0 ? wsd.max_seqs : kDefaultMaxSeqs;
+  const int32_t max_nodes = wsd.max_tree_nodes > 0 ? wsd.max_tree_nodes : kDefaultMaxNodes;
+  if (wsd.max_seqs < 0 || wsd.max_tree_nodes < 0 || max_seqs > 65536 || max_nodes > 65536)
+    return fail(PKV_ERR_ARG, "kv_pool_create: workspace limits must be 0 or 1 .. 65536");
+  WsLayout wl;
+  if (wsd.ptr) {
+    if (!device) return fail(PKV_ERR_ARG, "kv_pool_create: a host-only pool takes no workspace");
+    if ((reinterpret_cast<uintptr_t>(wsd.ptr) & (kWsAlign - 1)) != 0)
+      return fail(PKV_ERR_ARG, "kv_pool_create: the workspace must be 256-byte aligned");
+    wl = ws_layout(s, max_seqs, max_nodes);
+    if (wsd.bytes < wl.total)
+      return fail(PKV_ERR_ARG, "kv_pool_create: the workspace holds " + std::to_string(wsd.bytes) +
+                                   " bytes, calls within its limits need " + std::to_string(wl.total));
   }
   if (free_order) {
     std::vector<char> seen(s.num_blocks, 0);
@@ -481,6 +658,32 @@ pkv_status kv_pool_create(const pkv_desc* d, void* k_pool, void* v_pool,
     }
     p->k_pool = static_cast<uint16_t*>(k_pool);
     p->v_pool = static_cast<uint16_t*>(v_pool);
+    if (wsd.ptr) {
+      // fixed regions of the caller's workspace, and pinned staging large
+      // enough for any work list they hold, so calls allocate nothing
+      p->ws_fixed = true;
+      p->ws_max_seqs = max_seqs;
+      p->ws_max_nodes = max_nodes;
+      char* base = static_cast<char*>(wsd.ptr);
+      size_t at = 0;
+      for (auto [buf, bytes] : {std::pair<DevBuf*, size_t>{&p->decode_plan, wl.decode}, {&p->verify_plan, wl.verify},
+                                {&p->prefill_plan, wl.prefill}, {&p->partials, wl.partials}}) {
+        buf->ptr = base + at;
+        buf->cap = bytes;
+        buf->owned = false;
+        at += bytes;
+      }
+      const size_t stage = std::max({wl.decode, wl.verify, wl.prefill});
+      for (int i = 0; i < kStageSlots && e == hipSuccess; ++i) {
+        e = hipHostMalloc(&p->stage[i], stage, hipHostMallocDefault);
+        if (e == hipSuccess) p->stage_cap[i] = stage;
+        else p->stage[i] = nullptr;
+      }
+      if (e != hipSuccess) {
+        kv_pool_destroy(p);
+        return fail(PKV_ERR_HIP, std::string("kv_pool_create: pinned staging: ") + hipGetErrorString(e));
+      }
+    }
   }
   *out = p;
   return PKV_OK;
@@ -513,7 +716,7 @@ pkv_status kv_pool_create_q4(const pkv_desc* d, void* k_codes, void* v_codes, vo
   for (int32_t i = 0; i < s.head_dim; ++i)
     if (signs[i] != 1 && signs[i] != -1) return fail(PKV_ERR_ARG, "kv_pool_create_q4: signs must be +1 or -1");
   // a placeholder bf16 pair keeps the device path of kv_pool_create; never read
-  pkv_status st = kv_pool_create(d, k_codes, v_codes, free_order, out);
+  pkv_status st = kv_pool_create(d, k_codes, v_codes, nullptr, free_order, out);
   if (st != PKV_OK) return st;
   pkv_pool* p = *out;
   p->q4 = true;
@@ -525,9 +728,11 @@ pkv_status kv_pool_create_q4(const pkv_desc* d, void* k_codes, void* v_codes, vo
   std::vector<float> sf(signs, signs + s.head_dim);
   for (float& f : sf) f = f > 0 ? 1.f : -1.f;
   DeviceGuard g(p->dev);
-  st = ensure(p->signs, sf.size() * sizeof(float));
-  hipError_t e = st == PKV_OK ? hipMemcpy(p->signs.ptr, sf.data(), sf.size() * sizeof(float), hipMemcpyHostToDevice)
-                              : hipErrorOutOfMemory;
+  hipError_t e = hipMalloc(&p->signs.ptr, sf.size() * sizeof(float));
+  if (e == hipSuccess) {
+    p->signs.cap = sf.size() * sizeof(float);
+    e = hipMemcpy(p->signs.ptr, sf.data(), sf.size() * sizeof(float), hipMemcpyHostToDevice);
+  }
   if (e != hipSuccess) {
     kv_pool_destroy(p);
     *out = nullptr;
@@ -543,7 +748,11 @@ void kv_pool_destroy(pkv_pool* p) {
     DeviceGuard g(p->dev);
     (void)hipDeviceSynchronize();
     for (DevBuf* b : {&p->append_plan, &p->commit_plan, &p->decode_plan, &p->verify_plan, &p->prefill_plan, &p->partials, &p->signs})
-      if (b->ptr) (void)hipFree(b->ptr);
+      if (b->ptr && b->owned) (void)hipFree(b->ptr);
+    for (auto& r : p->retired) {
+      (void)hipFree(r.first);
+      (void)hipEventDestroy(r.second);
+    }
     for (int i = 0; i < kStageSlots; ++i) {
       if (p->stage[i]) (void)hipHostFree(p->stage[i]);
       if (p->stage_ev[i]) (void)hipEventDestroy(p->stage_ev[i]);
@@ -792,6 +1001,8 @@ pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, in
     return fail(PKV_ERR_ARG, "paged_attn_decode: layer out of range");
   if (!aligned16(q) || !aligned16(out))
     return fail(PKV_ERR_ARG, "paged_attn_decode: q and out must be 16-byte aligned");
+  if (p->ws_fixed && n_seqs > p->ws_max_seqs)
+    return fail(PKV_ERR_ARG, "paged_attn_decode: more sequences than the workspace's max_seqs");
   if (p->q4) return decode_q4(p, layer, seqs, n_seqs, q, sm_scale, out, lse, stream);
   DeviceGuard g(p->dev);
   PKV_HIP(g.err);
@@ -801,8 +1012,10 @@ pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, in
   bool hit = same_seqs && p->dcache_version == p->core.version();
   if (same_seqs && !hit && pkv::patch_decode(p->core, seqs, n_seqs, p->cfg, &p->dplan)) {
     // appends only filled the sequences' last blocks: same plan, longer tail items
-    if (!plan_fits_kernels(p->dplan, p->core.shape()))
+    if (!plan_fits_kernels(p->dplan, p->core.shape())) {
+      p->dcache_valid = false;
       return fail(PKV_ERR_ARG, "paged_attn_decode: internal plan exceeds the kernels' tile limits");
+    }
     pkv_status s = upload(p, p->decode_plan, p->dlayout.total, st,
                           [&](char* dst) { serialize(p->dplan, p->dlayout, dst); });
     if (s != PKV_OK) {
@@ -814,13 +1027,16 @@ pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, in
   }
   if (!hit) {
     p->dcache_valid = false;
-    std::string why;
-    pkv::Err e = pkv::plan_decode(p->core, seqs, n_seqs, p->cfg, &p->dplan, &why);
-    if (e != pkv::Err::ok) return fail(to_status(e), why);
+    pkv_status s = plan_to_fit(p, p->decode_plan, "paged_attn_decode", &p->dplan, &p->dlayout,
+                               [&](const pkv::PlanConfig& c, pkv::Plan* pl, std::string* why) {
+                                 return pkv::plan_decode(p->core, seqs, n_seqs, c, pl, why);
+                               });
+    if (s != PKV_OK) return s;
     if (!plan_fits_kernels(p->dplan, p->core.shape()))
       return fail(PKV_ERR_ARG, "paged_attn_decode: internal plan exceeds the kernels' tile limits");
-    p->dlayout = layout_of(p->dplan);
-    pkv_status s = upload(p, p->decode_plan, p->dlayout.total, st,
+    s = ensure(p, p->partials, partial_bytes(p->dplan, p->core.shape()), st);
+    if (s != PKV_OK) return s;
+    s = upload(p, p->decode_plan, p->dlayout.total, st,
                           [&](char* dst) { serialize(p->dplan, p->dlayout, dst); });
     if (s != PKV_OK) return s;
     p->dcache_seqs.assign(seqs, seqs + n_seqs);
@@ -844,16 +1060,21 @@ pkv_status paged_attn_tree_verify(pkv_pool* p, int32_t layer, const int64_t* seq
     return fail(PKV_ERR_ARG, "paged_attn_tree_verify: layer out of range");
   if (!aligned16(q) || !aligned16(out))
     return fail(PKV_ERR_ARG, "paged_attn_tree_verify: q and out must be 16-byte aligned");
-  std::string why;
-  pkv::Err e = pkv::plan_verify(p->core, seqs, n_seqs, n_nodes, parent, p->cfg, &p->vplan, &why);
-  if (e != pkv::Err::ok) return fail(to_status(e), why);
+  if (p->ws_fixed && (n_seqs > p->ws_max_seqs || n_nodes > p->ws_max_nodes))
+    return fail(PKV_ERR_ARG, "paged_attn_tree_verify: more sequences or tree nodes than the workspace's limits");
+  pkv_status s = plan_to_fit(p, p->verify_plan, "paged_attn_tree_verify", &p->vplan, &p->vlayout,
+                             [&](const pkv::PlanConfig& c, pkv::Plan* pl, std::string* why) {
+                               return pkv::plan_verify(p->core, seqs, n_seqs, n_nodes, parent, c, pl, why);
+                             });
+  if (s != PKV_OK) return s;
   DeviceGuard g(p->dev);
   PKV_HIP(g.err);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!plan_fits_kernels(p->vplan, p->core.shape()))
     return fail(PKV_ERR_ARG, "paged_attn_tree_verify: internal plan exceeds the kernels' tile limits");
-  p->vlayout = layout_of(p->vplan);
-  pkv_status s = upload(p, p->verify_plan, p->vlayout.total, st,
+  s = ensure(p, p->partials, partial_bytes(p->vplan, p->core.shape()), st);
+  if (s != PKV_OK) return s;
+  s = upload(p, p->verify_plan, p->vlayout.total, st,
                         [&](char* dst) { serialize(p->vplan, p->vlayout, dst); });
   if (s != PKV_OK) return s;
   return launch_plan(p, p->vplan, p->vlayout, p->verify_plan, layer, q, sm_scale, out, lse, st);
@@ -870,15 +1091,24 @@ pkv_status paged_attn_prefill(pkv_pool* p, int32_t layer, const int64_t* seqs, i
   if (!seqs || !n_new) return fail(PKV_ERR_ARG, "paged_attn_prefill: NULL seqs or n_new");
   if (layer < 0 || layer >= p->core.shape().num_layers)
     return fail(PKV_ERR_ARG, "paged_attn_prefill: layer out of range");
+  if (p->ws_fixed) {
+    if (n_seqs > p->ws_max_seqs)
+      return fail(PKV_ERR_ARG, "paged_attn_prefill: more sequences than the workspace's max_seqs");
+    for (int32_t i = 0; i < n_seqs; ++i)
+      if (n_new[i] > p->ws_max_nodes)
+        return fail(PKV_ERR_ARG, "paged_attn_prefill: more new tokens than the workspace's max_tree_nodes");
+  }
   const bool hit = p->pcache_valid && p->pcache_version == p->core.version() &&
                    p->pcache_seqs.size() == static_cast<size_t>(n_seqs) &&
                    std::memcmp(p->pcache_seqs.data(), seqs, n_seqs * sizeof(int64_t)) == 0 &&
                    std::memcmp(p->pcache_new.data(), n_new, n_seqs * sizeof(int32_t)) == 0;
   if (!hit) {
     p->pcache_valid = false;
-    std::string why;
-    pkv::Err e = pkv::plan_prefill(p->core, seqs, n_seqs, n_new, p->cfg, &p->pplan, &why);
-    if (e != pkv::Err::ok) return fail(to_status(e), why);
+    pkv_status s = plan_to_fit(p, p->prefill_plan, "paged_attn_prefill", &p->pplan, &p->playout,
+                               [&](const pkv::PlanConfig& c, pkv::Plan* pl, std::string* why) {
+                                 return pkv::plan_prefill(p->core, seqs, n_seqs, n_new, c, pl, why);
+                               });
+    if (s != PKV_OK) return s;
   }
   if (p->pplan.mfma.empty() && p->pplan.valu.empty()) return PKV_OK;   // no new tokens
   if (!q || !out) return fail(PKV_ERR_ARG, "paged_attn_prefill: NULL q or out");
@@ -890,8 +1120,9 @@ pkv_status paged_attn_prefill(pkv_pool* p, int32_t layer, const int64_t* seqs, i
   if (!hit) {
     if (!plan_fits_kernels(p->pplan, p->core.shape()))
       return fail(PKV_ERR_ARG, "paged_attn_prefill: internal plan exceeds the kernels' tile limits");
-    p->playout = layout_of(p->pplan);
-    pkv_status s = upload(p, p->prefill_plan, p->playout.total, st,
+    pkv_status s = ensure(p, p->partials, partial_bytes(p->pplan, p->core.shape()), st);
+    if (s != PKV_OK) return s;
+    s = upload(p, p->prefill_plan, p->playout.total, st,
                           [&](char* dst) { serialize(p->pplan, p->playout, dst); });
     if (s != PKV_OK) return s;
     p->pcache_seqs.assign(seqs, seqs + n_seqs);
@@ -1026,6 +1257,27 @@ pkv_status kv_last_append(const pkv_pool* p, int32_t* slots, int32_t slot_cap, i
   return PKV_OK;
 }
 
+}  // extern "C"
+
+namespace {
+void fill_stats(const pkv::Plan& plan, const pkv::Shape& sh, pkv_plan_stats* out) {
+  out->unique_tokens = plan.unique_tokens;
+  out->logical_tokens = plan.logical_tokens;
+  out->unique_blocks = plan.unique_blocks;
+  out->segments = plan.segments;
+  out->work_items = static_cast<int32_t>(plan.valu.size() + plan.mfma.size() + plan.direct.size() +
+                                         plan.paths.size());
+  out->merged_rows = static_cast<int32_t>(plan.merges.size()) * sh.num_q_heads;
+  out->direct = plan.direct.empty() ? 0 : 1;
+  out->max_parts = 0;
+  for (const pkv::MergeRow& m : plan.merges) out->max_parts = std::max(out->max_parts, m.n_parts);
+  out->plan_bytes = static_cast<int64_t>(layout_of(plan).total);
+  out->partial_bytes = static_cast<int64_t>(partial_bytes(plan, sh));
+}
+}  // namespace
+
+extern "C" {
+
 pkv_status paged_attn_decode_plan_stats(pkv_pool* p, const int64_t* seqs, int32_t n_seqs,
                                         pkv_plan_stats* out) {
   if (!p || !out || (n_seqs > 0 && !seqs) || n_seqs < 0)
@@ -1034,16 +1286,31 @@ pkv_status paged_attn_decode_plan_stats(pkv_pool* p, const int64_t* seqs, int32_
   std::string why;
   pkv::Err e = pkv::plan_decode(p->core, seqs, n_seqs, p->cfg, &plan, &why);
   if (e != pkv::Err::ok) return fail(to_status(e), why);
-  out->unique_tokens = plan.unique_tokens;
-  out->logical_tokens = plan.logical_tokens;
-  out->unique_blocks = plan.unique_blocks;
-  out->segments = plan.segments;
-  out->work_items = static_cast<int32_t>(plan.valu.size() + plan.mfma.size() + plan.direct.size() +
-                                         plan.paths.size());
-  out->merged_rows = static_cast<int32_t>(plan.merges.size()) * p->core.shape().num_q_heads;
-  out->direct = plan.direct.empty() ? 0 : 1;
-  out->max_parts = 0;
-  for (const pkv::MergeRow& m : plan.merges) out->max_parts = std::max(out->max_parts, m.n_parts);
+  fill_stats(plan, p->core.shape(), out);
+  return PKV_OK;
+}
+
+pkv_status paged_attn_verify_plan_stats(pkv_pool* p, const int64_t* seqs, int32_t n_seqs, int32_t n_nodes,
+                                        const int32_t* parent, pkv_plan_stats* out) {
+  if (!p || !out || n_seqs < 1 || !seqs || !parent)
+    return fail(PKV_ERR_ARG, "paged_attn_verify_plan_stats: bad argument");
+  pkv::Plan plan;
+  std::string why;
+  pkv::Err e = pkv::plan_verify(p->core, seqs, n_seqs, n_nodes, parent, p->cfg, &plan, &why);
+  if (e != pkv::Err::ok) return fail(to_status(e), why);
+  fill_stats(plan, p->core.shape(), out);
+  return PKV_OK;
+}
+
+pkv_status paged_attn_prefill_plan_stats(pkv_pool* p, const int64_t* seqs, int32_t n_seqs, const int32_t* n_new,
+                                         pkv_plan_stats* out) {
+  if (!p || !out || n_seqs < 1 || !seqs || !n_new)
+    return fail(PKV_ERR_ARG, "paged_attn_prefill_plan_stats: bad argument");
+  pkv::Plan plan;
+  std::string why;
+  pkv::Err e = pkv::plan_prefill(p->core, seqs, n_seqs, n_new, p->cfg, &plan, &why);
+  if (e != pkv::Err::ok) return fail(to_status(e), why);
+  fill_stats(plan, p->core.shape(), out);
   return PKV_OK;
 }
 

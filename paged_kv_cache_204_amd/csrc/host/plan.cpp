@@ -205,7 +205,21 @@ Err plan_decode(const BlockPool& pool, const int64_t* seqs, int32_t n_seqs,
            (cfg.mfma_min_rows > 0 && static_cast<int64_t>(nq) * G >= cfg.mfma_min_rows);
   };
   std::vector<Frame> stack;
-  if (n_seqs > 0) {
+  if (cfg.private_segments) {
+    // every query its own segment over its whole table: no shared reads,
+    // and with the longest chunks the fewest items and partial states
+    for (int32_t q = 0; q < n_seqs; ++q) {
+      Segment sg;
+      sg.queries = {q};
+      sg.blocks = st[q]->table.data();
+      sg.nblk = nblk(q);
+      sg.ntok = st[q]->len;
+      sg.ends = true;
+      plan->unique_blocks += sg.nblk;
+      plan->unique_tokens += sg.ntok;
+      segs.push_back(std::move(sg));
+    }
+  } else if (n_seqs > 0) {
     Frame root;
     root.pos = root.own = 0;
     for (int32_t i = 0; i < n_seqs; ++i) root.qs.push_back(i);

@@ -67,6 +67,8 @@ struct PlanConfig {
   int32_t tree_target_wgs = 256; // MFMA workgroups to aim for over all kv heads
   int32_t tree_max_parts = 8;    // partial states per query at most (<= kPathMaxParts)
   int32_t tree_min_wgs = 128;    // path workgroups (items x kv heads) a tree plan needs
+  int32_t private_segments = 0;  // 1: no trie, each decode query one segment over its table
+                                 // (the smallest plan when a workspace is tight)
 };
 
 // Rows of one MFMA work item for a row-tile setting (4 waves x 16 x tiles).

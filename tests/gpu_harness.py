@@ -24,7 +24,7 @@ def to_dev(bits: np.ndarray) -> torch.Tensor:
 
 
 class GpuPool:
-    def __init__(self, shape, free_order=None):
+    def __init__(self, shape, free_order=None, ws_limits=None, ws_bytes=None):
         self.shape = shape
         desc = dict(num_blocks=shape.num_blocks, block_size=shape.block_size,
                     num_layers=shape.num_layers, num_q_heads=shape.num_q_heads,
@@ -34,7 +34,17 @@ class GpuPool:
         # poison unwritten slots with bf16 NaN so a stray read shows up
         self.k = torch.full((n,), 0x7FC0, dtype=torch.int16, device="cuda")
         self.v = torch.full((n,), 0x7FC0, dtype=torch.int16, device="cuda")
-        self.pool = pkv.kv_pool_create(desc, self.k, self.v, free_order=free_order)
+        # ws_limits = (max_seqs, max_tree_nodes): a caller workspace of
+        # kv_workspace_bytes (or ws_bytes) bytes, from torch
+        self.ws = None
+        if ws_limits is not None:
+            nbytes = ws_bytes or pkv.kv_workspace_bytes(desc, *ws_limits)
+            self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            assert self.ws.data_ptr() % 256 == 0
+            self.pool = pkv.kv_pool_create(desc, self.k, self.v, free_order=free_order, workspace=self.ws,
+                                           max_seqs=ws_limits[0], max_tree_nodes=ws_limits[1])
+        else:
+            self.pool = pkv.kv_pool_create(desc, self.k, self.v, free_order=free_order)
         self.stream = torch.cuda.current_stream().cuda_stream
 
     def close(self):
@@ -50,7 +60,8 @@ class GpuPool:
         return k, v
 
 
-def run_gpu(workload, want=None, free_order="default", on_result=None, pool_cb=None):
+def run_gpu(workload, want=None, free_order="default", on_result=None, pool_cb=None, ws_limits=None,
+            ws_bytes=None):
     """Execute the program; return {op index: (out, lse)} as numpy float32.
 
     ``want``: op indices whose outputs are copied back (None = all).
@@ -58,7 +69,7 @@ def run_gpu(workload, want=None, free_order="default", on_result=None, pool_cb=N
     """
     s = workload.shape
     order = workload.free_order() if isinstance(free_order, str) else free_order
-    gp = GpuPool(s, order)
+    gp = GpuPool(s, order, ws_limits=ws_limits, ws_bytes=ws_bytes)
     handles = {}
     results = {}
     try:

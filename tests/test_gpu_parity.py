@@ -79,13 +79,14 @@ def check_pool_contents(oracle_pool):
     return cb
 
 
-def parity(wl, want=None, check_pool=True, label=None):
+def parity(wl, want=None, check_pool=True, label=None, ws_limits=None, ws_bytes=None):
     from gpu_harness import run_gpu, log
     label = label or wl.name
     log(f"[gpu] parity {label}: oracle")
     exp, opool, _ = oracle_run(wl, want=want)
     log(f"[gpu] parity {label}: device run ({len(wl.ops)} ops)")
-    got = run_gpu(wl, want=set(exp), pool_cb=check_pool_contents(opool) if check_pool else None)
+    got = run_gpu(wl, want=set(exp), pool_cb=check_pool_contents(opool) if check_pool else None,
+                  ws_limits=ws_limits, ws_bytes=ws_bytes)
     agg = Agg()
     for idx in exp:
         agg.add(got[idx], exp[idx], f"{label} op {idx}")
