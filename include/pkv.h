@@ -266,6 +266,26 @@ pkv_status paged_attn_decode(pkv_pool* pool, int32_t layer, const int64_t* seqs,
                              float* out, float* lse, void* stream);
 
 /*
+ * paged_attn_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it):
+ * the same arguments, kernels and results, but the call's work lists and
+ * partial softmax states live in a file-scope device array of the library
+ * (32 MiB per device: 8 MiB of work lists, 24 MiB of partial states), held
+ * by each device the library runs on until the process ends.  The call
+ * allocates no device or pinned memory: it plans afresh each time (reusing
+ * the pool's host buffers), uploads the work lists from pageable host memory
+ * on `stream`, and launches.  A call whose work lists or partial states
+ * exceed the array even when planned coarse returns PKV_ERR_OOM before any
+ * work is enqueued.  Nothing in the array needs to start at zero (every
+ * partial state is written before it is read).  Every call on one device
+ * shares that device's array: calls that overlap on a device, from any pool
+ * or stream, race.  4-bit pools: PKV_ERR_UNSUPPORTED.  With kernel timing on
+ * (pkv_timing_enable) a call may create HIP events.
+ */
+pkv_status paged_attn_decode_scratch(pkv_pool* pool, int32_t layer, const int64_t* seqs, int32_t n_seqs,
+                                     const void* q, float sm_scale, float* out, float* lse, void* stream);
+
+/*
  * Draft-tree verify at one layer (CAST page, technical summary, "Problem":
  * the target model checks the draft tree's tokens in one pass; EAGLE-style
  * dynamic trees keep alternative branches).  For each sequence the last

@@ -10,6 +10,7 @@
 #include <climits>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -148,6 +149,10 @@ struct pkv_pool {
   PlanLayout dlayout;
   pkv::Plan vplan;
   PlanLayout vlayout;
+  // paged_attn_decode_scratch: its plan and the host copy it uploads from
+  pkv::Plan splan;
+  PlanLayout slayout;
+  std::vector<char> sstage;
   // prefill plan cache: the same call repeated at every layer of a step
   // (same sequences and counts, pool unchanged) reuses the uploaded plan
   bool pcache_valid = false;
@@ -340,30 +345,31 @@ pkv::PlanConfig coarse_config(const pkv::PlanConfig& cfg) {
 
 // Whether a plan's work lists fit `region` and its partial states the
 // partial-state region; always true for a pool that grows its own buffers.
-bool fits_workspace(const pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay, const DevBuf& region) {
-  if (!p->ws_fixed) return true;
-  return lay.total <= region.cap && partial_bytes(plan, p->core.shape()) <= p->partials.cap;
+bool fits_workspace(const pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay, const DevBuf& region,
+                    const DevBuf& parts) {
+  if (region.owned && parts.owned) return true;
+  return lay.total <= region.cap && partial_bytes(plan, p->core.shape()) <= parts.cap;
 }
 
 // Plans a call with the pool's settings and, when that plan does not fit a
 // caller workspace, once more with coarse_config; PKV_ERR_OOM if neither fits.
 template <class PlanWith>
-pkv_status plan_to_fit(pkv_pool* p, const DevBuf& region, const char* what, pkv::Plan* plan, PlanLayout* lay,
-                       PlanWith plan_with) {
+pkv_status plan_to_fit(pkv_pool* p, const DevBuf& region, const DevBuf& parts, const char* what, pkv::Plan* plan,
+                       PlanLayout* lay, PlanWith plan_with) {
   std::string why;
   pkv::Err e = plan_with(p->cfg, plan, &why);
   if (e != pkv::Err::ok) return fail(to_status(e), why);
   *lay = layout_of(*plan);
-  if (fits_workspace(p, *plan, *lay, region)) return PKV_OK;
+  if (fits_workspace(p, *plan, *lay, region, parts)) return PKV_OK;
   e = plan_with(coarse_config(p->cfg), plan, &why);
   if (e != pkv::Err::ok) return fail(to_status(e), why);
   *lay = layout_of(*plan);
-  if (fits_workspace(p, *plan, *lay, region)) return PKV_OK;
+  if (fits_workspace(p, *plan, *lay, region, parts)) return PKV_OK;
   return fail(PKV_ERR_OOM, std::string(what) + ": the call's work lists (" + std::to_string(lay->total) +
                                " bytes) or partial states (" +
                                std::to_string(partial_bytes(*plan, p->core.shape())) +
                                " bytes) do not fit the workspace regions (" + std::to_string(region.cap) +
-                               " and " + std::to_string(p->partials.cap) + " bytes)");
+                               " and " + std::to_string(parts.cap) + " bytes)");
 }
 
 // Every item must fit the tiles its kernel path assumes (LDS arrays, rows
@@ -420,13 +426,13 @@ bool plan_fits_kernels(const pkv::Plan& plan, const pkv::Shape& sh) {
 // With timing enabled, a pair of events takes the attention kernel's own
 // start and end.
 pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
-                          const DevBuf& buf, int32_t layer, const void* q, float sm_scale,
+                          const DevBuf& buf, DevBuf& parts, int32_t layer, const void* q, float sm_scale,
                           float* out, float* lse, hipStream_t stream) {
   const pkv::Shape& sh = p->core.shape();
   const char* base = static_cast<const char*>(buf.ptr);
-  pkv_status s = ensure(p, p->partials, partial_bytes(plan, sh), stream);
+  pkv_status s = ensure(p, parts, partial_bytes(plan, sh), stream);
   if (s != PKV_OK) return s;
-  float* part_o = static_cast<float*>(p->partials.ptr);
+  float* part_o = static_cast<float*>(parts.ptr);
   float* part_lse = part_o + static_cast<size_t>(plan.partial_rows) * sh.head_dim;
 
   if (plan.stride_mfma > pkv::kMaxItemBlocks || plan.stride_valu > pkv::kMaxItemBlocks ||
@@ -1027,7 +1033,7 @@ pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, in
   }
   if (!hit) {
     p->dcache_valid = false;
-    pkv_status s = plan_to_fit(p, p->decode_plan, "paged_attn_decode", &p->dplan, &p->dlayout,
+    pkv_status s = plan_to_fit(p, p->decode_plan, p->partials, "paged_attn_decode", &p->dplan, &p->dlayout,
                                [&](const pkv::PlanConfig& c, pkv::Plan* pl, std::string* why) {
                                  return pkv::plan_decode(p->core, seqs, n_seqs, c, pl, why);
                                });
@@ -1043,7 +1049,85 @@ pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, in
     p->dcache_version = p->core.version();
     p->dcache_valid = true;
   }
-  return launch_plan(p, p->dplan, p->dlayout, p->decode_plan, layer, q, sm_scale, out, lse, st);
+  return launch_plan(p, p->dplan, p->dlayout, p->decode_plan, p->partials, layer, q, sm_scale, out, lse, st);
+}
+
+}  // extern "C"
+
+// ---- decode without allocation -------------------------------------------
+//
+// paged_attn_decode_scratch keeps its work lists and partial states in one
+// file-scope device array instead of the pool's buffers.  In host code the
+// array's name stands for no device address: each device's copy is looked
+// up once (hipGetSymbolAddress, with that device current) and only that
+// address is handed to copies and kernels.
+namespace {
+
+constexpr size_t kScratchBytes = size_t{32} << 20;
+constexpr size_t kScratchPlanBytes = size_t{8} << 20;   // work lists; the rest holds partial states
+constexpr int kScratchDevices = 64;
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+char* g_scratch_addr[kScratchDevices] = {};
+
+// The address of `dev`'s copy of scratch; `dev` must be the current device.
+pkv_status scratch_address(int dev, char** out) {
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode_scratch: device index past the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PKV_ERR_HIP, std::string("paged_attn_decode_scratch: hipGetSymbolAddress: ") +
+                                   hipGetErrorString(e));
+    g_scratch_addr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_addr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attn_decode_scratch(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs,
+                                     const void* q, float sm_scale, float* out, float* lse, void* stream) {
+  if (!p) return fail(PKV_ERR_ARG, "paged_attn_decode_scratch: NULL pool");
+  if (!p->device) return fail(PKV_ERR_ARG, "paged_attn_decode_scratch: the pool has no device storage");
+  if (p->q4) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode_scratch: 4-bit pools are not supported");
+  if (n_seqs < 0) return fail(PKV_ERR_ARG, "paged_attn_decode_scratch: negative n_seqs");
+  if (n_seqs == 0) return PKV_OK;
+  if (!seqs || !q || !out) return fail(PKV_ERR_ARG, "paged_attn_decode_scratch: NULL seqs, q or out");
+  if (layer < 0 || layer >= p->core.shape().num_layers)
+    return fail(PKV_ERR_ARG, "paged_attn_decode_scratch: layer out of range");
+  if (!aligned16(q) || !aligned16(out))
+    return fail(PKV_ERR_ARG, "paged_attn_decode_scratch: q and out must be 16-byte aligned");
+  DeviceGuard g(p->dev);
+  PKV_HIP(g.err);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = nullptr;
+  pkv_status s = scratch_address(p->dev, &base);
+  if (s != PKV_OK) return s;
+  DevBuf lists{base, kScratchPlanBytes, false};
+  DevBuf parts{base + kScratchPlanBytes, kScratchBytes - kScratchPlanBytes, false};
+  // planned afresh each call (the array may hold another pool's lists),
+  // coarse when the pool's settings give more than the array holds
+  s = plan_to_fit(p, lists, parts, "paged_attn_decode_scratch", &p->splan, &p->slayout,
+                  [&](const pkv::PlanConfig& c, pkv::Plan* pl, std::string* why) {
+                    return pkv::plan_decode(p->core, seqs, n_seqs, c, pl, why);
+                  });
+  if (s != PKV_OK) return s;
+  if (!plan_fits_kernels(p->splan, p->core.shape()))
+    return fail(PKV_ERR_ARG, "paged_attn_decode_scratch: internal plan exceeds the kernels' tile limits");
+  // from pageable host memory: the runtime stages the copy itself
+  p->sstage.resize(p->slayout.total);
+  serialize(p->splan, p->slayout, p->sstage.data());
+  if (p->slayout.total > 0)
+    PKV_HIP(hipMemcpyAsync(lists.ptr, p->sstage.data(), p->slayout.total, hipMemcpyHostToDevice, st));
+  return launch_plan(p, p->splan, p->slayout, lists, parts, layer, q, sm_scale, out, lse, st);
 }
 
 pkv_status paged_attn_tree_verify(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs,
@@ -1062,7 +1146,7 @@ pkv_status paged_attn_tree_verify(pkv_pool* p, int32_t layer, const int64_t* seq
     return fail(PKV_ERR_ARG, "paged_attn_tree_verify: q and out must be 16-byte aligned");
   if (p->ws_fixed && (n_seqs > p->ws_max_seqs || n_nodes > p->ws_max_nodes))
     return fail(PKV_ERR_ARG, "paged_attn_tree_verify: more sequences or tree nodes than the workspace's limits");
-  pkv_status s = plan_to_fit(p, p->verify_plan, "paged_attn_tree_verify", &p->vplan, &p->vlayout,
+  pkv_status s = plan_to_fit(p, p->verify_plan, p->partials, "paged_attn_tree_verify", &p->vplan, &p->vlayout,
                              [&](const pkv::PlanConfig& c, pkv::Plan* pl, std::string* why) {
                                return pkv::plan_verify(p->core, seqs, n_seqs, n_nodes, parent, c, pl, why);
                              });
@@ -1077,7 +1161,7 @@ pkv_status paged_attn_tree_verify(pkv_pool* p, int32_t layer, const int64_t* seq
   s = upload(p, p->verify_plan, p->vlayout.total, st,
                         [&](char* dst) { serialize(p->vplan, p->vlayout, dst); });
   if (s != PKV_OK) return s;
-  return launch_plan(p, p->vplan, p->vlayout, p->verify_plan, layer, q, sm_scale, out, lse, st);
+  return launch_plan(p, p->vplan, p->vlayout, p->verify_plan, p->partials, layer, q, sm_scale, out, lse, st);
 }
 
 pkv_status paged_attn_prefill(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs,
@@ -1104,7 +1188,7 @@ pkv_status paged_attn_prefill(pkv_pool* p, int32_t layer, const int64_t* seqs, i
                    std::memcmp(p->pcache_new.data(), n_new, n_seqs * sizeof(int32_t)) == 0;
   if (!hit) {
     p->pcache_valid = false;
-    pkv_status s = plan_to_fit(p, p->prefill_plan, "paged_attn_prefill", &p->pplan, &p->playout,
+    pkv_status s = plan_to_fit(p, p->prefill_plan, p->partials, "paged_attn_prefill", &p->pplan, &p->playout,
                                [&](const pkv::PlanConfig& c, pkv::Plan* pl, std::string* why) {
                                  return pkv::plan_prefill(p->core, seqs, n_seqs, n_new, c, pl, why);
                                });
@@ -1130,7 +1214,7 @@ pkv_status paged_attn_prefill(pkv_pool* p, int32_t layer, const int64_t* seqs, i
     p->pcache_version = p->core.version();
     p->pcache_valid = true;
   }
-  return launch_plan(p, p->pplan, p->playout, p->prefill_plan, layer, q, sm_scale, out, lse, st);
+  return launch_plan(p, p->pplan, p->playout, p->prefill_plan, p->partials, layer, q, sm_scale, out, lse, st);
 }
 
 // ---- radix prefix cache --------------------------------------------------
