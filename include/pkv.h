@@ -266,6 +266,23 @@ pkv_status paged_attn_decode(pkv_pool* pool, int32_t layer, const int64_t* seqs,
                              float* out, float* lse, void* stream);
 
 /*
+ * paged_attn_decode over the consecutive layers layer0 .. layer0 +
+ * n_layers - 1 in one call, for schedules that hold the queries of several
+ * layers at once: layer l's queries at q + l * n_seqs * num_q_heads *
+ * head_dim (bf16 [n_layers][n_seqs][num_q_heads][head_dim]), its output and
+ * lse rows likewise ([n_layers][n_seqs][num_q_heads][head_dim] fp32,
+ * [n_layers][n_seqs][num_q_heads] or NULL).  One plan serves every layer
+ * (the layers share the block tables); a call of short queries (the direct
+ * plan) is ONE kernel launch over all its layers, other plans launch once
+ * per layer.  Results equal n_layers paged_attn_decode calls bit for bit.
+ * A layer range outside the pool: PKV_ERR_ARG; 4-bit pools:
+ * PKV_ERR_UNSUPPORTED; otherwise as paged_attn_decode.
+ */
+pkv_status paged_attn_decode_layers(pkv_pool* pool, int32_t layer0, int32_t n_layers, const int64_t* seqs,
+                                    int32_t n_seqs, const void* q, float sm_scale, float* out, float* lse,
+                                    void* stream);
+
+/*
  * paged_attn_decode for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid it):
  * the same arguments, kernels and results, but the call's work lists and

@@ -22,7 +22,7 @@ __all__ = [
     "PkvError", "PkvDesc", "load", "library_path",
     "kv_pool_bytes", "kv_workspace_bytes", "kv_workspace_layout", "kv_pool_create", "kv_pool_destroy", "kv_pool_q4_bytes", "kv_pool_create_q4",
     "seq_allocate", "seq_fork", "seq_free", "kv_append",
-    "paged_attn_decode", "paged_attn_decode_scratch", "paged_attn_tree_verify", "paged_attn_prefill", "kv_tree_commit",
+    "paged_attn_decode", "paged_attn_decode_layers", "paged_attn_decode_scratch", "paged_attn_tree_verify", "paged_attn_prefill", "kv_tree_commit",
     "seq_block_table", "block_refcount", "free_list", "kv_last_append",
     "paged_attn_decode_plan_stats", "paged_attn_verify_plan_stats", "paged_attn_prefill_plan_stats",
     "pkv_timing_enable", "pkv_timing_read", "pkv_last_error",
@@ -113,6 +113,7 @@ def load():
         "kv_append": (_I32, [_P, _PI64, _I32, _I32, _P, _P, _P]),
         "paged_attn_decode": (_I32, [_P, _I32, _PI64, _I32, _P, ctypes.c_float, _P, _P, _P]),
         "paged_attn_decode_scratch": (_I32, [_P, _I32, _PI64, _I32, _P, ctypes.c_float, _P, _P, _P]),
+        "paged_attn_decode_layers": (_I32, [_P, _I32, _I32, _PI64, _I32, _P, ctypes.c_float, _P, _P, _P]),
         "paged_attn_tree_verify": (_I32, [_P, _I32, _PI64, _I32, _I32, _PI32, _P,
                                           ctypes.c_float, _P, _P, _P]),
         "paged_attn_prefill": (_I32, [_P, _I32, _PI64, _I32, _PI32, _P, ctypes.c_float, _P, _P,
@@ -312,6 +313,14 @@ def paged_attn_decode(pool, layer, seqs, q, sm_scale, out, lse=None, stream=None
                                               _addr(out), _addr(lse), _stream(stream))
     if code != PKV_OK:
         _check(code)
+
+
+def paged_attn_decode_layers(pool, layer0, n_layers, seqs, q, sm_scale, out, lse=None, stream=None):
+    """Decode over layers layer0 .. layer0 + n_layers - 1 in one call: q
+    [n_layers][n][Hq][D] bf16, out [n_layers][n][Hq][D], lse [n_layers][n][Hq]."""
+    p, n = _seq_array(seqs)
+    _check(load().paged_attn_decode_layers(pool, int(layer0), int(n_layers), p, n, _addr(q), float(sm_scale),
+                                           _addr(out), _addr(lse), _stream(stream)))
 
 
 def paged_attn_decode_scratch(pool, layer, seqs, q, sm_scale, out, lse=None, stream=None):

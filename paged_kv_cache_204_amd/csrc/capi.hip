@@ -427,8 +427,20 @@ bool plan_fits_kernels(const pkv::Plan& plan, const pkv::Shape& sh) {
 // start and end.
 pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
                           const DevBuf& buf, DevBuf& parts, int32_t layer, const void* q, float sm_scale,
-                          float* out, float* lse, hipStream_t stream) {
+                          float* out, float* lse, hipStream_t stream, int32_t n_layers = 1,
+                          int64_t layer_rows = 0) {
   const pkv::Shape& sh = p->core.shape();
+  if (n_layers > 1 && plan.direct.empty()) {
+    // the plan's launches once per layer (partial states reused in stream order)
+    for (int32_t l = 0; l < n_layers; ++l) {
+      const size_t rows = static_cast<size_t>(layer_rows) * l;
+      pkv_status s = launch_plan(p, plan, lay, buf, parts, layer + l,
+                                 static_cast<const uint16_t*>(q) + rows * sh.head_dim, sm_scale,
+                                 out + rows * sh.head_dim, lse ? lse + rows : nullptr, stream);
+      if (s != PKV_OK) return s;
+    }
+    return PKV_OK;
+  }
   const char* base = static_cast<const char*>(buf.ptr);
   pkv_status s = ensure(p, parts, partial_bytes(plan, sh), stream);
   if (s != PKV_OK) return s;
@@ -502,8 +514,10 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
   else {
     int32_t max_tok = 0;
     for (const pkv::WorkItem& it : plan.direct) max_tok = std::max(max_tok, it.n_tok);
+    ap.layer_chunks = static_cast<uint64_t>(sh.num_blocks) * sh.num_kv_heads * sh.block_size * sh.head_dim / 8;
+    ap.layer_rows = static_cast<uint64_t>(layer_rows);
     PKV_HIP(pkv::launch_direct(ap, static_cast<int32_t>(plan.direct.size()), sh.head_dim,
-                                plan.stride_direct, max_tok, stream, ev_a, ev_b));
+                                plan.stride_direct, max_tok, stream, ev_a, ev_b, n_layers));
   }
   if (timed) p->ev_pending.emplace_back(ev_a, ev_b);
   if (!plan.merges.empty()) {
@@ -996,23 +1010,13 @@ pkv_status decode_q4(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_
 
 }  // namespace
 
-pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs,
-                             const void* q, float sm_scale, float* out, float* lse, void* stream) {
-  if (!p) return fail(PKV_ERR_ARG, "paged_attn_decode: NULL pool");
-  if (!p->device) return fail(PKV_ERR_ARG, "paged_attn_decode: the pool has no device storage");
-  if (n_seqs < 0) return fail(PKV_ERR_ARG, "paged_attn_decode: negative n_seqs");
-  if (n_seqs == 0) return PKV_OK;
-  if (!seqs || !q || !out) return fail(PKV_ERR_ARG, "paged_attn_decode: NULL seqs, q or out");
-  if (layer < 0 || layer >= p->core.shape().num_layers)
-    return fail(PKV_ERR_ARG, "paged_attn_decode: layer out of range");
-  if (!aligned16(q) || !aligned16(out))
-    return fail(PKV_ERR_ARG, "paged_attn_decode: q and out must be 16-byte aligned");
-  if (p->ws_fixed && n_seqs > p->ws_max_seqs)
-    return fail(PKV_ERR_ARG, "paged_attn_decode: more sequences than the workspace's max_seqs");
-  if (p->q4) return decode_q4(p, layer, seqs, n_seqs, q, sm_scale, out, lse, stream);
-  DeviceGuard g(p->dev);
-  PKV_HIP(g.err);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+// The decode plan of a call -- the cached one, patched, or made afresh and
+// fitted to the workspace -- uploaded to the pool's decode region on `st`.
+pkv_status decode_prepare(pkv_pool* p, const int64_t* seqs, int32_t n_seqs, hipStream_t st) {
   const bool same_seqs = p->dcache_valid && p->dcache_seqs.size() == static_cast<size_t>(n_seqs) &&
                          std::memcmp(p->dcache_seqs.data(), seqs, n_seqs * sizeof(int64_t)) == 0;
   bool hit = same_seqs && p->dcache_version == p->core.version();
@@ -1049,7 +1053,58 @@ pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, in
     p->dcache_version = p->core.version();
     p->dcache_valid = true;
   }
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attn_decode(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs,
+                             const void* q, float sm_scale, float* out, float* lse, void* stream) {
+  if (!p) return fail(PKV_ERR_ARG, "paged_attn_decode: NULL pool");
+  if (!p->device) return fail(PKV_ERR_ARG, "paged_attn_decode: the pool has no device storage");
+  if (n_seqs < 0) return fail(PKV_ERR_ARG, "paged_attn_decode: negative n_seqs");
+  if (n_seqs == 0) return PKV_OK;
+  if (!seqs || !q || !out) return fail(PKV_ERR_ARG, "paged_attn_decode: NULL seqs, q or out");
+  if (layer < 0 || layer >= p->core.shape().num_layers)
+    return fail(PKV_ERR_ARG, "paged_attn_decode: layer out of range");
+  if (!aligned16(q) || !aligned16(out))
+    return fail(PKV_ERR_ARG, "paged_attn_decode: q and out must be 16-byte aligned");
+  if (p->ws_fixed && n_seqs > p->ws_max_seqs)
+    return fail(PKV_ERR_ARG, "paged_attn_decode: more sequences than the workspace's max_seqs");
+  if (p->q4) return decode_q4(p, layer, seqs, n_seqs, q, sm_scale, out, lse, stream);
+  DeviceGuard g(p->dev);
+  PKV_HIP(g.err);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  pkv_status s = decode_prepare(p, seqs, n_seqs, st);
+  if (s != PKV_OK) return s;
   return launch_plan(p, p->dplan, p->dlayout, p->decode_plan, p->partials, layer, q, sm_scale, out, lse, st);
+}
+
+pkv_status paged_attn_decode_layers(pkv_pool* p, int32_t layer0, int32_t n_layers, const int64_t* seqs,
+                                    int32_t n_seqs, const void* q, float sm_scale, float* out, float* lse,
+                                    void* stream) {
+  if (!p) return fail(PKV_ERR_ARG, "paged_attn_decode_layers: NULL pool");
+  if (!p->device) return fail(PKV_ERR_ARG, "paged_attn_decode_layers: the pool has no device storage");
+  if (p->q4) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode_layers: 4-bit pools are not supported");
+  if (n_seqs < 0) return fail(PKV_ERR_ARG, "paged_attn_decode_layers: negative n_seqs");
+  if (layer0 < 0 || n_layers < 1 || n_layers > 65535 ||
+      static_cast<int64_t>(layer0) + n_layers > p->core.shape().num_layers)
+    return fail(PKV_ERR_ARG, "paged_attn_decode_layers: layer range outside the pool's layers");
+  if (n_seqs == 0) return PKV_OK;
+  if (!seqs || !q || !out) return fail(PKV_ERR_ARG, "paged_attn_decode_layers: NULL seqs, q or out");
+  if (!aligned16(q) || !aligned16(out))
+    return fail(PKV_ERR_ARG, "paged_attn_decode_layers: q and out must be 16-byte aligned");
+  if (p->ws_fixed && n_seqs > p->ws_max_seqs)
+    return fail(PKV_ERR_ARG, "paged_attn_decode_layers: more sequences than the workspace's max_seqs");
+  DeviceGuard g(p->dev);
+  PKV_HIP(g.err);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  pkv_status s = decode_prepare(p, seqs, n_seqs, st);
+  if (s != PKV_OK) return s;
+  return launch_plan(p, p->dplan, p->dlayout, p->decode_plan, p->partials, layer0, q, sm_scale, out, lse, st,
+                     n_layers, static_cast<int64_t>(n_seqs) * p->core.shape().num_q_heads);
 }
 
 }  // extern "C"

@@ -49,6 +49,10 @@ struct AttnParams {
   // queries' partial states
   const PathStep* steps;
   const MergeRow* merges;
+  // direct launches over several layers: one layer of a pool in 16-byte
+  // chunks, and the query (out) rows of one layer (queries x Hq)
+  uint64_t layer_chunks;
+  uint64_t layer_rows;
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
@@ -143,9 +147,12 @@ hipError_t launch_path(const AttnParams& p, const PathItem* items, int32_t n_ite
 // over all of its keys (n_grp 1, tail_start INT_MAX), written straight to
 // out / lse; items[i]'s block list at blocks + i * stride (<= kMaxItemBlocks).
 // max_tok: the largest n_tok of the items (it picks the kernel's form).
+// n_layers > 1: the same items over layers p.layer .. p.layer + n_layers - 1
+// in one launch (grid z), layer z's q / out / lse rows at z * p.layer_rows
+// and its pool data at z * p.layer_chunks past layer p.layer's.
 hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
                          int32_t max_tok, hipStream_t s, hipEvent_t ev_start = nullptr,
-                         hipEvent_t ev_stop = nullptr);
+                         hipEvent_t ev_stop = nullptr, int32_t n_layers = 1);
 
 // Log-sum-exp merge of the partial states of several work items.
 struct MergeParams {

@@ -726,7 +726,11 @@ struct DirectSmemAll {
 // loads of all of its steps at once -- K into registers, then V by LDS DMA
 // into DEPTH tiles of its own -- so the call waits for one memory round
 // trip, not one per DEPTH steps; V then costs no registers.
-template <int D, int W, int DEPTH, bool ALL>
+//
+// LAYERS: grid.z runs over consecutive layers of one call (the same items
+// and block lists); workgroup z reads layer p.layer + z of the pools, its
+// query rows and writes its out / lse rows at z times the layer's row count.
+template <int D, int W, int DEPTH, bool ALL, bool LAYERS>
 __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restrict__ items,
                                                           const int32_t* __restrict__ blocks,
                                                           const uint16_t* __restrict__ q,
@@ -759,6 +763,16 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
   const int n_tok = items[item].n_tok;
   const int q_index = items[item].q_index[0];
   const int bmask = (1 << log2B) - 1;
+  float* out_rows = p.out;
+  float* lse_rows = p.lse;
+  if constexpr (LAYERS) {
+    const size_t z = blockIdx.z;
+    k_layer += z * p.layer_chunks;
+    v_layer += z * p.layer_chunks;
+    q += z * p.layer_rows * D;
+    out_rows += z * p.layer_rows * D;
+    if (lse_rows) lse_rows += z * p.layer_rows;
+  }
   const uint4* kb = k_layer + ((static_cast<size_t>(h) * (D / 8)) << log2B);
   const uint4* vb = v_layer + ((static_cast<size_t>(h) * (D / 8)) << log2B);
   const int lane = tid & 63;
@@ -936,8 +950,8 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
       l = fmaf(a, sm.fin.l[w][row], l);
       acc = fmaf(a, sm.fin.o[w][row][c], acc);
     }
-    p.out[(row0 + row) * D + c] = acc / l;
-    if (c == 0 && p.lse) p.lse[row0 + row] = (mx + log2f(l)) * kLn2;
+    out_rows[(row0 + row) * D + c] = acc / l;
+    if (c == 0 && lse_rows) lse_rows[row0 + row] = (mx + log2f(l)) * kLn2;
   }
 }
 
@@ -978,14 +992,9 @@ hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, i
 }
 
 
-hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
-                         int32_t max_tok, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
-  if (n_items == 0) return hipSuccess;
-  if (stride < 1 || stride > kMaxItemBlocks || p.G > 16) return hipErrorInvalidValue;
-  const int64_t n_wg = static_cast<int64_t>(n_items) * p.Hkv;
-  if (n_wg > INT32_MAX) return hipErrorInvalidValue;
-  if (n_items > 65535) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<uint32_t>(p.Hkv), static_cast<uint32_t>(n_items));
+template <bool LAYERS>
+hipError_t launch_direct_t(const AttnParams& p, dim3 grid, int32_t head_dim, int32_t stride, int32_t max_tok,
+                           hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const uint4* kl = layer_head_base(p, p.k_pool, 0, head_dim);
   const uint4* vl = layer_head_base(p, p.v_pool, 0, head_dim);
   const uint32_t blk_chunks = static_cast<uint32_t>(p.Hkv * p.B * head_dim / 8);
@@ -995,17 +1004,30 @@ hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim,
   // of at most 3 steps per wave (768 keys) load everything in one round.
   constexpr int kAllSteps = 3;
   if (head_dim == 64 && max_tok <= kAllSteps * 8 * kStep)
-    hipExtLaunchKernelGGL((direct_kernel<64, 8, kAllSteps, true>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p.items,
-                          p.blocks, p.q, stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
+    hipExtLaunchKernelGGL((direct_kernel<64, 8, kAllSteps, true, LAYERS>), grid, dim3(512), 0, s, ev_start, ev_stop, 0,
+                          p.items, p.blocks, p.q, stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
   else if (head_dim == 64)
-    hipExtLaunchKernelGGL((direct_kernel<64, 8, 2, false>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p.items, p.blocks,
-                          p.q, stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
-  else if (head_dim == 128)
-    hipExtLaunchKernelGGL((direct_kernel<128, 4, 2, false>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, p.items,
+    hipExtLaunchKernelGGL((direct_kernel<64, 8, 2, false, LAYERS>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p.items,
                           p.blocks, p.q, stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
+  else if (head_dim == 128)
+    hipExtLaunchKernelGGL((direct_kernel<128, 4, 2, false, LAYERS>), grid, dim3(256), 0, s, ev_start, ev_stop, 0,
+                          p.items, p.blocks, p.q, stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_direct(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
+                         int32_t max_tok, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop, int32_t n_layers) {
+  if (n_items == 0) return hipSuccess;
+  if (stride < 1 || stride > kMaxItemBlocks || p.G > 16 || n_layers < 1 || n_layers > 65535)
+    return hipErrorInvalidValue;
+  const int64_t n_wg = static_cast<int64_t>(n_items) * p.Hkv * n_layers;
+  if (n_wg > INT32_MAX) return hipErrorInvalidValue;
+  if (n_items > 65535) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(p.Hkv), static_cast<uint32_t>(n_items), static_cast<uint32_t>(n_layers));
+  return n_layers > 1 ? launch_direct_t<true>(p, grid, head_dim, stride, max_tok, s, ev_start, ev_stop)
+                      : launch_direct_t<false>(p, grid, head_dim, stride, max_tok, s, ev_start, ev_stop);
 }
 
 }  // namespace pkv
