@@ -37,20 +37,17 @@ constexpr int kPathThreads = 64 * kPathWaves;
 constexpr int kPathTiles = kPathMaxRows / 16;
 constexpr float kPathLoShare = 16.f;   // residual term while a weight exceeds sum / 16
 
+// A wave's K and V tiles (32 tokens x D bf16 each) hold exactly its final
+// state (32 rows x D fp32), which it writes there after its last step.
 template <int D>
-struct PathFin {
-  float o[kPathWaves][kPathMaxRows][D];   // each wave's unnormalised state (swizzled columns)
+struct PathSmem {
+  char slot[kPathWaves][2][kStep * D * 2];   // [wave][K, V]: the wave's step, then its state
   float m[kPathWaves][kPathMaxRows];
   float l[kPathWaves][kPathMaxRows];
-  float wgt[kPathMaxRows][kPathWaves + kPathMaxParts];   // each row's state weights
 };
-template <int D>
-union PathSmem {
-  char slot[kPathWaves][2][kStep * D * 2];   // [wave][K, V]: the wave's step
-  PathFin<D> fin;
-};
+static_assert(2 * kStep * 2 == kPathMaxRows * 4, "a wave's state fills its two tiles");
 
-// column c (a multiple of 4) of row r in PathFin::o: 16-byte groups rotated
+// column c (a multiple of 4) of row r in a wave's state: 16-byte groups rotated
 // by the row, so a wave's stores of 16 rows spread over the banks
 __device__ __forceinline__ int fin_col(int r, int c) { return c ^ ((r & 7) << 2); }
 
@@ -142,6 +139,18 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const PathItem* __re
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) qf[j][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
+  }
+  // The rows this thread combines at the end (the units of the final pass):
+  // their queries and merge rows, read now so that their latency passes
+  // under the steps.
+  constexpr int NU = (kPathMaxRows * Q4 + kPathThreads - 1) / kPathThreads;
+  int u_merge[NU], u_qrow[NU];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int row = (tid + kPathThreads * i) / Q4;
+    const int qj = row < R ? row / G : 0;
+    u_merge[i] = row < R ? it.merge[qj] : -1;
+    u_qrow[i] = it.q_index[qj];
   }
   // the compiler's wait for the query operands lands here
 #pragma unroll
@@ -289,84 +298,84 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const PathItem* __re
   wait_vmcnt<0>();
 
   // ---- the eight waves' states, then the queries' partial states ----
-  lds_barrier();   // every wave is done with its slots (aliased below)
+  // this wave's tiles are free: its loads have landed (above) and its LDS
+  // reads have returned
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  float* fo = reinterpret_cast<float*>(sm.slot[wave][0]);
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int r = 16 * j + l16;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
-      *reinterpret_cast<float4*>(&sm.fin.o[wave][r][fin_col(r, 16 * dt + 4 * g4)]) =
+      *reinterpret_cast<float4*>(&fo[r * D + fin_col(r, 16 * dt + 4 * g4)]) =
           make_float4(o[j][dt][0], o[j][dt][1], o[j][dt][2], o[j][dt][3]);
     if (g4 == 0) {
-      sm.fin.m[wave][r] = m_run[j];
-      sm.fin.l[wave][r] = o[j][ND][0];
+      sm.m[wave][r] = m_run[j];
+      sm.l[wave][r] = o[j][ND][0];
     }
   }
   lds_barrier();
-  // one thread per row: the common max and every state's normalised weight
-  if (tid < R) {
-    const int row = tid;
-    const int mi = it.merge[row / G];
+  // Four consecutive dims of one row per thread and unit: the row's common
+  // max over the waves' states and its partial states, their weights, and
+  // the weighted sum.  The thread of a row's first unit writes its lse.
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int u = tid + kPathThreads * i;
+    if (u >= R * Q4) break;
+    const int row = u / Q4;
+    const int c = (u % Q4) * 4;
+    const int mi = u_merge[i];
     const int np = mi >= 0 ? p.merges[mi].n_parts : 0;
+    const int hq = h * G + row % G;
     float lk[kPathMaxParts];
 #pragma unroll
     for (int k = 0; k < kPathMaxParts; ++k)
-      lk[k] = k < np ? p.part_lse[static_cast<size_t>(p.merges[mi].inl[k]) + h * G + row % G] : -INFINITY;
+      lk[k] = k < np ? p.part_lse[static_cast<size_t>(p.merges[mi].inl[k]) + hq] : -INFINITY;
+    float mw[kPathWaves], lw[kPathWaves];
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kPathWaves; ++w)
-      if (sm.fin.l[w][row] > 0.f) mx = fmaxf(mx, sm.fin.m[w][row]);
+    for (int w = 0; w < kPathWaves; ++w) {
+      mw[w] = sm.m[w][row];
+      lw[w] = sm.l[w][row];
+      if (lw[w] > 0.f) mx = fmaxf(mx, mw[w]);
+    }
 #pragma unroll
     for (int k = 0; k < kPathMaxParts; ++k) mx = fmaxf(mx, lk[k]);
-    float aw[kPathWaves], ak[kPathMaxParts];
     float l = 0.f;
 #pragma unroll
     for (int w = 0; w < kPathWaves; ++w) {
-      const float lw = sm.fin.l[w][row];
-      aw[w] = lw > 0.f ? fast_exp2(sm.fin.m[w][row] - mx) : 0.f;
-      l = fmaf(aw[w], lw, l);
+      mw[w] = lw[w] > 0.f ? fast_exp2(mw[w] - mx) : 0.f;   // the wave state's scale
+      l = fmaf(mw[w], lw[w], l);
     }
 #pragma unroll
     for (int k = 0; k < kPathMaxParts; ++k) {
-      ak[k] = lk[k] == -INFINITY ? 0.f : fast_exp2(lk[k] - mx);
-      l += ak[k];
+      lk[k] = lk[k] == -INFINITY ? 0.f : fast_exp2(lk[k] - mx);   // the partial state's weight
+      l += lk[k];
     }
     const float inv = 1.f / l;
-#pragma unroll
-    for (int w = 0; w < kPathWaves; ++w) sm.fin.wgt[row][w] = aw[w] * inv;
-#pragma unroll
-    for (int k = 0; k < kPathMaxParts; ++k) sm.fin.wgt[row][kPathWaves + k] = ak[k] * inv;
-    const size_t orow = static_cast<size_t>(it.q_index[row / G]) * p.Hq + h * G + row % G;
-    if (p.lse) p.lse[orow] = (mx + log2f(l)) * kLn2;
-  }
-  lds_barrier();
-  // four consecutive dims of one row per thread and unit
-  for (int u = tid; u < R * Q4; u += kPathThreads) {
-    const int row = u / Q4;
-    const int c = (u % Q4) * 4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < kPathWaves; ++w) {
-      const float a = sm.fin.wgt[row][w];
-      const float4 x = *reinterpret_cast<const float4*>(&sm.fin.o[w][row][fin_col(row, c)]);
+      const float a = mw[w] * inv;
+      const float4 x =
+          *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sm.slot[w][0]) + row * D + fin_col(row, c));
       acc.x = fmaf(a, x.x, acc.x);
       acc.y = fmaf(a, x.y, acc.y);
       acc.z = fmaf(a, x.z, acc.z);
       acc.w = fmaf(a, x.w, acc.w);
     }
-    const int mi = it.merge[row / G];
-    const int np = mi >= 0 ? p.merges[mi].n_parts : 0;
     for (int k = 0; k < np; ++k) {
-      const float a = sm.fin.wgt[row][kPathWaves + k];
+      const float a = lk[k] * inv;
       const float4 y = *reinterpret_cast<const float4*>(
-          p.part_o + (static_cast<size_t>(p.merges[mi].inl[k]) + h * G + row % G) * D + c);
+          p.part_o + (static_cast<size_t>(p.merges[mi].inl[k]) + hq) * D + c);
       acc.x = fmaf(a, y.x, acc.x);
       acc.y = fmaf(a, y.y, acc.y);
       acc.z = fmaf(a, y.z, acc.z);
       acc.w = fmaf(a, y.w, acc.w);
     }
-    const size_t orow = static_cast<size_t>(it.q_index[row / G]) * p.Hq + h * G + row % G;
+    const size_t orow = static_cast<size_t>(u_qrow[i]) * p.Hq + hq;
     *reinterpret_cast<float4*>(p.out + orow * D + c) = acc;
+    if (c == 0 && p.lse) p.lse[orow] = (mx + log2f(l)) * kLn2;
   }
 }
 
