@@ -149,6 +149,13 @@ struct pkv_pool {
   PlanLayout dlayout;
   pkv::Plan vplan;
   PlanLayout vlayout;
+  // verify plan cache: the same tree over the same sequences on an
+  // unchanged pool (every layer of one verify step) reuses the uploaded plan
+  bool vcache_valid = false;
+  uint64_t vcache_version = 0;
+  int32_t vcache_nodes = 0;
+  std::vector<int64_t> vcache_seqs;
+  std::vector<int32_t> vcache_parent;
   // paged_attn_decode_scratch: its plan and the host copy it uploads from
   pkv::Plan splan;
   PlanLayout slayout;
@@ -1201,21 +1208,34 @@ pkv_status paged_attn_tree_verify(pkv_pool* p, int32_t layer, const int64_t* seq
     return fail(PKV_ERR_ARG, "paged_attn_tree_verify: q and out must be 16-byte aligned");
   if (p->ws_fixed && (n_seqs > p->ws_max_seqs || n_nodes > p->ws_max_nodes))
     return fail(PKV_ERR_ARG, "paged_attn_tree_verify: more sequences or tree nodes than the workspace's limits");
-  pkv_status s = plan_to_fit(p, p->verify_plan, p->partials, "paged_attn_tree_verify", &p->vplan, &p->vlayout,
-                             [&](const pkv::PlanConfig& c, pkv::Plan* pl, std::string* why) {
-                               return pkv::plan_verify(p->core, seqs, n_seqs, n_nodes, parent, c, pl, why);
-                             });
-  if (s != PKV_OK) return s;
+  const size_t n_par = static_cast<size_t>(n_seqs) * (n_nodes > 0 ? n_nodes : 0);
+  const bool hit = p->vcache_valid && p->vcache_version == p->core.version() && p->vcache_nodes == n_nodes &&
+                   p->vcache_seqs.size() == static_cast<size_t>(n_seqs) &&
+                   std::memcmp(p->vcache_seqs.data(), seqs, n_seqs * sizeof(int64_t)) == 0 &&
+                   std::memcmp(p->vcache_parent.data(), parent, n_par * sizeof(int32_t)) == 0;
   DeviceGuard g(p->dev);
   PKV_HIP(g.err);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (!plan_fits_kernels(p->vplan, p->core.shape()))
-    return fail(PKV_ERR_ARG, "paged_attn_tree_verify: internal plan exceeds the kernels' tile limits");
-  s = ensure(p, p->partials, partial_bytes(p->vplan, p->core.shape()), st);
-  if (s != PKV_OK) return s;
-  s = upload(p, p->verify_plan, p->vlayout.total, st,
-                        [&](char* dst) { serialize(p->vplan, p->vlayout, dst); });
-  if (s != PKV_OK) return s;
+  if (!hit) {
+    p->vcache_valid = false;
+    pkv_status s = plan_to_fit(p, p->verify_plan, p->partials, "paged_attn_tree_verify", &p->vplan, &p->vlayout,
+                               [&](const pkv::PlanConfig& c, pkv::Plan* pl, std::string* why) {
+                                 return pkv::plan_verify(p->core, seqs, n_seqs, n_nodes, parent, c, pl, why);
+                               });
+    if (s != PKV_OK) return s;
+    if (!plan_fits_kernels(p->vplan, p->core.shape()))
+      return fail(PKV_ERR_ARG, "paged_attn_tree_verify: internal plan exceeds the kernels' tile limits");
+    s = ensure(p, p->partials, partial_bytes(p->vplan, p->core.shape()), st);
+    if (s != PKV_OK) return s;
+    s = upload(p, p->verify_plan, p->vlayout.total, st,
+               [&](char* dst) { serialize(p->vplan, p->vlayout, dst); });
+    if (s != PKV_OK) return s;
+    p->vcache_seqs.assign(seqs, seqs + n_seqs);
+    p->vcache_parent.assign(parent, parent + n_par);
+    p->vcache_nodes = n_nodes;
+    p->vcache_version = p->core.version();
+    p->vcache_valid = true;
+  }
   return launch_plan(p, p->vplan, p->vlayout, p->verify_plan, p->partials, layer, q, sm_scale, out, lse, st);
 }
 
