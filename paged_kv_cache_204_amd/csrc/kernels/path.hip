@@ -84,22 +84,44 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const PathItem* __re
   const int mine = wave < n_steps ? (n_steps - 1 - wave) / kPathWaves + 1 : 0;   // this wave's steps
 
   // K (V) of a step into the wave's K (V) tile: run u fills chunk slot
-  // c = 64 u + lane, row c / CPR, chunk (c % CPR) ^ tile_swz(row).  Tokens
-  // past the step's count re-read its last token (masked below), so every
-  // run stays in the pool.
+  // c = 64 u + lane, row c / CPR, chunk (c % CPR) ^ tile_swz(row).  A full
+  // step (32 tokens) reads each lane's chunk at a fixed byte offset from its
+  // block's base (its slot within the block: the row, past the step's first
+  // slot); run u reads the step's first block when u < CPR / 4 (rows 0..15)
+  // and its second otherwise.  A shorter step re-reads its last token in
+  // the rows past its count (masked below), so every run stays in written
+  // slots of the pool.
+  uint32_t lane_off[RUNS];
+#pragma unroll
+  for (int u = 0; u < RUNS; ++u) {
+    const int c = u * 64 + lane;
+    const int r = c / CPR;
+    const int ch = (c % CPR) ^ tile_swz<D>(r);
+    lane_off[u] = static_cast<uint32_t>(((p.B == 16 ? (r & 15) : r) * CPR + ch) * 16);
+  }
   auto issue = [&](const PathStep& ps, int kv) __attribute__((always_inline)) {
     const int off = ps.meta & 0xFF;
-    const int last = ((ps.meta >> 8) & 0xFF) - 1;
+    const int n_tok = (ps.meta >> 8) & 0xFF;
     char* dst = sm.slot[wave][kv];
     const uint4* src = kv ? vb : kb;
+    if (n_tok == kStep) {
+      const char* at_a = reinterpret_cast<const char*>(
+          src + static_cast<uint64_t>(static_cast<uint32_t>(ps.blk_a)) * blk_chunks + off * CPR);
+      const char* at_b = reinterpret_cast<const char*>(
+          src + static_cast<uint64_t>(static_cast<uint32_t>(ps.blk_b)) * blk_chunks + off * CPR);
 #pragma unroll
-    for (int u = 0; u < RUNS; ++u) {
-      const int c = u * 64 + lane;
-      const int r = c / CPR;
-      const int ch = (c % CPR) ^ tile_swz<D>(r);
-      const int t = min(r, last);
-      const int blk = t < 16 ? ps.blk_a : ps.blk_b;
-      lds_dma16(src + chunk_index(blk, blk_chunks, ((off + t) & bmask) * CPR + ch), dst + u * 1024);
+      for (int u = 0; u < RUNS; ++u) lds_dma16_at(u < CPR / 4 ? at_a : at_b, lane_off[u], dst + u * 1024);
+    } else {
+      const int last = n_tok - 1;
+#pragma unroll
+      for (int u = 0; u < RUNS; ++u) {
+        const int c = u * 64 + lane;
+        const int r = c / CPR;
+        const int ch = (c % CPR) ^ tile_swz<D>(r);
+        const int t = min(r, last);
+        const int blk = t < 16 ? ps.blk_a : ps.blk_b;
+        lds_dma16(src + chunk_index(blk, blk_chunks, ((off + t) & bmask) * CPR + ch), dst + u * 1024);
+      }
     }
   };
 

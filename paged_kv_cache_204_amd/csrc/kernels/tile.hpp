@@ -68,6 +68,19 @@ __device__ __forceinline__ void lds_dma16(const uint4* src, const void* lds) {
       : "memory");
 }
 
+// The same copy from a wave-uniform base address plus a 32-bit per-lane
+// byte offset (the SGPR-base form of the instruction): no 64-bit address
+// arithmetic per lane.
+__device__ __forceinline__ void lds_dma16_at(const void* base, uint32_t off, const void* lds) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_ptr)(lds)));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(m0)
+      : "memory");
+}
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // i % 4 of the 4-element rows named by lanes 4k + i / 4, for k = 0..3.
 __device__ __forceinline__ v4i16 lds_read_tr16(const void* at) {
