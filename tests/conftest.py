@@ -1,3 +1,4 @@
+import json
 import os
 import sys
 
@@ -19,6 +20,34 @@ def gpu_available():
         return torch.cuda.is_available()
     except Exception:  # pragma: no cover
         return False
+
+
+# Worst-case parity margins of the GPU tests that ran, per case: written at
+# the end of the session to $PKV_PARITY_MARGINS (default
+# profiles/parity_margins.json) with the tolerances they were held to.
+MARGINS = {}
+
+
+def record_margin(label, max_abs, mean_abs, n, tol_max, tol_mean):
+    MARGINS[label] = {"max_abs": float(max_abs), "mean_abs": float(mean_abs), "elements": int(n),
+                      "tol_max": tol_max, "tol_mean": tol_mean}
+
+
+def pytest_sessionfinish(session, exitstatus):
+    if not MARGINS:
+        return
+    path = os.environ.get("PKV_PARITY_MARGINS", os.path.join(ROOT, "profiles", "parity_margins.json"))
+    worst = max(MARGINS.values(), key=lambda m: m["max_abs"] / m["tol_max"])
+    doc = {"cases": dict(sorted(MARGINS.items())),
+           "worst_max_abs": max(m["max_abs"] for m in MARGINS.values()),
+           "worst_mean_abs": max(m["mean_abs"] for m in MARGINS.values()),
+           "worst_case_by_tolerance": [k for k, v in MARGINS.items() if v is worst][0],
+           "tests_exit_status": int(exitstatus)}
+    try:
+        with open(path, "w") as f:
+            json.dump(doc, f, indent=1)
+    except OSError:
+        pass
 
 
 @pytest.fixture(scope="session")

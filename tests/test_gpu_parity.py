@@ -58,6 +58,8 @@ class Agg:
         assert self.n > 0
         mean = self.sum / self.n
         print(f"[parity] {label}: max |d| {self.max:.3e} mean |d| {mean:.3e}", flush=True)
+        from conftest import record_margin
+        record_margin(label, self.max, mean, self.n, TOL_MAX, TOL_MEAN)
         assert mean <= TOL_MEAN, f"{label}: mean |d| {mean:.3e}"
         return mean
 

@@ -152,6 +152,8 @@ def test_q4_pool_contents_and_decode_parity(dev, case):
         tot += d.sum()
         cnt += d.size
     print(f"[parity] {name}: max |d| {worst:.3e} mean |d| {tot / cnt:.3e}", flush=True)
+    from conftest import record_margin
+    record_margin(name, worst, tot / cnt, cnt, TOL_MAX, TOL_MEAN)
     assert tot / cnt <= TOL_MEAN
 
 
