@@ -37,11 +37,13 @@ def test_traffic_summary_scales_by_the_copy_and_tracks_the_kernel_source(tmp_pat
                     [("void pkv::attn_kernel<64, 1, 8>(...)", 100.0),
                      ("void pkv::attn_kernel<64, 1, 8>(...)", 300.0),
                      ("pkv::merge_kernel(...)", 999.0),
-                     ("at::native::copy_kernel", calib_kib / 2)])
+                     ("at::native::reduce_kernel<512, 1>(...)", calib_kib * 2),
+                     ("__amd_rocclr_copyBuffer", calib_kib / 2)])
     _write_counters(tmp_path / "w", "WRITE_SIZE",
                     [("void pkv::attn_kernel<64, 1, 8>(...)", 50.0),
                      ("void pkv::attn_kernel<64, 1, 8>(...)", 50.0),
-                     ("at::native::copy_kernel", calib_kib)])
+                     ("at::native::vectorized_elementwise_kernel<4, FillFunctor>", calib_kib * 4),
+                     ("__amd_rocclr_copyBuffer", calib_kib)])
     out = tmp_path / "t.json"
     res = bench.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "c2_trellis")
     assert abs(res["fetch"]["scale"] - 2.0) < 1e-12 and abs(res["write"]["scale"] - 1.0) < 1e-12
@@ -55,13 +57,15 @@ def test_traffic_summary_scales_by_the_copy_and_tracks_the_kernel_source(tmp_pat
 
 def test_traffic_summary_takes_the_direct_kernel(tmp_path):
     calib_kib = bench.CALIB_BYTES / 1024
-    # the library's other kernels must not be taken for the copy
+    # the library's other kernels (and the flush buffer's fill and reads)
+    # must not be taken for the copy
     for sub, counter in (("f", "FETCH_SIZE"), ("w", "WRITE_SIZE")):
         _write_counters(tmp_path / sub, counter,
                         [("void pkv::direct_kernel<64, 8, 2>(...)", 40.0),
                          ("pkv::merge_kernel(...)", calib_kib * 4),
                          ("pkv::append_kernel(...)", calib_kib * 8),
-                         ("at::native::copy_kernel", calib_kib)])
+                         ("__amd_rocclr_copyBuffer", calib_kib / 16),
+                         ("__amd_rocclr_copyBuffer", calib_kib)])
     res = bench.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "t.json"),
                                 "c2_trellis")
     assert res["kernels"] == ["direct_kernel"]
