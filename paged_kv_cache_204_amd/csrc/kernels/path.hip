@@ -39,12 +39,18 @@ constexpr float kPathLoShare = 16.f;   // residual term while a weight exceeds s
 
 // A wave's K and V tiles (32 tokens x D bf16 each) hold exactly its final
 // state (32 rows x D fp32), which it writes there after its last step.
+// Then, per row: the weights of its 8 wave states and up to 8 partial
+// states, the partial states' rows, and the row's query.
 template <int D>
 struct PathSmem {
-  char slot[kPathWaves][2][kStep * D * 2];   // [wave][K, V]: the wave's step, then its state
-  float m[kPathWaves][kPathMaxRows];
-  float l[kPathWaves][kPathMaxRows];
+  alignas(16) char slot[kPathWaves][2][kStep * D * 2];   // [wave][K, V]: the wave's step, then its state
+  alignas(16) float m[kPathMaxRows][kPathWaves];
+  alignas(16) float l[kPathMaxRows][kPathWaves];
+  alignas(16) float wt[kPathMaxRows][2 * kPathWaves];    // [row][wave states 0..7, partial states 8..15]
+  alignas(16) int32_t part[kPathMaxRows][kPathMaxParts]; // the partial states' rows, -1 past the last
+  int32_t qrow[kPathMaxRows];
 };
+static_assert(kPathMaxParts == kPathWaves, "one weight lane per wave state and per partial state");
 static_assert(2 * kStep * 2 == kPathMaxRows * 4, "a wave's state fills its two tiles");
 
 // column c (a multiple of 4) of row r in a wave's state: 16-byte groups rotated
@@ -144,9 +150,18 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const PathItem* __re
   }
 
   // tile j's row l16 is item row 16 j + l16: query (16 j + l16) / G, head
-  // (16 j + l16) % G of this kv head
+  // (16 j + l16) % G of this kv head; tile_q[j]: the queries with rows in
+  // tile j (a step whose mask holds them all needs no per-row mask there)
   int my_q[NT];
   bool row_ok[NT];
+  uint32_t tile_q[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int first = (16 * j) / G;
+    const int last = min(16 * j + 15, R - 1) / G;
+    const int nb = last - first + 1;
+    tile_q[j] = 16 * j < R ? (nb >= 32 ? ~0u : (1u << nb) - 1u) << first : 0u;
+  }
   bf16x8 qf[NT][NK];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -162,18 +177,16 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const PathItem* __re
       for (int kk = 0; kk < NK; ++kk) qf[j][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  // The rows this thread combines at the end (the units of the final pass):
-  // their queries and merge rows, read now so that their latency passes
-  // under the steps.
-  constexpr int NU = (kPathMaxRows * Q4 + kPathThreads - 1) / kPathThreads;
-  int u_merge[NU], u_qrow[NU];
-#pragma unroll
-  for (int i = 0; i < NU; ++i) {
-    const int row = (tid + kPathThreads * i) / Q4;
-    const int qj = row < R ? row / G : 0;
-    u_merge[i] = row < R ? it.merge[qj] : -1;
-    u_qrow[i] = it.q_index[qj];
-  }
+  // At the end each thread weighs one state of one row: row wr, state ws
+  // (the wave states 0..7, the row's partial states 8..15).  The row's
+  // query and merge row are read now, so that their latency passes under
+  // the steps.
+  const int wr = tid >> 4;
+  const int ws = tid & 15;
+  const bool wr_ok = wr < R;
+  const int w_merge = wr_ok ? it.merge[wr / G] : -1;
+  const int w_qrow = it.q_index[wr_ok ? wr / G : 0];
+  const int w_hq = h * G + wr % G;
   // the compiler's wait for the query operands lands here
 #pragma unroll
   for (int j = 0; j < NT; ++j)
@@ -225,12 +238,18 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const PathItem* __re
     bool grow = false;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const bool vis_row = row_ok[j] && ((cur.qmask >> my_q[j]) & 1u);
       float sv[8];
+      if (n_tok == kStep && (cur.qmask & tile_q[j]) == tile_q[j]) {
+        // every key of the step, every row of the tile
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tok = 16 * (e >> 2) + 4 * g4 + (e & 3);
-        sv[e] = (vis_row && tok < n_tok) ? sacc[j][e >> 2][e & 3] : -INFINITY;
+        for (int e = 0; e < 8; ++e) sv[e] = sacc[j][e >> 2][e & 3];
+      } else {
+        const bool vis_row = row_ok[j] && ((cur.qmask >> my_q[j]) & 1u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tok = 16 * (e >> 2) + 4 * g4 + (e & 3);
+          sv[e] = (vis_row && tok < n_tok) ? sacc[j][e >> 2][e & 3] : -INFINITY;
+        }
       }
       float m = sv[0];
 #pragma unroll
@@ -320,84 +339,101 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const PathItem* __re
   wait_vmcnt<0>();
 
   // ---- the eight waves' states, then the queries' partial states ----
+  // a weight lane of a partial state requests its row and lse now; they
+  // arrive while the waves leave their states in LDS
+  int w_part = -1;
+  float w_lse = -INFINITY;
+  if (ws >= kPathWaves && w_merge >= 0) {
+    const MergeRow& mr = p.merges[w_merge];
+    if (ws - kPathWaves < mr.n_parts) {
+      w_part = mr.inl[ws - kPathWaves];
+      w_lse = p.part_lse[static_cast<size_t>(w_part) + w_hq];
+    }
+  }
   // this wave's tiles are free: its loads have landed (above) and its LDS
   // reads have returned
   __builtin_amdgcn_s_waitcnt(0xC07F);
-  float* fo = reinterpret_cast<float*>(sm.slot[wave][0]);
+  // (as 16-byte units, so that every access is one 128-bit LDS operation)
+  float4* fo = reinterpret_cast<float4*>(sm.slot[wave][0]);
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int r = 16 * j + l16;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
-      *reinterpret_cast<float4*>(&fo[r * D + fin_col(r, 16 * dt + 4 * g4)]) =
-          make_float4(o[j][dt][0], o[j][dt][1], o[j][dt][2], o[j][dt][3]);
+      fo[(r * D + fin_col(r, 16 * dt + 4 * g4)) >> 2] = make_float4(o[j][dt][0], o[j][dt][1], o[j][dt][2], o[j][dt][3]);
     if (g4 == 0) {
-      sm.m[wave][r] = m_run[j];
-      sm.l[wave][r] = o[j][ND][0];
+      sm.m[r][wave] = m_run[j];
+      sm.l[r][wave] = o[j][ND][0];
     }
   }
   lds_barrier();
-  // Four consecutive dims of one row per thread and unit: the row's common
-  // max over the waves' states and its partial states, their weights, and
-  // the weighted sum.  The thread of a row's first unit writes its lse.
+  // Per row, 16 lanes: the row's common max over its states (a wave state
+  // counts once it has a key), each state's scale, the row's total weight,
+  // and the states' normalised weights.  The row's first lane writes its
+  // lse.
+  {
+    float v = w_lse;
+    float lw = 1.f;
+    if (ws < kPathWaves) {
+      lw = sm.l[wr][ws];
+      v = lw > 0.f ? sm.m[wr][ws] : -INFINITY;
+    }
+    const float mx = group_max<16>(v);
+    const float e = v == -INFINITY ? 0.f : fast_exp2(v - mx);
+    const float total = group_sum<16>(e * lw);
+    sm.wt[wr][ws] = total > 0.f ? e / total : 0.f;
+    if (ws >= kPathWaves) sm.part[wr][ws - kPathWaves] = w_part;
+    if (ws == 0) {
+      sm.qrow[wr] = w_qrow;
+      if (wr_ok && p.lse) p.lse[static_cast<size_t>(w_qrow) * p.Hq + w_hq] = (mx + log2f(total)) * kLn2;
+    }
+  }
+  lds_barrier();
+  // Four consecutive dims of one row per thread and unit: the weighted sum
+  // of the row's wave states and partial states.
+  constexpr int NU = (kPathMaxRows * Q4 + kPathThreads - 1) / kPathThreads;
 #pragma unroll
   for (int i = 0; i < NU; ++i) {
     const int u = tid + kPathThreads * i;
     if (u >= R * Q4) break;
     const int row = u / Q4;
     const int c = (u % Q4) * 4;
-    const int mi = u_merge[i];
-    const int np = mi >= 0 ? p.merges[mi].n_parts : 0;
-    const int hq = h * G + row % G;
-    float lk[kPathMaxParts];
-#pragma unroll
-    for (int k = 0; k < kPathMaxParts; ++k)
-      lk[k] = k < np ? p.part_lse[static_cast<size_t>(p.merges[mi].inl[k]) + hq] : -INFINITY;
-    float mw[kPathWaves], lw[kPathWaves];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kPathWaves; ++w) {
-      mw[w] = sm.m[w][row];
-      lw[w] = sm.l[w][row];
-      if (lw[w] > 0.f) mx = fmaxf(mx, mw[w]);
-    }
-#pragma unroll
-    for (int k = 0; k < kPathMaxParts; ++k) mx = fmaxf(mx, lk[k]);
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kPathWaves; ++w) {
-      mw[w] = lw[w] > 0.f ? fast_exp2(mw[w] - mx) : 0.f;   // the wave state's scale
-      l = fmaf(mw[w], lw[w], l);
-    }
-#pragma unroll
-    for (int k = 0; k < kPathMaxParts; ++k) {
-      lk[k] = lk[k] == -INFINITY ? 0.f : fast_exp2(lk[k] - mx);   // the partial state's weight
-      l += lk[k];
-    }
-    const float inv = 1.f / l;
+    const float4* wrow = reinterpret_cast<const float4*>(sm.wt[row]);
+    const float4 wa = wrow[0];
+    const float4 wb = wrow[1];
+    const float wv[kPathWaves] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < kPathWaves; ++w) {
-      const float a = mw[w] * inv;
-      const float4 x =
-          *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sm.slot[w][0]) + row * D + fin_col(row, c));
-      acc.x = fmaf(a, x.x, acc.x);
-      acc.y = fmaf(a, x.y, acc.y);
-      acc.z = fmaf(a, x.z, acc.z);
-      acc.w = fmaf(a, x.w, acc.w);
+      const float4 x = reinterpret_cast<const float4*>(sm.slot[w][0])[(row * D + fin_col(row, c)) >> 2];
+      acc.x = fmaf(wv[w], x.x, acc.x);
+      acc.y = fmaf(wv[w], x.y, acc.y);
+      acc.z = fmaf(wv[w], x.z, acc.z);
+      acc.w = fmaf(wv[w], x.w, acc.w);
     }
-    for (int k = 0; k < np; ++k) {
-      const float a = lk[k] * inv;
-      const float4 y = *reinterpret_cast<const float4*>(
-          p.part_o + (static_cast<size_t>(p.merges[mi].inl[k]) + hq) * D + c);
-      acc.x = fmaf(a, y.x, acc.x);
-      acc.y = fmaf(a, y.y, acc.y);
-      acc.z = fmaf(a, y.z, acc.z);
-      acc.w = fmaf(a, y.w, acc.w);
+    const int hq = h * G + row % G;
+    if (sm.part[row][0] >= 0) {
+      const int4 ia = reinterpret_cast<const int4*>(sm.part[row])[0];
+      const int4 ib = reinterpret_cast<const int4*>(sm.part[row])[1];
+      const int pi[kPathMaxParts] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+      const float4 pa = wrow[2];
+      const float4 pb = wrow[3];
+      const float pw[kPathMaxParts] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      float4 y[kPathMaxParts];
+#pragma unroll
+      for (int k = 0; k < kPathMaxParts; ++k)
+        y[k] = pi[k] >= 0 ? *reinterpret_cast<const float4*>(p.part_o + (static_cast<size_t>(pi[k]) + hq) * D + c)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < kPathMaxParts; ++k) {
+        acc.x = fmaf(pw[k], y[k].x, acc.x);
+        acc.y = fmaf(pw[k], y[k].y, acc.y);
+        acc.z = fmaf(pw[k], y[k].z, acc.z);
+        acc.w = fmaf(pw[k], y[k].w, acc.w);
+      }
     }
-    const size_t orow = static_cast<size_t>(u_qrow[i]) * p.Hq + hq;
+    const size_t orow = static_cast<size_t>(sm.qrow[row]) * p.Hq + hq;
     *reinterpret_cast<float4*>(p.out + orow * D + c) = acc;
-    if (c == 0 && p.lse) p.lse[orow] = (mx + log2f(l)) * kLn2;
   }
 }
 
