@@ -37,12 +37,14 @@ constexpr int kPathThreads = 64 * kPathWaves;
 constexpr int kPathTiles = kPathMaxRows / 16;
 constexpr float kPathLoShare = 16.f;   // residual term while a weight exceeds sum / 16
 
-// A wave's K and V tiles (32 tokens x D bf16 each) hold exactly its final
+// The item's query rows (32 rows x D bf16, laid out as a K tile).  A
+// wave's K and V tiles (32 tokens x D bf16 each) hold exactly its final
 // state (32 rows x D fp32), which it writes there after its last step.
 // Then, per row: the weights of its 8 wave states and up to 8 partial
 // states, the partial states' rows, and the row's query.
 template <int D>
 struct PathSmem {
+  alignas(16) char q[kPathMaxRows * D * 2];
   alignas(16) char slot[kPathWaves][2][kStep * D * 2];   // [wave][K, V]: the wave's step, then its state
   alignas(16) float m[kPathMaxRows][kPathWaves];
   alignas(16) float l[kPathMaxRows][kPathWaves];
@@ -51,6 +53,7 @@ struct PathSmem {
   int32_t qrow[kPathMaxRows];
 };
 static_assert(kPathMaxParts == kPathWaves, "one weight lane per wave state and per partial state");
+static_assert(kPathMaxRows == kStep, "the query rows fill one K tile layout");
 static_assert(2 * kStep * 2 == kPathMaxRows * 4, "a wave's state fills its two tiles");
 
 // column c (a multiple of 4) of row r in a wave's state: 16-byte groups rotated
@@ -82,6 +85,34 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const PathItem* __re
   const int n_steps = it.n_steps;
   const int step0 = it.step_off;
   const int R = it.n_q * G;
+
+  // At the end each thread weighs one state of one row: row wr, state ws
+  // (the wave states 0..7, the row's partial states 8..15).  The row's
+  // query and merge row are read now, so that their latency passes under
+  // the steps.
+  const int wr = tid >> 4;
+  const int ws = tid & 15;
+  const bool wr_ok = wr < R;
+  const int w_merge = wr_ok ? it.merge[wr / G] : -1;
+  const int w_qrow = it.q_index[wr_ok ? wr / G : 0];
+  const int w_hq = h * G + wr % G;
+
+  // The item's query rows go to LDS first, one 1 KB run per wave (laid out
+  // as a K tile: slot c = 64 u + lane holds row c / CPR, chunk
+  // (c % CPR) ^ tile_swz(row)), ahead of the first step's K and V; rows
+  // past the item's last are read from its first row and zeroed below.
+  constexpr int Q_RUNS = kPathMaxRows * CPR / 64;
+  if (wave < Q_RUNS) {
+    const int c = wave * 64 + lane;
+    const int r = c / CPR;
+    const int ch = (c % CPR) ^ tile_swz<D>(r);
+    const int qj = r < R ? r / G : 0;
+    int qi = it.q_index[0];
+#pragma unroll
+    for (int t = 1; t < kPathMaxQ; ++t) qi = qj == t ? it.q_index[t] : qi;
+    const uint16_t* qrow = p.q + (static_cast<size_t>(qi) * p.Hq + h * G + (r < R ? r % G : 0)) * D;
+    lds_dma16(reinterpret_cast<const uint4*>(qrow) + ch, sm.q + wave * 1024);
+  }
 
   const uint4* kb = layer_head_base(p, p.k_pool, h, D);
   const uint4* vb = layer_head_base(p, p.v_pool, h, D);
@@ -162,36 +193,25 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const PathItem* __re
     const int nb = last - first + 1;
     tile_q[j] = 16 * j < R ? (nb >= 32 ? ~0u : (1u << nb) - 1u) << first : 0u;
   }
+  // the query rows: this wave's run has landed once at most the first
+  // step's K and V runs are in flight (issued after it); the barrier makes
+  // every wave's run visible
+  if (mine > 0)
+    wait_vmcnt<2 * RUNS>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
   bf16x8 qf[NT][NK];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int r = 16 * j + l16;
     row_ok[j] = r < R;
     my_q[j] = row_ok[j] ? r / G : 0;
-    const int qi = it.q_index[my_q[j]];
-    const uint16_t* qrow = p.q + (static_cast<size_t>(qi) * p.Hq + h * G + (row_ok[j] ? r % G : 0)) * D;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) qf[j][kk] = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * g4);
-    if (!row_ok[j]) {
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) qf[j][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    for (int kk = 0; kk < NK; ++kk)
+      qf[j][kk] = row_ok[j] ? *reinterpret_cast<const bf16x8*>(sm.q + tile_byte<D>(r, 4 * kk + g4))
+                            : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
-  // At the end each thread weighs one state of one row: row wr, state ws
-  // (the wave states 0..7, the row's partial states 8..15).  The row's
-  // query and merge row are read now, so that their latency passes under
-  // the steps.
-  const int wr = tid >> 4;
-  const int ws = tid & 15;
-  const bool wr_ok = wr < R;
-  const int w_merge = wr_ok ? it.merge[wr / G] : -1;
-  const int w_qrow = it.q_index[wr_ok ? wr / G : 0];
-  const int w_hq = h * G + wr % G;
-  // the compiler's wait for the query operands lands here
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) asm volatile("" : "+v"(qf[j][kk]));
 
   float m_run[NT];
   f32x4 o[NT][ND + 1];   // o[j][ND]: row sums (P V against a tile of ones)
