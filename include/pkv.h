@@ -285,7 +285,11 @@ pkv_status paged_attn_decode_layers(pkv_pool* pool, int32_t layer0, int32_t n_la
 /*
  * paged_attn_decode for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid it):
- * the same arguments, kernels and results, but the call's work lists and
+ * the same arguments and results, and the same kernels except that none of
+ * them uses private (scratch) memory, which the runtime would size at its
+ * first launch (for 256-row dense tiles at head_dim 128 this entry takes
+ * the eight-wave kernel instead of the sixteen-wave one, which spills a few
+ * registers).  The call's work lists and
  * partial softmax states live in a file-scope device array of the library
  * (32 MiB per device: 8 MiB of work lists, 24 MiB of partial states), held
  * by each device the library runs on until the process ends.  The call

@@ -431,11 +431,12 @@ bool plan_fits_kernels(const pkv::Plan& plan, const pkv::Shape& sh) {
 // The attention kernel of one call (the direct kernel for direct plans)
 // and, when some queries have several partial states, the merge kernel.
 // With timing enabled, a pair of events takes the attention kernel's own
-// start and end.
+// start and end.  no_scratch: only kernels without private (scratch)
+// memory, whose first launch could make the runtime allocate.
 pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay,
                           const DevBuf& buf, DevBuf& parts, int32_t layer, const void* q, float sm_scale,
                           float* out, float* lse, hipStream_t stream, int32_t n_layers = 1,
-                          int64_t layer_rows = 0) {
+                          int64_t layer_rows = 0, bool no_scratch = false) {
   const pkv::Shape& sh = p->core.shape();
   if (n_layers > 1 && plan.direct.empty()) {
     // the plan's launches once per layer (partial states reused in stream order)
@@ -443,7 +444,8 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
       const size_t rows = static_cast<size_t>(layer_rows) * l;
       pkv_status s = launch_plan(p, plan, lay, buf, parts, layer + l,
                                  static_cast<const uint16_t*>(q) + rows * sh.head_dim, sm_scale,
-                                 out + rows * sh.head_dim, lse ? lse + rows : nullptr, stream);
+                                 out + rows * sh.head_dim, lse ? lse + rows : nullptr, stream, 1, 0,
+                                 no_scratch);
       if (s != PKV_OK) return s;
     }
     return PKV_OK;
@@ -501,7 +503,7 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
       int32_t max_rows = 0;
       for (const pkv::WorkItem& it : plan.mfma) max_rows = std::max(max_rows, it.n_grp * ap.G);
       PKV_HIP(pkv::launch_wide(ap, static_cast<int32_t>(plan.mfma.size()), sh.head_dim, plan.stride_mfma,
-                               max_rows, stream, ev_a, nullptr));
+                               max_rows, stream, ev_a, nullptr, no_scratch));
       ev_a = nullptr;
     }
     PKV_HIP(pkv::launch_path(ap, paths, static_cast<int32_t>(plan.paths.size()), sh.head_dim, stream, ev_a,
@@ -513,7 +515,7 @@ pkv_status launch_plan(pkv_pool* p, const pkv::Plan& plan, const PlanLayout& lay
   {
     int32_t max_rows = 0;
     for (const pkv::WorkItem& it : plan.mfma) max_rows = std::max(max_rows, it.n_grp * ap.G);
-    PKV_HIP(pkv::launch_wide(ap, n_items, sh.head_dim, plan.stride_mfma, max_rows, stream, ev_a, ev_b));
+    PKV_HIP(pkv::launch_wide(ap, n_items, sh.head_dim, plan.stride_mfma, max_rows, stream, ev_a, ev_b, no_scratch));
   }
   else if (plan.direct.empty())
     PKV_HIP(pkv::launch_attn(ap, n_items, sh.head_dim, plan.mfma_row_tiles,
@@ -1189,7 +1191,8 @@ pkv_status paged_attn_decode_scratch(pkv_pool* p, int32_t layer, const int64_t* 
   serialize(p->splan, p->slayout, p->sstage.data());
   if (p->slayout.total > 0)
     PKV_HIP(hipMemcpyAsync(lists.ptr, p->sstage.data(), p->slayout.total, hipMemcpyHostToDevice, st));
-  return launch_plan(p, p->splan, p->slayout, lists, parts, layer, q, sm_scale, out, lse, st);
+  return launch_plan(p, p->splan, p->slayout, lists, parts, layer, q, sm_scale, out, lse, st, 1, 0,
+                     /*no_scratch=*/true);
 }
 
 pkv_status paged_attn_tree_verify(pkv_pool* p, int32_t layer, const int64_t* seqs, int32_t n_seqs,

@@ -128,12 +128,15 @@ hipError_t launch_attn(const AttnParams& p, int32_t n_items, int32_t head_dim, i
                        hipEvent_t ev_stop = nullptr);
 
 // Dense tiles only (every item an MFMA item, up to 256 rows): one workgroup
-// of four waves per (item, kv head), software-pipelined steps; items[i]'s
-// block list at blocks + i * stride (<= kMaxItemBlocks); max_rows: the most
-// rows (row groups x G) of any item, 1..256.
+// of 4, 8 or 16 waves per (item, kv head), software-pipelined steps;
+// items[i]'s block list at blocks + i * stride (<= kMaxItemBlocks);
+// max_rows: the most rows (row groups x G) of any item, 1..256.
+// no_scratch: only kernels that use no private (scratch) memory -- the
+// sixteen-wave variant spills a few registers, and the runtime sizes a
+// queue's scratch area at the first launch that needs it.
 hipError_t launch_wide(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
                        int32_t max_rows, hipStream_t s, hipEvent_t ev_start = nullptr,
-                       hipEvent_t ev_stop = nullptr);
+                       hipEvent_t ev_stop = nullptr, bool no_scratch = false);
 
 // Path items of a tree decode plan: one workgroup of eight waves per (path
 // item, kv head); the waves take the item's steps (p.steps) in turn, then

@@ -6,8 +6,9 @@
 //
 // One workgroup runs one item for one kv head: up to 256 query rows (row
 // groups x the G query heads of the kv head) in 16-row tiles, tile t held by
-// wave t % W (4 waves of one tile, 8 of one or 8 of two, fixed per launch by
-// its largest item), over the item's keys in 32-token steps.  Per step, with v_mfma_f32_16x16x32_bf16:
+// wave t % W (4 waves of one tile, 8 of one, or for 256 rows 16 of one at
+// head_dim 128 and 8 of two at head_dim 64; fixed per launch by its largest
+// item), over the item's keys in 32-token steps.  Per step, with v_mfma_f32_16x16x32_bf16:
 //   S^T = K Q^T  (A = K rows from LDS, B = the tile's Q in registers: each
 //                 lane then holds 4 keys of ONE query row per 16-key half),
 //   online softmax of S (lane local, two cross-row swaps per reduction),
@@ -39,7 +40,7 @@ namespace {
 using dense::WideSmem;
 
 template <int D, int W, int NT, int RING, int UNROLL>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void wide_kernel(
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 16 ? 4 : 2))) void wide_kernel(
     const WorkItem* __restrict__ items, const int32_t* __restrict__ blocks, const RowGroup* __restrict__ groups,
     const uint16_t* __restrict__ q, int32_t stride, AttnParams p) {
   __shared__ WideSmem<D, RING> sm;
@@ -53,8 +54,9 @@ template <int D, int W, int NT>
 hipError_t launch_wide_t(const AttnParams& p, dim3 grid, int32_t stride, hipStream_t s, hipEvent_t a,
                          hipEvent_t b) {
   constexpr int kRingTiles = 4;
-  // unrolled by the ring, except where its constant slots cost the two-tile
-  // head_dim 128 variant a register spill
+  // unrolled by the ring (constant slots), except for the two-tile head_dim
+  // 128 variant, where that costs a register spill (the sixteen-wave one
+  // spills a few registers either way and is faster unrolled by the ring)
   constexpr int kUnroll = (D == 128 && NT == 2) ? 2 : kRingTiles;
   hipExtLaunchKernelGGL((wide_kernel<D, W, NT, kRingTiles, kUnroll>), grid, dim3(64 * W), 0, s, a, b, 0, p.items,
                         p.blocks, p.groups, p.q, stride, p);
@@ -64,15 +66,19 @@ hipError_t launch_wide_t(const AttnParams& p, dim3 grid, int32_t stride, hipStre
 }  // namespace
 
 hipError_t launch_wide(const AttnParams& p, int32_t n_items, int32_t head_dim, int32_t stride,
-                       int32_t max_rows, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                       int32_t max_rows, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop,
+                       bool no_scratch) {
   if (n_items == 0) return hipSuccess;
   if (stride < 1 || stride > kMaxItemBlocks || max_rows < 1 || max_rows > 256) return hipErrorInvalidValue;
   const int64_t n_wg = static_cast<int64_t>(n_items) * p.Hkv;
   if (n_wg > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(n_wg));
   // by the largest item: up to 64 rows four waves of one tile, up to 128
-  // eight waves of one tile, else eight waves of two (four tiles per wave
-  // do not fit the registers)
+  // eight waves of one tile, else sixteen waves of one at head_dim 128 (four
+  // waves per SIMD instead of two: measured on the tree-verify call, 41.6 ->
+  // 38 us per launch; eight waves of two where no scratch may be used) and
+  // eight waves of two at head_dim 64 (a step there has 8 load runs, fewer
+  // than sixteen waves)
   if (head_dim == 64) {
     if (max_rows <= 64) return launch_wide_t<64, 4, 1>(p, grid, stride, s, ev_start, ev_stop);
     if (max_rows <= 128) return launch_wide_t<64, 8, 1>(p, grid, stride, s, ev_start, ev_stop);
@@ -81,7 +87,8 @@ hipError_t launch_wide(const AttnParams& p, int32_t n_items, int32_t head_dim, i
   if (head_dim == 128) {
     if (max_rows <= 64) return launch_wide_t<128, 4, 1>(p, grid, stride, s, ev_start, ev_stop);
     if (max_rows <= 128) return launch_wide_t<128, 8, 1>(p, grid, stride, s, ev_start, ev_stop);
-    return launch_wide_t<128, 8, 2>(p, grid, stride, s, ev_start, ev_stop);
+    if (no_scratch) return launch_wide_t<128, 8, 2>(p, grid, stride, s, ev_start, ev_stop);
+    return launch_wide_t<128, 16, 1>(p, grid, stride, s, ev_start, ev_stop);
   }
   return hipErrorInvalidValue;
 }
