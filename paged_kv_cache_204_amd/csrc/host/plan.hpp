@@ -56,7 +56,8 @@ struct PlanConfig {
                                  // (there is parallelism to spare: fewer, longer chunks
                                  // and a cheaper merge); 0 turns this off
   int32_t max_chunk_blocks = 512;// block ids per work item at most (LDS staging)
-  int32_t mixed_kernel_only = 0; // 1: dense-tile-only plans run on the mixed kernel too
+  int32_t mixed_kernel_only = 0; // 1: dense-tile-only plans at head_dim 128 run on the mixed
+                                 // kernel too (at head_dim 64 they do anyway)
   // tree decode plans (block size >= 16): path items over the trie, very
   // long shared segments through MFMA items as partial states
   int32_t tree_decode = 1;       // 0 turns tree plans off
