@@ -21,8 +21,13 @@
  * Conventions for every call:
  *   - Status codes, never exceptions or aborts.  On any error the host state
  *     (tables, refcounts, free list, sequence ids) is exactly as before the
- *     call and no device work has been enqueued.  pkv_last_error() gives a
- *     message for the calling thread's last failure.
+ *     call and no device work has been enqueued -- except PKV_ERR_HIP from a
+ *     kernel launch itself (a runtime or device failure, not an argument
+ *     the library checks): work enqueued before it in the same call (a plan
+ *     upload, the earlier sequences of a commit that runs them one by one)
+ *     may have run, so the device contents of the pool are then undefined
+ *     and the pool should be destroyed.  pkv_last_error() gives a message
+ *     for the calling thread's last failure.
  *   - Ownership: every device pointer (the two K/V pools, the workspace, new
  *     K/V, Q, out, lse) is owned by the caller and must stay valid until the
  *     work enqueued on the stream has finished.  The pool handle owns its host
@@ -236,7 +241,8 @@ pkv_status kv_append(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
  * All-or-nothing (PKV_ERR_OOM / PKV_ERR_ARG / PKV_ERR_SEQ change nothing).
  * Device work (device pools): one launch on `stream` (one per sequence
  * when a block one sequence writes in place is read by another).
- * 1 <= n_nodes <= 64; sequences must be distinct.
+ * 1 <= n_nodes <= 64; n_seqs <= 65535 (PKV_ERR_ARG beyond); sequences must
+ * be distinct.
  */
 pkv_status kv_tree_commit(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs, int32_t n_nodes,
                           const int32_t* parent, const int32_t* path_len, const int32_t* paths,

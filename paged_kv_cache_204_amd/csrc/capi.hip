@@ -904,6 +904,9 @@ pkv_status kv_tree_commit(pkv_pool* p, const int64_t* seqs, int32_t n_seqs, int3
   if (!p) return fail(PKV_ERR_ARG, "kv_tree_commit: NULL pool");
   if (p->q4) return fail(PKV_ERR_UNSUPPORTED, "kv_tree_commit: 4-bit pools support decode only");
   if (n_seqs == 0) return PKV_OK;
+  // the commit launch takes one grid row per sequence (checked before any
+  // work is enqueued)
+  if (n_seqs > 65535) return fail(PKV_ERR_ARG, "kv_tree_commit: at most 65535 sequences per call");
   pkv::PendingCommit pc;
   std::string why;
   pkv::Err e = p->core.prepare_commit(seqs, n_seqs, n_nodes, parent, path_len, paths, &pc, &why);

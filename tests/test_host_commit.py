@@ -92,3 +92,19 @@ def test_random_commit_programs_match_the_oracle(B, N, seed):
                 assert pkv.seq_block_table(c, cs) == (m.table(ms), m.length(ms))
     finally:
         pkv.kv_pool_destroy(c)
+
+
+def test_commit_refuses_more_sequences_than_one_launch_takes():
+    # the commit launch takes one grid row per sequence: 65535 at most, refused
+    # before any work and without touching the pool
+    n = 65536
+    c = host_pool(n, 1)
+    ids = [pkv.seq_allocate(c) for _ in range(n)]
+    pkv.kv_append(c, ids, 1)
+    before = pkv.free_list(c), [pkv.seq_block_table(c, i) for i in ids[:4] + ids[-4:]]
+    par = np.full((n, 1), -1, dtype=np.int32)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.kv_tree_commit(c, ids, 1, par, [[0]] * n)
+    assert e.value.code == pkv.PKV_ERR_ARG and "65535" in e.value.message
+    assert (pkv.free_list(c), [pkv.seq_block_table(c, i) for i in ids[:4] + ids[-4:]]) == before
+    pkv.kv_pool_destroy(c)
