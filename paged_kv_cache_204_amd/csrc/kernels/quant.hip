@@ -250,7 +250,15 @@ __global__ __launch_bounds__(64 * W) void q4_mfma_kernel(Q4DecodeParams p) {
                   (static_cast<uint32_t>(f16_bits(kLevels[i >> 4])) << 16);
   for (int g = wave; g < 16; g += W) {
     float y0 = 0.f, y1 = 0.f;
-    if (g < G && lane < HALF) {
+    if (g >= G) {
+      // rows of the tile past the group: zero operands, no rotation
+      if (lane < HALF) {
+        qrot[g][2 * lane] = 0.f;
+        qrot[g][2 * lane + 1] = 0.f;
+      }
+      continue;
+    }
+    if (lane < HALF) {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(p.q + (row0 + g) * D + 2 * lane);
       y0 = p.signs[2 * lane] * bf16_lo(w);
       y1 = p.signs[2 * lane + 1] * bf16_hi(w);
@@ -295,22 +303,81 @@ __global__ __launch_bounds__(64 * W) void q4_mfma_kernel(Q4DecodeParams p) {
   const int nsteps = (it.n_tok + kQStep - 1) / kQStep;
   for (int s = wave; s < nsteps; s += W) {
     const int t0 = s * kQStep;
-    // K operands and the norms of this lane's two K keys
+    // K operands (keys 16 tt + l16), V codes (keys ci / CPR) and the norms of
+    // the keys this lane's scores hold (16 tt + 4 g4 + i)
     uint32_t kw[2][NK];
-    float kn_l[2], vn_l[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int64_t vec = vec_of(t0 + 16 * tt + l16);
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) kw[tt][kk] = kc32[vec * (D / 8) + 4 * kk + g4];
-      kn_l[tt] = __half2float(__ushort_as_half(p.k_norms[vec]));
-      vn_l[tt] = __half2float(__ushort_as_half(p.v_norms[vec]));
-    }
     uint32_t vw[VPER];
+    float knk[8], vnk[8];
+    if (p.B >= 16) {
+      // Each 16-key half of the step lies in one block (blocks of 16: the
+      // step's first and second block; larger: one block), so a load takes
+      // the half's block base, the same for the whole wave, and a 32-bit
+      // lane offset.  Keys past the end re-read the last key of the half's
+      // block (masked below).
+      const int r_last = t_last - t0;
+      const int32_t* tbl = p.blocks + it.blk_off;
+      const int64_t va = p.layer * layer_vecs + static_cast<int64_t>(tbl[t0 >> p.log2B]) * head_vecs +
+                         static_cast<int64_t>(h) * p.B + (t0 & (p.B - 1));
+      const bool two = p.B == 16 && r_last >= 16;
+      const int64_t vb = two ? p.layer * layer_vecs + static_cast<int64_t>(tbl[(t0 + 16) >> p.log2B]) * head_vecs +
+                                   static_cast<int64_t>(h) * p.B
+                             : va;
+      const int off_b = two ? 16 : 0;   // key of the second half's base
+      const uint32_t* kh[2] = {kc32 + va * (D / 8), kc32 + vb * (D / 8)};
+      const uint32_t* vh[2] = {vc32 + va * (D / 8), vc32 + vb * (D / 8)};
+      const uint16_t* knh[2] = {p.k_norms + va, p.k_norms + vb};
+      const uint16_t* vnh[2] = {p.v_norms + va, p.v_norms + vb};
+      const int hoff[2] = {0, off_b};
 #pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int ci = lane + 64 * i;
-      vw[i] = vc32[vec_of(t0 + ci / CPR) * (D / 8) + ci % CPR];
+      for (int tt = 0; tt < 2; ++tt) {
+        const int r = min(16 * tt + l16, r_last) - hoff[tt];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) kw[tt][kk] = kh[tt][r * (D / 8) + 4 * kk + g4];
+        // four consecutive keys' norms, one 8-byte load each (a group past
+        // the end re-reads the half's last whole group)
+        const int r0 = min(16 * tt + 4 * g4, r_last & ~3) - hoff[tt];
+        const uint2 kn2 = *reinterpret_cast<const uint2*>(knh[tt] + r0);
+        const uint2 vn2 = *reinterpret_cast<const uint2*>(vnh[tt] + r0);
+        knk[4 * tt + 0] = __half2float(__ushort_as_half(static_cast<uint16_t>(kn2.x)));
+        knk[4 * tt + 1] = __half2float(__ushort_as_half(static_cast<uint16_t>(kn2.x >> 16)));
+        knk[4 * tt + 2] = __half2float(__ushort_as_half(static_cast<uint16_t>(kn2.y)));
+        knk[4 * tt + 3] = __half2float(__ushort_as_half(static_cast<uint16_t>(kn2.y >> 16)));
+        vnk[4 * tt + 0] = __half2float(__ushort_as_half(static_cast<uint16_t>(vn2.x)));
+        vnk[4 * tt + 1] = __half2float(__ushort_as_half(static_cast<uint16_t>(vn2.x >> 16)));
+        vnk[4 * tt + 2] = __half2float(__ushort_as_half(static_cast<uint16_t>(vn2.y)));
+        vnk[4 * tt + 3] = __half2float(__ushort_as_half(static_cast<uint16_t>(vn2.y >> 16)));
+      }
+#pragma unroll
+      for (int i = 0; i < VPER; ++i) {
+        const int ci = lane + 64 * i;
+        constexpr int KPI = 64 / CPR;               // keys per i: all in one half
+        const int half = (KPI * i) >> 4;
+        const int r = min(ci / CPR, r_last) - hoff[half];
+        vw[i] = vh[half][r * (D / 8) + ci % CPR];
+      }
+    } else {
+      float kn_l[2], vn_l[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int64_t vec = vec_of(t0 + 16 * tt + l16);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) kw[tt][kk] = kc32[vec * (D / 8) + 4 * kk + g4];
+        kn_l[tt] = __half2float(__ushort_as_half(p.k_norms[vec]));
+        vn_l[tt] = __half2float(__ushort_as_half(p.v_norms[vec]));
+      }
+#pragma unroll
+      for (int i = 0; i < VPER; ++i) {
+        const int ci = lane + 64 * i;
+        vw[i] = vc32[vec_of(t0 + ci / CPR) * (D / 8) + ci % CPR];
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int src = 4 * g4 + i;                 // the lane that loaded key 16 tt + 4 g4 + i
+          knk[4 * tt + i] = __shfl(kn_l[tt], src, 64);
+          vnk[4 * tt + i] = __shfl(vn_l[tt], src, 64);
+        }
     }
     // V tile as fp16 levels (this wave's earlier reads of it are done)
     wave_sync_lds();
@@ -328,16 +395,13 @@ __global__ __launch_bounds__(64 * W) void q4_mfma_kernel(Q4DecodeParams p) {
       for (int kk = 0; kk < NK; ++kk)
         sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(levels8(kw[tt][kk]), qf[kk], sacc[tt], 0, 0, 0);
     }
-    float z[8], vnk[8];
+    float z[8];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int src = 4 * g4 + i;                 // the lane that loaded key 16 tt + 4 g4 + i
-        const float kn = __shfl(kn_l[tt], src, 64);
-        vnk[4 * tt + i] = __shfl(vn_l[tt], src, 64);
-        const int tok = t0 + 16 * tt + src;
-        z[4 * tt + i] = tok < it.n_tok ? sacc[tt][i] * kn * zscale : -INFINITY;
+        const int tok = t0 + 16 * tt + 4 * g4 + i;
+        z[4 * tt + i] = tok < it.n_tok ? sacc[tt][i] * knk[4 * tt + i] * zscale : -INFINITY;
       }
     float mx = z[0];
 #pragma unroll
