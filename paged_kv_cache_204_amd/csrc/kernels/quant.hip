@@ -195,8 +195,12 @@ __device__ __forceinline__ void fwht_f32(float& y0, float& y1, int lane, int hal
 // levels, so 8 dims of a key are four table reads.  In the rotated space a
 // key's score is (scale / D) * n_k * sum_d qh_d level_d, qh = H (s * q): the
 // MFMA contracts qh (fp16) with the levels and the key norm scales the
-// result; the V norm scales the probability before P.V.  The waves' softmax
-// states meet in LDS, and the merged rows are rotated back once.
+// result; the V norm scales the probability before P.V.  A wave requests its
+// next step's codes and norms before it computes the current one (two
+// register sets in turn), and its first step's before the query rotation;
+// the running output is rescaled only in steps that raise a row's max.  The
+// waves' softmax states meet in LDS, and the merged rows are rotated back
+// once.
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef short v4i16q __attribute__((ext_vector_type(4)));
@@ -224,13 +228,25 @@ union Q4Smem {
   } fin;
 };
 
-template <int D, int W>
-__global__ __launch_bounds__(64 * W) void q4_mfma_kernel(Q4DecodeParams p) {
+// K/V codes and norms of one 32-key step, as loaded: the next step's are
+// requested before the current step is computed.
+template <int D>
+struct Q4StepRaw {
+  uint32_t kw[2][D / 32];             // K operands: keys 16 tt + l16, dims 32 kk + 8 g4 ..
+  uint32_t vw[kQStep * (D / 8) / 64]; // V chunks ci = lane + 64 i: key ci / CPR, chunk ci % CPR
+  uint2 kn[2], vn[2];                 // norms: keys 16 tt + 4 g4 .. + 3 (blocks of 16 or more),
+                                      // else key 16 tt + l16 in the low half of .x
+};
+
+template <int D, int W, bool BIG>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 : 2))) void q4_mfma_kernel(
+    Q4DecodeParams p) {
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
   constexpr int CPR = D / 8;                 // 8-dim chunks per key row
   constexpr int VPER = kQStep * CPR / 64;    // V chunks per lane per step
   constexpr int HALF = D / 2;
+  constexpr int RPW = 16 / W;                // rows of the 16-row query tile per wave
   __shared__ uint32_t pair_lut[256];         // code byte -> (fp16 level lo, hi)
   __shared__ __align__(16) float qrot[16][D];   // rotated query rows, then merged outputs
   __shared__ __align__(16) Q4Smem<D, W> sm;
@@ -241,41 +257,10 @@ __global__ __launch_bounds__(64 * W) void q4_mfma_kernel(Q4DecodeParams p) {
   const Q4Item it = p.items[item];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
   const int64_t row0 = static_cast<int64_t>(it.q_index) * p.Hq + static_cast<int64_t>(h) * G;
-  for (int i = tid; i < 256; i += 64 * W)
-    pair_lut[i] = static_cast<uint32_t>(f16_bits(kLevels[i & 15])) |
-                  (static_cast<uint32_t>(f16_bits(kLevels[i >> 4])) << 16);
-  for (int g = wave; g < 16; g += W) {
-    float y0 = 0.f, y1 = 0.f;
-    if (g >= G) {
-      // rows of the tile past the group: zero operands, no rotation
-      if (lane < HALF) {
-        qrot[g][2 * lane] = 0.f;
-        qrot[g][2 * lane + 1] = 0.f;
-      }
-      continue;
-    }
-    if (lane < HALF) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(p.q + (row0 + g) * D + 2 * lane);
-      y0 = p.signs[2 * lane] * bf16_lo(w);
-      y1 = p.signs[2 * lane + 1] * bf16_hi(w);
-    }
-    fwht_f32(y0, y1, lane, HALF);
-    if (lane < HALF) {
-      qrot[g][2 * lane] = y0;
-      qrot[g][2 * lane + 1] = y1;
-    }
-  }
-  __syncthreads();
-  // B operand: row l16, dims 32 kk + 8 g4 .. + 7
-  f16x8 qf[NK];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[kk][e] = static_cast<_Float16>(qrot[l16][32 * kk + 8 * g4 + e]);
 
   const int64_t head_vecs = static_cast<int64_t>(p.Hkv) * p.B;
   const int64_t layer_vecs = head_vecs * p.N;
@@ -287,33 +272,15 @@ __global__ __launch_bounds__(64 * W) void q4_mfma_kernel(Q4DecodeParams p) {
     const int32_t blk = p.blocks[it.blk_off + (t >> p.log2B)];
     return p.layer * layer_vecs + blk * head_vecs + static_cast<int64_t>(h) * p.B + (t & (p.B - 1));
   };
-  auto levels8 = [&](uint32_t word) {
-    const uint32_t a = pair_lut[word & 255u], b = pair_lut[(word >> 8) & 255u];
-    const uint32_t c = pair_lut[(word >> 16) & 255u], d = pair_lut[word >> 24];
-    const uint4 u = make_uint4(a, b, c, d);
-    return __builtin_bit_cast(f16x8, u);
-  };
-  const float zscale = p.scale_log2 / static_cast<float>(D);
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4v o[ND];
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  uint16_t (*vs)[D + 8] = sm.v[wave];
-
-  const int nsteps = (it.n_tok + kQStep - 1) / kQStep;
-  for (int s = wave; s < nsteps; s += W) {
+  // step s's codes and norms into d; keys past the end re-read the last key
+  // (masked when the scores are formed)
+  auto load_step = [&](int s, Q4StepRaw<D>& d) __attribute__((always_inline)) {
     const int t0 = s * kQStep;
-    // K operands (keys 16 tt + l16), V codes (keys ci / CPR) and the norms of
-    // the keys this lane's scores hold (16 tt + 4 g4 + i)
-    uint32_t kw[2][NK];
-    uint32_t vw[VPER];
-    float knk[8], vnk[8];
-    if (p.B >= 16) {
+    if constexpr (BIG) {
       // Each 16-key half of the step lies in one block (blocks of 16: the
       // step's first and second block; larger: one block), so a load takes
       // the half's block base, the same for the whole wave, and a 32-bit
-      // lane offset.  Keys past the end re-read the last key of the half's
-      // block (masked below).
+      // lane offset.
       const int r_last = t_last - t0;
       const int32_t* tbl = p.blocks + it.blk_off;
       const int64_t va = p.layer * layer_vecs + static_cast<int64_t>(tbl[t0 >> p.log2B]) * head_vecs +
@@ -330,61 +297,132 @@ __global__ __launch_bounds__(64 * W) void q4_mfma_kernel(Q4DecodeParams p) {
       const int hoff[2] = {0, off_b};
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int r = min(16 * tt + l16, r_last) - hoff[tt];
+        const uint32_t r = static_cast<uint32_t>(min(16 * tt + l16, r_last) - hoff[tt]);
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) kw[tt][kk] = kh[tt][r * (D / 8) + 4 * kk + g4];
+        for (int kk = 0; kk < NK; ++kk) d.kw[tt][kk] = kh[tt][r * (D / 8) + 4 * kk + g4];
         // four consecutive keys' norms, one 8-byte load each (a group past
         // the end re-reads the half's last whole group)
-        const int r0 = min(16 * tt + 4 * g4, r_last & ~3) - hoff[tt];
-        const uint2 kn2 = *reinterpret_cast<const uint2*>(knh[tt] + r0);
-        const uint2 vn2 = *reinterpret_cast<const uint2*>(vnh[tt] + r0);
-        knk[4 * tt + 0] = __half2float(__ushort_as_half(static_cast<uint16_t>(kn2.x)));
-        knk[4 * tt + 1] = __half2float(__ushort_as_half(static_cast<uint16_t>(kn2.x >> 16)));
-        knk[4 * tt + 2] = __half2float(__ushort_as_half(static_cast<uint16_t>(kn2.y)));
-        knk[4 * tt + 3] = __half2float(__ushort_as_half(static_cast<uint16_t>(kn2.y >> 16)));
-        vnk[4 * tt + 0] = __half2float(__ushort_as_half(static_cast<uint16_t>(vn2.x)));
-        vnk[4 * tt + 1] = __half2float(__ushort_as_half(static_cast<uint16_t>(vn2.x >> 16)));
-        vnk[4 * tt + 2] = __half2float(__ushort_as_half(static_cast<uint16_t>(vn2.y)));
-        vnk[4 * tt + 3] = __half2float(__ushort_as_half(static_cast<uint16_t>(vn2.y >> 16)));
+        const uint32_t r0 = static_cast<uint32_t>(min(16 * tt + 4 * g4, r_last & ~3) - hoff[tt]);
+        d.kn[tt] = *reinterpret_cast<const uint2*>(knh[tt] + r0);
+        d.vn[tt] = *reinterpret_cast<const uint2*>(vnh[tt] + r0);
       }
 #pragma unroll
       for (int i = 0; i < VPER; ++i) {
         const int ci = lane + 64 * i;
         constexpr int KPI = 64 / CPR;               // keys per i: all in one half
         const int half = (KPI * i) >> 4;
-        const int r = min(ci / CPR, r_last) - hoff[half];
-        vw[i] = vh[half][r * (D / 8) + ci % CPR];
+        const uint32_t r = static_cast<uint32_t>(min(ci / CPR, r_last) - hoff[half]);
+        d.vw[i] = vh[half][r * (D / 8) + ci % CPR];
       }
     } else {
-      float kn_l[2], vn_l[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int64_t vec = vec_of(t0 + 16 * tt + l16);
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) kw[tt][kk] = kc32[vec * (D / 8) + 4 * kk + g4];
-        kn_l[tt] = __half2float(__ushort_as_half(p.k_norms[vec]));
-        vn_l[tt] = __half2float(__ushort_as_half(p.v_norms[vec]));
+        for (int kk = 0; kk < NK; ++kk) d.kw[tt][kk] = kc32[vec * (D / 8) + 4 * kk + g4];
+        d.kn[tt] = make_uint2(p.k_norms[vec], 0u);
+        d.vn[tt] = make_uint2(p.v_norms[vec], 0u);
       }
 #pragma unroll
       for (int i = 0; i < VPER; ++i) {
         const int ci = lane + 64 * i;
-        vw[i] = vc32[vec_of(t0 + ci / CPR) * (D / 8) + ci % CPR];
+        d.vw[i] = vc32[vec_of(t0 + ci / CPR) * (D / 8) + ci % CPR];
       }
+    }
+  };
+  auto h2f = [](uint32_t bits) { return __half2float(__ushort_as_half(static_cast<uint16_t>(bits))); };
+
+  for (int i = tid; i < 256; i += 64 * W)
+    pair_lut[i] = static_cast<uint32_t>(f16_bits(kLevels[i & 15])) |
+                  (static_cast<uint32_t>(f16_bits(kLevels[i >> 4])) << 16);
+  // The wave's query rows and signs are requested next, then its first
+  // step's codes, so that their latency passes under the rotation.
+  uint32_t qw[RPW];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+  for (int i = 0; i < RPW; ++i) {
+    const int g = wave + W * i;
+    qw[i] = (g < G && lane < HALF) ? *reinterpret_cast<const uint32_t*>(p.q + (row0 + g) * D + 2 * lane) : 0u;
+  }
+  const float2 sg = lane < HALF ? *reinterpret_cast<const float2*>(p.signs + 2 * lane) : make_float2(0.f, 0.f);
+  // every query has a key (empty sequences are refused), so every wave
+  // loads a step; a wave without steps of its own loads the last one and
+  // leaves it unused
+  const int nsteps = (it.n_tok + kQStep - 1) / kQStep;
+  Q4StepRaw<D> cur, nxt;
+  load_step(min(wave, nsteps - 1), cur);
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int g = wave + W * i;
+    if (g >= G) {
+      // rows of the tile past the group: zero operands, no rotation
+      if (lane < HALF) {
+        qrot[g][2 * lane] = 0.f;
+        qrot[g][2 * lane + 1] = 0.f;
+      }
+      continue;
+    }
+    float y0 = sg.x * bf16_lo(qw[i]);
+    float y1 = sg.y * bf16_hi(qw[i]);
+    fwht_f32(y0, y1, lane, HALF);
+    if (lane < HALF) {
+      qrot[g][2 * lane] = y0;
+      qrot[g][2 * lane + 1] = y1;
+    }
+  }
+  // LDS only: the first step's loads stay in flight across the barrier
+  lds_barrier();
+  // B operand: row l16, dims 32 kk + 8 g4 .. + 7
+  f16x8 qf[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[kk][e] = static_cast<_Float16>(qrot[l16][32 * kk + 8 * g4 + e]);
+
+  auto levels8 = [&](uint32_t word) {
+    const uint32_t a = pair_lut[word & 255u], b = pair_lut[(word >> 8) & 255u];
+    const uint32_t c = pair_lut[(word >> 16) & 255u], d = pair_lut[word >> 24];
+    const uint4 u = make_uint4(a, b, c, d);
+    return __builtin_bit_cast(f16x8, u);
+  };
+  const float zscale = p.scale_log2 / static_cast<float>(D);
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4v o[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  uint16_t (*vs)[D + 8] = sm.v[wave];
+
+  // One step from its loaded codes and norms.
+  auto compute_step = [&](int s, const Q4StepRaw<D>& cur) __attribute__((always_inline)) {
+    const int t0 = s * kQStep;
+    // norms of the keys this lane's scores hold (16 tt + 4 g4 + i)
+    float knk[8], vnk[8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      if constexpr (BIG) {
+        knk[4 * tt + 0] = h2f(cur.kn[tt].x);
+        knk[4 * tt + 1] = h2f(cur.kn[tt].x >> 16);
+        knk[4 * tt + 2] = h2f(cur.kn[tt].y);
+        knk[4 * tt + 3] = h2f(cur.kn[tt].y >> 16);
+        vnk[4 * tt + 0] = h2f(cur.vn[tt].x);
+        vnk[4 * tt + 1] = h2f(cur.vn[tt].x >> 16);
+        vnk[4 * tt + 2] = h2f(cur.vn[tt].y);
+        vnk[4 * tt + 3] = h2f(cur.vn[tt].y >> 16);
+      } else {
+        const float kn_l = h2f(cur.kn[tt].x), vn_l = h2f(cur.vn[tt].x);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int src = 4 * g4 + i;                 // the lane that loaded key 16 tt + 4 g4 + i
-          knk[4 * tt + i] = __shfl(kn_l[tt], src, 64);
-          vnk[4 * tt + i] = __shfl(vn_l[tt], src, 64);
+          knk[4 * tt + i] = __shfl(kn_l, src, 64);
+          vnk[4 * tt + i] = __shfl(vn_l, src, 64);
         }
+      }
     }
     // V tile as fp16 levels (this wave's earlier reads of it are done)
     wave_sync_lds();
 #pragma unroll
     for (int i = 0; i < VPER; ++i) {
       const int ci = lane + 64 * i;
-      *reinterpret_cast<f16x8*>(&vs[ci / CPR][(ci % CPR) * 8]) = levels8(vw[i]);
+      *reinterpret_cast<f16x8*>(&vs[ci / CPR][(ci % CPR) * 8]) = levels8(cur.vw[i]);
     }
     // S^T = K Q^T: lane (l16, g4) gets keys 16 tt + 4 g4 + i of row l16
     f32x4v sacc[2];
@@ -393,30 +431,39 @@ __global__ __launch_bounds__(64 * W) void q4_mfma_kernel(Q4DecodeParams p) {
       sacc[tt] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(levels8(kw[tt][kk]), qf[kk], sacc[tt], 0, 0, 0);
+        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(levels8(cur.kw[tt][kk]), qf[kk], sacc[tt], 0, 0, 0);
     }
-    float z[8];
+    // y = n_k * (qh . level): the logit before the factor zscale, which the
+    // exponent applies (zscale > 0, so the max commutes with it)
+    float y[8];
+    if (t0 + kQStep <= it.n_tok) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int e = 0; e < 8; ++e) y[e] = sacc[e >> 2][e & 3] * knk[e];
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 16 * tt + 4 * g4 + i;
-        z[4 * tt + i] = tok < it.n_tok ? sacc[tt][i] * knk[4 * tt + i] * zscale : -INFINITY;
+      for (int e = 0; e < 8; ++e) {
+        const int tok = t0 + 16 * (e >> 2) + 4 * g4 + (e & 3);
+        y[e] = tok < it.n_tok ? sacc[e >> 2][e & 3] * knk[e] : -INFINITY;
       }
-    float mx = z[0];
+    }
+    float mx = y[0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, z[j]);
-    mx = xor32_max(xor16_max(mx));
-    const float m_new = fmaxf(m_run, mx);          // finite: every step holds a key
-    const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
-    l_run *= alpha;
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, y[j]);
+    mx = xor32_max(xor16_max(mx)) * zscale;
+    // the running max moves only when this step passes it; o and l are
+    // rescaled then (they are still zero before the first step)
+    const bool grow = mx > m_run;
+    if (__ballot(grow && m_run != -INFINITY)) {
+      const float alpha = (m_run == -INFINITY || !grow) ? 1.f : fast_exp2(m_run - mx);
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
-    m_run = m_new;
+      for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+    }
+    m_run = grow ? mx : m_run;                     // finite: every step holds a key
     f16x8 pf;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pr = fast_exp2(z[j] - m_new);
+      const float pr = fast_exp2(fmaf(y[j], zscale, -m_run));
       l_run += pr;
       pf[j] = static_cast<_Float16>(pr * vnk[j]);
     }
@@ -432,8 +479,29 @@ __global__ __launch_bounds__(64 * W) void q4_mfma_kernel(Q4DecodeParams p) {
       const f16x8 a = __builtin_bit_cast(f16x8, both);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, o[dt], 0, 0, 0);
     }
+  };
+  // Two buffers in turn: the wave's next step is requested before the
+  // current one is computed.  Each branch computes its own copy of the step,
+  // so that the load-counter wait before it is fixed: the copy after a
+  // request waits only for the older loads.
+  if (wave < nsteps) {
+    for (int s = wave;; s += 2 * W) {
+      if (s + W < nsteps) {
+        load_step(s + W, nxt);
+        compute_step(s, cur);
+      } else {
+        compute_step(s, cur);
+        break;
+      }
+      if (s + 2 * W < nsteps) {
+        load_step(s + 2 * W, cur);
+        compute_step(s + W, nxt);
+      } else {
+        compute_step(s + W, nxt);
+        break;
+      }
+    }
   }
-
   // ---- merge of the W wave states, rotation back --------------------------
   const float l_w = xor32_sum(xor16_sum(l_run));
   __syncthreads();   // every wave is done with its V tile (aliased below)
@@ -493,10 +561,15 @@ hipError_t launch_q4_decode(const Q4DecodeParams& p, int32_t n_items, int32_t he
                             hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (n_items == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(n_items) * p.Hkv));
-  if (head_dim == 64)
-    hipExtLaunchKernelGGL((q4_mfma_kernel<64, 8>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p);
+  const bool big = p.B >= 16;
+  if (head_dim == 64 && big)
+    hipExtLaunchKernelGGL((q4_mfma_kernel<64, 8, true>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p);
+  else if (head_dim == 64)
+    hipExtLaunchKernelGGL((q4_mfma_kernel<64, 8, false>), grid, dim3(512), 0, s, ev_start, ev_stop, 0, p);
+  else if (head_dim == 128 && big)
+    hipExtLaunchKernelGGL((q4_mfma_kernel<128, 4, true>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, p);
   else if (head_dim == 128)
-    hipExtLaunchKernelGGL((q4_mfma_kernel<128, 4>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, p);
+    hipExtLaunchKernelGGL((q4_mfma_kernel<128, 4, false>), grid, dim3(256), 0, s, ev_start, ev_stop, 0, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

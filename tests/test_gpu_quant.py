@@ -106,6 +106,9 @@ CASES = [
     ("q4_d128_short", Shape(16, 4, 128, 16, 1, 64), 5, 4, 3, 3),
     ("q4_d64_g16", Shape(16, 1, 64, 16, 1, 128), 300, 2, 40, 2),
     ("q4_d128_g3", Shape(12, 4, 128, 32, 1, 128), 610, 2, 17, 2),
+    # blocks under 16 tokens: per-key block lookups in the decode kernel
+    ("q4_d64_b8", Shape(16, 2, 64, 8, 1, 512), 100, 3, 45, 2),
+    ("q4_d128_b2", Shape(8, 2, 128, 2, 1, 1024), 70, 2, 21, 2),
 ]
 
 
