@@ -160,6 +160,47 @@ def test_q4_pool_contents_and_decode_parity(dev, case):
     assert tot / cnt <= TOL_MEAN
 
 
+# Decode batches large enough that the kernel runs fewer waves per (query,
+# kv head): at head_dim 64 the launch takes 1, 2 or 4 waves from 2048, 1024
+# and 512 workgroups up, at 128 it takes 1 or 2 from 1024 and 512.  A sample
+# of the sessions is checked against the oracle.
+BATCH_CASES = [
+    ("q4_d64_w1", Shape(32, 4, 64, 16, 1, 16 + 600 * 2 + 8), 600),
+    ("q4_d64_w2", Shape(32, 4, 64, 16, 1, 16 + 300 * 2 + 8), 300),
+    ("q4_d64_w4", Shape(32, 4, 64, 32, 1, 16 + 130 * 2 + 8), 130),
+    ("q4_d128_w1", Shape(32, 8, 128, 16, 1, 16 + 130 * 2 + 8), 130),
+    ("q4_d128_w2", Shape(32, 8, 128, 16, 1, 16 + 70 * 2 + 8), 70),
+]
+
+
+@pytest.mark.parametrize("case", BATCH_CASES, ids=[c[0] for c in BATCH_CASES])
+def test_q4_decode_batch_forms(dev, case):
+    name, shape, sessions = case
+    wl = synth.fork_workload(name, 60 + BATCH_CASES.index(case), shape, prefix_len=200,
+                             n_branches=sessions, branch_len=5, decode_steps=1, permute=True)
+    signs = wl.rotation_signs()
+    got, _ = run_q4(wl, signs)
+    worst, tot, cnt, checked = 0.0, 0.0, 0, 0
+    for idx, op, pool, handles, _ in run_program(wl, want=set()):
+        if op[0] != "decode":
+            continue
+        q = wl.decode_query(op[3], len(op[1]))
+        sel = list(range(0, len(op[1]), 7)) + [len(op[1]) - 1]
+        o_exp, l_exp = decode_q4(pool, op[2], [handles[op[1][i]] for i in sel], q[sel], wl.sm_scale, signs)
+        d = np.abs(got[idx][0][sel].astype(np.float64) - o_exp)
+        dl = np.abs(got[idx][1][sel].astype(np.float64) - l_exp)
+        assert d.max() <= TOL_MAX and dl.max() <= TOL_MAX, (name, idx, d.max(), dl.max())
+        worst = max(worst, d.max())
+        tot += d.sum()
+        cnt += d.size
+        checked += len(sel)
+    assert checked >= sessions // 7
+    print(f"[parity] {name}: {checked} sessions, max |d| {worst:.3e} mean |d| {tot / cnt:.3e}", flush=True)
+    from conftest import record_margin
+    record_margin(name, worst, tot / cnt, cnt, TOL_MAX, TOL_MEAN)
+    assert tot / cnt <= TOL_MEAN
+
+
 def test_q4_pool_refuses_other_calls(dev):
     import torch
     import paged_kv_cache_204_amd as pkv
