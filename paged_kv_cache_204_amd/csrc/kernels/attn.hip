@@ -710,6 +710,11 @@ struct DirectSmemAll {
   char vt[W][S][kStep * D * 2];
   DirectFin<D, W> fin;
 };
+template <int D, int W, int NSLOT>
+union DirectSmemSteps {
+  char vt[NSLOT][kStep * D * 2];
+  DirectFin<D, W> fin;
+};
 
 // The grid is (kv head, item), so a workgroup finds its item and head
 // without arithmetic on kernel arguments, and the first loads (the item's
@@ -730,7 +735,7 @@ struct DirectSmemAll {
 // LAYERS: grid.z runs over consecutive layers of one call (the same items
 // and block lists); workgroup z reads layer p.layer + z of the pools, its
 // query rows and writes its out / lse rows at z times the layer's row count.
-template <int D, int W, int DEPTH, bool ALL, bool LAYERS>
+template <int D, int W, int DEPTH, bool ALL, bool LAYERS, int NSLOT = 0>
 __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restrict__ items,
                                                           const int32_t* __restrict__ blocks,
                                                           const uint16_t* __restrict__ q,
@@ -745,7 +750,7 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
   constexpr int VPER = kStep * CPR / 64;   // V chunks per lane per step
   constexpr int LPER = (kMaxItemBlocks + 64 * W - 1) / (64 * W);   // block-list entries per thread
   static_assert(VPER * 64 == kStep * CPR, "a step's V splits evenly over a wave");
-  using Smem = std::conditional_t<ALL, DirectSmemAll<D, W, DEPTH>, DirectSmem<D, W>>;
+  using Smem = std::conditional_t<ALL, std::conditional_t<(NSLOT > 0), DirectSmemSteps<D, W, NSLOT>, DirectSmemAll<D, W, DEPTH>>, DirectSmem<D, W>>;
   __shared__ Smem sm;
   __shared__ int32_t blk_s[kMaxItemBlocks];
 
@@ -844,16 +849,21 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
         const int r = q / CPR;
         vci[j][u] = chunk_at((wave + j * W) * kStep + r, (q % CPR) ^ tile_swz<D>(r));
       }
+    const int issued = NSLOT > 0 ? min(mine, DEPTH) : DEPTH;
+    auto vtile = [&](int j) -> char* {
+      if constexpr (NSLOT > 0) return sm.vt[wave + j * W]; else return sm.vt[wave][j];
+    };
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j)
+      if (NSLOT == 0 || j < issued)
 #pragma unroll
-      for (int u = 0; u < VPER; ++u) lds_dma16(vb + vci[j][u], sm.vt[wave][j] + 1024 * u);
+        for (int u = 0; u < VPER; ++u) lds_dma16(vb + vci[j][u], vtile(j) + 1024 * u);
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
       if (j >= mine) break;
       // step j's V runs have landed: only later steps' runs may be in flight
-      wait_vmcnt_steps<VPER, DEPTH - 1>(DEPTH - 1 - j);
-      const char* vt = sm.vt[wave][j];
+      wait_vmcnt_steps<VPER, DEPTH - 1>(issued - 1 - j);
+      const char* vt = vtile(j);
       const auto kop = [&](int tt, int kk) { return rk[j][tt][kk]; };
       const auto vop = [&](int dt) {
         const int r = 4 * g4 + (l16 >> 2);
@@ -924,7 +934,7 @@ __global__ __launch_bounds__(64 * W) void direct_kernel(const WorkItem* __restri
 
   // ---- merge of the W wave states ------------------------------------------
   const float l_w = xor32_sum(xor16_sum(l_run[0]));
-  if constexpr (!ALL) lds_barrier();   // every wave is done with its V region (aliased below)
+  if constexpr (!ALL || NSLOT > 0) lds_barrier();   // every wave is done with its V region (aliased below)
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
     *reinterpret_cast<float4*>(&sm.fin.o[wave][l16][16 * dt + 4 * g4]) =
@@ -1003,7 +1013,17 @@ hipError_t launch_direct_t(const AttnParams& p, dim3 grid, int32_t head_dim, int
   // registers than eight waves per workgroup leave, so four.  At 64, calls
   // of at most 3 steps per wave (768 keys) load everything in one round.
   constexpr int kAllSteps = 3;
-  if (head_dim == 64 && max_tok <= kAllSteps * 8 * kStep)
+  // With more workgroups than CUs, calls of at most kStepSlots steps keep
+  // their V tiles in one step-indexed array that the merge area overlays
+  // (74 KB of LDS instead of 133): two workgroups per CU, so one's loads
+  // overlap the other's math and merge.  With fewer, the separate merge area
+  // saves the barrier before the merge.
+  constexpr int kStepSlots = 18;
+  const int64_t n_wg = static_cast<int64_t>(grid.x) * grid.y * grid.z;
+  if (head_dim == 64 && max_tok <= kStepSlots * kStep && n_wg > 256)
+    hipExtLaunchKernelGGL((direct_kernel<64, 8, kAllSteps, true, LAYERS, kStepSlots>), grid, dim3(512), 0, s, ev_start,
+                          ev_stop, 0, p.items, p.blocks, p.q, stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
+  else if (head_dim == 64 && max_tok <= kAllSteps * 8 * kStep)
     hipExtLaunchKernelGGL((direct_kernel<64, 8, kAllSteps, true, LAYERS>), grid, dim3(512), 0, s, ev_start, ev_stop, 0,
                           p.items, p.blocks, p.q, stride, p.Hq, g_log2B, blk_chunks, kl, vl, p);
   else if (head_dim == 64)

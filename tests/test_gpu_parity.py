@@ -241,6 +241,11 @@ def test_shape_edges(dev, shape, label, path, monkeypatch):
 # roll two steps ahead: the fifth case's calls hold 765 .. 769 keys (both
 # forms, 768 the last one-round call); the sixth has 16-token blocks (two
 # per step) and G 16, the seventh 64-token blocks (half a block per step).
+# Calls of more workgroups than CUs at head_dim 64 and at most 576 keys run
+# two workgroups per CU with step-indexed V tiles: the eighth case (320
+# workgroups, 514 .. 516 keys), the ninth (300, ragged 21 .. 469 keys, so
+# some waves have no step), the tenth (280 workgroups at 651 .. 720 keys,
+# past the step-indexed tiles: the one-round form again).
 DIRECT_CASES = [
     # shape, prefix, own keys of branch i = base + i * inc, branches[, decode steps]
     (Shape(8, 8, 64, 16, 1, 64), 1, 0, 1, 6),
@@ -250,6 +255,9 @@ DIRECT_CASES = [
     (Shape(32, 4, 64, 32, 1, 256), 760, 4, 0, 3, 5),
     (Shape(16, 1, 64, 16, 1, 256), 40, 0, 100, 6),
     (Shape(32, 4, 64, 64, 1, 64), 100, 3, 50, 5),
+    (Shape(32, 4, 64, 32, 1, 1024), 256, 257, 0, 80, 3),
+    (Shape(16, 2, 64, 16, 1, 4096), 20, 0, 3, 150, 2),
+    (Shape(32, 4, 64, 32, 1, 2048), 600, 50, 1, 70, 2),
 ]
 
 
