@@ -260,7 +260,7 @@ pkv_status kv_tree_commit(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs, i
  * Blocks shared by several of the sequences (a common prefix) are read once
  * per query group and the partial softmax states are merged by log-sum-exp.
  * Calls of short queries (by default every query at most 1024 keys and at
- * most 4096 query x kv-head pairs) instead run one workgroup per query and
+ * most 768 query x kv-head pairs) instead run one workgroup per query and
  * kv head over all of its keys, in a single launch with no merge; the
  * environment variables PKV_DIRECT_MAX_TOKENS / PKV_DIRECT_MAX_WGS, read at
  * kv_pool_create, move these limits (0 turns that mode off).

@@ -43,7 +43,7 @@ struct PlanConfig {
   int32_t unshare_max_tokens = 256;  // ... and tokens, too sparse for the MFMA path,
                                      // is read by each query's own item instead
   int32_t direct_max_tokens = 1024;  // decode calls whose queries all have at most this many
-  int32_t direct_max_wgs = 4096;     // keys, over at most this many (query, kv head) pairs,
+  int32_t direct_max_wgs = 768;      // keys, over at most this many (query, kv head) pairs,
                                      // run one workgroup per pair over all of its keys (no
                                      // partial states, no merge); 0 turns this off
   int32_t tile = 64;             // key tokens per kernel tile; chunks are multiples
