@@ -710,6 +710,9 @@ struct DirectSmemAll {
   char vt[W][S][kStep * D * 2];
   DirectFin<D, W> fin;
 };
+// The same with one V tile per step of the call (step s in tile s, at most
+// NSLOT steps) under the merge area, which the waves fill after a barrier:
+// less LDS, so two workgroups fit on a CU.
 template <int D, int W, int NSLOT>
 union DirectSmemSteps {
   char vt[NSLOT][kStep * D * 2];
@@ -730,7 +733,9 @@ union DirectSmemSteps {
 // ALL (calls whose every wave has at most DEPTH steps): a wave issues the
 // loads of all of its steps at once -- K into registers, then V by LDS DMA
 // into DEPTH tiles of its own -- so the call waits for one memory round
-// trip, not one per DEPTH steps; V then costs no registers.
+// trip, not one per DEPTH steps; V then costs no registers.  NSLOT > 0
+// (calls of at most NSLOT steps): the V tiles are indexed by step and a wave
+// loads only the steps it computes.
 //
 // LAYERS: grid.z runs over consecutive layers of one call (the same items
 // and block lists); workgroup z reads layer p.layer + z of the pools, its
