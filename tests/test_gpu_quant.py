@@ -164,19 +164,22 @@ def test_q4_pool_contents_and_decode_parity(dev, case):
 # kv head): at head_dim 64 the launch takes 1, 2 or 4 waves from 2048, 1024
 # and 512 workgroups up, at 128 it takes 1 or 2 from 1024 and 512.  A sample
 # of the sessions is checked against the oracle.
+# The last case has one 32-key step per query (9 keys), so every wave of the
+# one-wave form computes a single step.
 BATCH_CASES = [
-    ("q4_d64_w1", Shape(32, 4, 64, 16, 1, 16 + 600 * 2 + 8), 600),
-    ("q4_d64_w2", Shape(32, 4, 64, 16, 1, 16 + 300 * 2 + 8), 300),
-    ("q4_d64_w4", Shape(32, 4, 64, 32, 1, 16 + 130 * 2 + 8), 130),
-    ("q4_d128_w1", Shape(32, 8, 128, 16, 1, 16 + 130 * 2 + 8), 130),
-    ("q4_d128_w2", Shape(32, 8, 128, 16, 1, 16 + 70 * 2 + 8), 70),
+    ("q4_d64_w1", Shape(32, 4, 64, 16, 1, 16 + 600 * 2 + 8), 600, 200),
+    ("q4_d64_w2", Shape(32, 4, 64, 16, 1, 16 + 300 * 2 + 8), 300, 200),
+    ("q4_d64_w4", Shape(32, 4, 64, 32, 1, 16 + 130 * 2 + 8), 130, 200),
+    ("q4_d128_w1", Shape(32, 8, 128, 16, 1, 16 + 130 * 2 + 8), 130, 200),
+    ("q4_d128_w2", Shape(32, 8, 128, 16, 1, 16 + 70 * 2 + 8), 70, 200),
+    ("q4_d64_w1_short", Shape(32, 4, 64, 16, 1, 16 + 600 * 2 + 8), 600, 3),
 ]
 
 
 @pytest.mark.parametrize("case", BATCH_CASES, ids=[c[0] for c in BATCH_CASES])
 def test_q4_decode_batch_forms(dev, case):
-    name, shape, sessions = case
-    wl = synth.fork_workload(name, 60 + BATCH_CASES.index(case), shape, prefix_len=200,
+    name, shape, sessions, prefix = case
+    wl = synth.fork_workload(name, 60 + BATCH_CASES.index(case), shape, prefix_len=prefix,
                              n_branches=sessions, branch_len=5, decode_steps=1, permute=True)
     signs = wl.rotation_signs()
     got, _ = run_q4(wl, signs)
