@@ -301,7 +301,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D == 64 
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) d.kw[tt][kk] = kh[tt][r * (D / 8) + 4 * kk + g4];
         // four consecutive keys' norms, one 8-byte load each (a group past
-        // the end re-reads the half's last whole group)
+        // the end re-reads the half's last whole group, which may run past
+        // the last key into unwritten slots: masked when the step is computed)
         const uint32_t r0 = static_cast<uint32_t>(min(16 * tt + 4 * g4, r_last & ~3) - hoff[tt]);
         d.kn[tt] = *reinterpret_cast<const uint2*>(knh[tt] + r0);
         d.vn[tt] = *reinterpret_cast<const uint2*>(vnh[tt] + r0);
@@ -440,10 +441,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D == 64 
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = sacc[e >> 2][e & 3] * knk[e];
     } else {
+      // keys past the end: no score, and no V norm (a norm group that runs
+      // past the last key holds slots never written, whose bits may be inf
+      // or NaN, and 0 * inf would reach P V)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tok = t0 + 16 * (e >> 2) + 4 * g4 + (e & 3);
         y[e] = tok < it.n_tok ? sacc[e >> 2][e & 3] * knk[e] : -INFINITY;
+        vnk[e] = tok < it.n_tok ? vnk[e] : 0.f;
       }
     }
     float mx = y[0];

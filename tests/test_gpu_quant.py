@@ -39,8 +39,10 @@ class Q4Pool:
         cb, nb = pkv.kv_pool_q4_bytes(desc)
         self.kc = torch.full((cb,), 0x5A, dtype=torch.uint8, device="cuda")
         self.vc = torch.full((cb,), 0x5A, dtype=torch.uint8, device="cuda")
-        self.kn = torch.zeros(nb // 2, dtype=torch.int16, device="cuda")
-        self.vn = torch.zeros(nb // 2, dtype=torch.int16, device="cuda")
+        # norms of unwritten slots start as fp16 NaN: a decode must never
+        # let them reach its output
+        self.kn = torch.full((nb // 2,), 0x7E00, dtype=torch.int16, device="cuda")
+        self.vn = torch.full((nb // 2,), 0x7E00, dtype=torch.int16, device="cuda")
         self.pool = pkv.kv_pool_create_q4(desc, self.kc, self.vc, self.kn, self.vn, signs,
                                           free_order=free_order)
         self.stream = torch.cuda.current_stream().cuda_stream
